@@ -1,0 +1,115 @@
+"""Pins of the oracle's sparse + sliding-window attention against a library
+routine (PyTorch fp64 scaled_dot_product_attention), the log-sum-exp merge
+identity and closed-form special cases."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_csa2_amd import inputs
+from conftest import read_golden
+
+CONST = dict(read_golden("pages_constants.txt"))
+TOPK = int(CONST["topk"])
+WINDOW = int(CONST["swa_window"])
+E2M1 = {int(c): float(v) for c, v in read_golden("e2m1_grid.txt")}
+
+
+def _decode_independent(codes, scales):
+    """FP4 decode from the spec table and PyTorch's E4M3 cast (not the oracle's)."""
+    lo, hi = codes & 15, codes >> 4
+    nib = np.stack([lo, hi], -1).reshape(codes.shape[0], -1)
+    mag = np.vectorize(E2M1.get)(nib & 7).astype(np.float64)
+    val = np.where(nib & 8, -mag, mag)
+    s = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return val * np.repeat(s, 16, axis=1)
+
+
+def _sdpa(q, keys, scale):
+    qt = torch.from_numpy(q)[None, :, None, :]              # [1, H, 1, D]
+    kt = torch.from_numpy(keys)[None, None].expand(1, q.shape[0], -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=scale)
+    z = (qt @ kt.transpose(-1, -2)) * scale
+    return o[0, :, 0].numpy(), torch.logsumexp(z, -1)[0, :, 0].numpy()
+
+
+def _case(n, H, D, T, tag):
+    lat = inputs.normal((n, D), f"lat{tag}").numpy()
+    q = inputs.normal((H, D), f"q{tag}", dtype=torch.bfloat16).double().numpy()
+    swa = inputs.normal((T, D), f"swa{tag}", dtype=torch.bfloat16).double().numpy()
+    return lat, q, swa
+
+
+@pytest.mark.parametrize("n,H,D", [(300, 16, 128), (512, 64, 512)])
+def test_short_context_equals_dense_attention(orc, n, H, D):
+    # n <= 512: Top-512 selects every entry, so CSA2 attention is dense attention
+    # over all entries plus the window.
+    lat, q, swa = _case(n, H, D, WINDOW, f"d{n}")
+    codes, scales = orc.fp4_encode(lat)
+    s = np.full(n, 1.0, np.float32)
+    idx = orc.topk(s, TOPK)
+    assert np.all(idx[:n] == np.arange(n))
+    o, lse = orc.attention(q, codes, scales, idx, swa, WINDOW - 1, WINDOW, 1 / np.sqrt(D))
+    keys = np.concatenate([_decode_independent(codes, scales), swa])
+    o_ref, lse_ref = _sdpa(q, keys, 1 / np.sqrt(D))
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_lse_merge_identity(orc):
+    n, H, D = 900, 16, 256
+    lat, q, swa = _case(n, H, D, 200, "m")
+    codes, scales = orc.fp4_encode(lat)
+    idx = inputs.small_ints((TOPK,), "idx_m", -1, n - 1, dtype=torch.int32).numpy()
+    sc = 0.7 / np.sqrt(D)
+    o_u, l_u = orc.attention(q, codes, scales, idx, swa, 150, WINDOW, sc)
+    o_a, l_a = orc.attention(q, codes, scales, idx, None, 0, 0, sc)
+    o_b, l_b = orc.attention(q, None, None, None, swa, 150, WINDOW, sc)
+    l_m = np.logaddexp(l_a, l_b)
+    o_m = (np.exp(l_a - l_m)[:, None] * o_a + np.exp(l_b - l_m)[:, None] * o_b)
+    np.testing.assert_allclose(o_u, o_m, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(l_u, l_m, rtol=1e-13)
+
+
+def test_window_bounds(orc):
+    # slot 5 with window 128 sees rows 0..5 only; rows after the slot never count.
+    D, H = 128, 16
+    swa = inputs.normal((40, D), "wb", dtype=torch.bfloat16).double().numpy()
+    q = inputs.normal((H, D), "wq", dtype=torch.bfloat16).double().numpy()
+    o, lse = orc.attention(q, None, None, None, swa, 5, WINDOW, 0.1)
+    o_ref, lse_ref = _sdpa(q, swa[:6], 0.1)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    # window 3 at slot 30 -> rows 28..30
+    o, lse = orc.attention(q, None, None, None, swa, 30, 3, 0.1)
+    o_ref, lse_ref = _sdpa(q, swa[28:31], 0.1)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
+
+
+def test_identical_keys_give_that_key(orc):
+    D, H = 128, 16
+    row = inputs.normal((1, D), "same").numpy()
+    lat = np.repeat(row, 50, 0)
+    codes, scales = orc.fp4_encode(lat)
+    key = _decode_independent(codes[:1], scales[:1])[0]
+    q = inputs.normal((H, D), "sq").double().numpy()
+    idx = np.arange(50, dtype=np.int32)
+    o, lse = orc.attention(q, codes, scales, idx, None, 0, 0, 1.0)
+    np.testing.assert_allclose(o, np.broadcast_to(key, o.shape), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, (q @ key) + np.log(50), rtol=1e-13)
+
+
+def test_dominant_logit_picks_its_key(orc):
+    D, H = 128, 16
+    lat = inputs.normal((64, D), "dom").numpy()
+    codes, scales = orc.fp4_encode(lat)
+    keys = _decode_independent(codes, scales)
+    q = np.repeat(keys[17:18] * 50.0, H, 0)   # q . key_17 dominates every other logit
+    o, _ = orc.attention(q, codes, scales, np.arange(64, dtype=np.int32), None, 0, 0, 1.0)
+    np.testing.assert_allclose(o, np.broadcast_to(keys[17], o.shape), atol=1e-9)
+
+
+def test_empty_key_set(orc):
+    q = np.ones((16, 128))
+    o, lse = orc.attention(q, np.zeros((4, 64), np.uint8), np.zeros((4, 8), np.uint8),
+                           np.full(8, -1, np.int32), None, 0, 0, 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))

@@ -1,0 +1,65 @@
+"""Pins of the oracle's static layer-mode schedule (Full / Reindex / Reuse)."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_csa2_amd import inputs
+from conftest import read_golden
+
+CONST = dict(read_golden("pages_constants.txt"))
+
+
+def _seq_and_layers(pattern, n, H=16, D=128, H_i=4, D_i=64, T=128, tag="s"):
+    lat = inputs.normal((n, D), f"{tag}lat").numpy()
+    import oracle
+    codes, scales = oracle.fp4_encode(lat)
+    K = inputs.bf16_bits(inputs.normal((n, D_i), f"{tag}K", dtype=torch.bfloat16))
+    seq = dict(K_idx=K, codes=codes, scales=scales, n_vis=n)
+    layers = []
+    for l, _ in enumerate(pattern):
+        layers.append(dict(
+            q=inputs.normal((H, D), f"{tag}q{l}", dtype=torch.bfloat16).double().numpy(),
+            q_idx=inputs.bf16_bits(inputs.normal((H_i, D_i), f"{tag}qi{l}", dtype=torch.bfloat16)),
+            swa=inputs.normal((T, D), f"{tag}swa{l}", dtype=torch.bfloat16).double().numpy(),
+            slot=T - 1))
+    return seq, layers
+
+
+def test_pattern_constants_from_pages():
+    dec = CONST["decoder_pattern"].replace(",", "")
+    enc = CONST["encoder_pattern"].replace(",", "")
+    assert len(dec) == 20 and dec.count("F") == 1 and dec.count("R") == 4
+    assert len(enc) == 18 and enc.count("F") == 3
+    assert inputs.WORKLOADS["ragged_paged_b64"].pattern == dec
+    assert inputs.WORKLOADS["encoder_prefill_q2k_n32k"].pattern == enc[:6]
+    assert int(CONST["pool_blocks"]) * int(CONST["pool_block_size"]) == int(CONST["pool_positions"])
+
+
+def test_reuse_reproduces_latest_selection(orc):
+    pattern = "FUURUU"
+    seq, layers = _seq_and_layers(pattern, 40000)
+    out = orc.run_stack(pattern, seq, layers)
+    np.testing.assert_array_equal(out[1]["idx"], out[0]["idx"])
+    np.testing.assert_array_equal(out[2]["idx"], out[0]["idx"])
+    np.testing.assert_array_equal(out[4]["idx"], out[3]["idx"])
+    np.testing.assert_array_equal(out[5]["idx"], out[3]["idx"])
+    assert not np.array_equal(out[3]["idx"], out[0]["idx"])  # Reindex re-selects with its own query
+    # Reindex selections live inside the Full layer's pool
+    assert set((out[3]["idx"] // 8).tolist()) <= set(out[0]["pool"].tolist())
+    # Reuse layers still attend with their own Q / SWA
+    assert not np.allclose(out[1]["o"], out[0]["o"])
+
+
+def test_reuse_with_same_inputs_as_source_gives_same_output(orc):
+    seq, layers = _seq_and_layers("FU", 5000, tag="same")
+    layers[1] = dict(layers[0])
+    out = orc.run_stack("FU", seq, layers)
+    np.testing.assert_array_equal(out[1]["o"], out[0]["o"])
+
+
+def test_mode_sequence_errors(orc):
+    seq, layers = _seq_and_layers("UR", 3000, tag="err")
+    with pytest.raises(ValueError):
+        orc.run_stack("U", seq, layers[:1])
+    with pytest.raises(ValueError):
+        orc.run_stack("R", seq, layers[1:])
