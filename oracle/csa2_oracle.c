@@ -76,6 +76,9 @@ double oracle_e4m3fn_decode(uint8_t code) {
  * codes, so values above the largest finite value (448) go to 448:
  * the scale saturates rather than overflowing. */
 uint8_t oracle_e4m3fn_round(double q) {
+    /* Saturation stated outright: far above 448 the fp64 differences below
+     * absorb 448 and every candidate would look equally distant. */
+    if (q >= 448.0) return 0x7E;
     int best = 0;
     double best_err = fabs(q - oracle_e4m3fn_decode(0));
     for (int code = 1; code <= 0x7E; ++code) {
@@ -99,6 +102,7 @@ double oracle_e2m1_magnitude(int mag) {
 
 /* Nearest E2M1 magnitude code to a non-negative real, ties to the even code. */
 static int e2m1_round_magnitude(double q) {
+    if (q >= 6.0) return 7; /* saturate at the largest magnitude, 6 */
     int best = 0;
     double best_err = fabs(q - oracle_e2m1_magnitude(0));
     for (int mag = 1; mag < 8; ++mag) {

@@ -136,6 +136,20 @@ def test_fp4_error_bound_and_scale_rule(orc):
     assert np.all(err[within] <= step[within])
 
 
+def test_fp4_saturation_far_out_of_range(orc):
+    # amax/6 ~ 1e29: the scale saturates at 448 and every element at 6 * 448
+    x = np.zeros((1, 32), np.float32)
+    x[0, :16] = 1e30
+    x[0, 3] = -1e30
+    x[0, 16:] = np.linspace(-3e38, 3e38, 16, dtype=np.float32)
+    codes, sc = orc.fp4_encode(x)
+    assert sc[0, 0] == 0x7E and sc[0, 1] == 0x7E
+    y = orc.fp4_decode(codes, sc)
+    assert y[0, 0] == 2688 and y[0, 3] == -2688 and y[0, 16] == -2688 and y[0, 31] == 2688
+    for q in [448.0, 455.0, 463.999, 3e38, 1e300]:
+        assert orc.e4m3fn_round(q) == 0x7E
+
+
 def test_fp4_saturation_and_zero_group(orc):
     x = np.zeros((2, 16), np.float32)
     x[0, :] = 1e5                      # amax/6 far above 448
