@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""CSA2 decode benchmark on one MI355X.
+
+A step is one decode token of every sequence through the whole hot path of the
+hierarchical-decode workload (4 sequences x 1,048,576 entries, layer pattern
+Full + 3 Reindex): FP4 append of the new entry, Full-mode indexer scan of every
+entry, Top-512 and the 2048-block pool, three Reindex layers that score and
+select inside the pool, and four layers of FP4 sparse + sliding-window
+attention.  Inputs are seeded synthetic tensors resident in HBM before the
+timed region starts.
+
+Prints one JSON line.  `value` is query-tokens/s of the whole job; `roofline`
+describes the dominant kernel (the Full-mode indexer scan), whose duration is
+measured with HIP events on the stream it runs on; `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="hier_decode_b4_n1m")
+    ap.add_argument("--scan-reps", type=int, default=20, help="extra timed launches of the indexer scan")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def alg_bytes(w, n_entries_total):
+    """Bytes the method must move per step (intermediate score buffers excluded).
+    Full scan: 2*D_i per visible entry + the indexer query; Reindex: 2*D_i per
+    pool position; attention per layer and query row: K FP4 entries of
+    D/2 + D/16 bytes, the index list, the main query (bf16), the output (fp32)
+    and the window rows (bf16)."""
+    rows = w.B * w.Q
+    full = 2 * w.D_i * n_entries_total + rows * w.H_i * w.D_i * 2
+    reindex = w.pattern.count("R") * rows * min(8 * w.P, n_entries_total // w.B) * 2 * w.D_i
+    attn_row = w.K * (w.D // 2 + w.D // 16) + 4 * w.K + 2 * w.H * w.D + 4 * w.H * w.D + 2 * w.window * w.D
+    attn = w.layers * rows * attn_row
+    append = w.B * (4 * w.D + w.D // 2 + w.D // 16)
+    return dict(full=full, reindex=reindex, attn=attn, append=append, total=full + reindex + attn + append)
+
+
+def cpu_baseline(inst, budget_s):
+    """Time the CPU oracle on whole query rows of the same workload until the
+    budget is used (at least one row)."""
+    import numpy as np
+    import oracle
+    from fp4_kv_cache_csa2_amd import inputs
+    import torch
+
+    oracle.build(force=False)
+    w = inst.w
+    done, t_total = 0, 0.0
+    for b in range(w.B):
+        lo, hi = int(inst.offsets[b]), int(inst.offsets[b + 1])
+        K_b = inputs.bf16_bits(inst.k_logical[lo:hi])
+        qi = [None if L["q_idx"] is None else inputs.bf16_bits(L["q_idx"][b, 0]) for L in inst.layers]
+        qs = [L["q"][b, 0].double().cpu().numpy() for L in inst.layers]
+        sw = [L["swa"][b].double().cpu().numpy() for L in inst.layers]
+        # the FP4 cache rows the oracle will attend are encoded outside the timed region
+        sel, _ = oracle.select_stack(w.pattern, K_b, int(inst.n_vis_host[b, 0]), qi, w.K, w.P)
+        ids = np.unique(np.concatenate([s[s >= 0] for s in sel]))
+        lat = inst.latent[torch.from_numpy(lo + ids).to(inst.latent.device)].cpu().numpy()
+        rc, rs = oracle.fp4_encode(lat)
+        t0 = time.perf_counter()
+        sel, _ = oracle.select_stack(w.pattern, K_b, int(inst.n_vis_host[b, 0]), qi, w.K, w.P)
+        for l in range(w.layers):
+            idx_c = np.where(sel[l] >= 0, np.searchsorted(ids, sel[l]), -1).astype(np.int32)
+            oracle.attention(qs[l], rc, rs, idx_c, sw[l], int(inst.q_slot_host[b, 0]), w.window, inst.sm_scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    return {"value": done / t_total, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences x 1 query token through the whole {w.pattern} stack at "
+                      f"N={inst.n_max} (scoring, Top-K, pool, Reindex, fp64 attention); single-threaded C; "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from fp4_kv_cache_csa2_amd import api, inputs, workload
+
+    w = inputs.WORKLOADS[args.workload]
+    assert w.Q == 1, "the benchmark measures decode"
+    torch.cuda.set_device(0)
+    inst = workload.make_instance(w)
+    run = workload.StackRunner(inst)
+    dev = inst.latent.device
+    stream = torch.cuda.current_stream()
+
+    # the new token's main-KV entry (a1): re-quantised into the last slot of each sequence
+    pos = torch.from_numpy(inst.lengths - 1).to(dev)
+    x_new = inst.latent[torch.from_numpy(inst.offsets[:-1] + inst.lengths - 1).to(dev)].contiguous()
+    scan_ev = []
+
+    def step(record_scan: bool):
+        st = run.state
+        st.c.has_idx = 0
+        st.c.has_pool = 0
+        api.csa2_fp4_append(x_new, pos, inst.cache)
+        for l, mode in enumerate(w.pattern):
+            L = inst.layers[l]
+            kw = dict(q=L["q"], q_idx=L["q_idx"], swa_kv=L["swa"], q_slot=inst.q_slot, window=w.window,
+                      sm_scale=inst.sm_scale, o=run.o[l], lse=run.lse[l], cache=inst.cache, kview=inst.kview,
+                      n_vis=inst.n_vis, n_max=inst.n_max, K=w.K, P=w.P, build_pool=True, ws=run.ws, state=st)
+            if mode == "F" and record_scan:
+                # the Full layer split at the scan so its kernel can be timed with events on this stream
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                api.csa2_index_full(L["q_idx"], inst.kview, inst.n_vis, inst.n_max, run.scan_scores,
+                                    run.scan_bmax)
+                e1.record(stream)
+                scan_ev.append((e0, e1))
+                api.csa2_topk(run.scan_scores, w.K, st.idx, ws=run.topk_ws)
+                api.csa2_topk(run.scan_bmax, w.P, st.pool, ws=run.topk_ws)
+                st.c.has_idx = 1
+                st.c.has_pool = 1
+                api.csa2_layer_forward("U", **kw)
+            else:
+                api.csa2_layer_forward(mode, **kw)
+
+    rows = inst.rows
+    nb = (inst.n_max + 7) // 8
+    run.scan_scores = torch.empty(rows, inst.n_max, dtype=torch.float32, device=dev)
+    run.scan_bmax = torch.empty(rows, nb, dtype=torch.float32, device=dev)
+    tk = max(api.csa2_topk_workspace_size(rows, inst.n_max, w.K), api.csa2_topk_workspace_size(rows, nb, w.P))
+    run.topk_ws = torch.empty(max(tk, 256), dtype=torch.uint8, device=dev)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    scan_ms = [a.elapsed_time(b) for a, b in scan_ev]
+    # extra back-to-back launches of the scan alone (same inputs) for a steadier kernel figure
+    ev = []
+    for _ in range(args.scan_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.csa2_index_full(inst.layers[0]["q_idx"], inst.kview, inst.n_vis, inst.n_max, run.scan_scores,
+                            run.scan_bmax)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    rep_ms = [a.elapsed_time(b) for a, b in ev]
+    scan_avg_ms = sum(scan_ms) / len(scan_ms)
+
+    n_total = int(inst.lengths.sum())
+    ab = alg_bytes(w, n_total)
+    qtok = rows / (ms_step / 1e3)
+    achieved = ab["full"] / (scan_avg_ms * 1e-3) / 1e9  # GB/s
+    out = {
+        "metric": "CSA2 decode query-tokens/s at 1M ctx; achieved HBM GB/s vs peak",
+        "value": round(qtok, 2),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1); FP4 cache quantised on the GPU)",
+        "config": {"workload": w.name, "B": w.B, "Q": w.Q, "N": inst.n_max, "pattern": w.pattern, "D": w.D,
+                   "H": w.H, "H_i": w.H_i, "D_i": w.D_i, "K": w.K, "pool": f"{w.P}x8", "window": w.window},
+        "step_alg_bytes": ab["total"],
+        "step_hbm_GBps": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "index_kernel<128,false> (Full-mode indexer scan)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": ab["full"], "avg_launch_ms": round(scan_avg_ms, 5),
+                     "avg_launch_ms_back_to_back": round(sum(rep_ms) / len(rep_ms), 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inst, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

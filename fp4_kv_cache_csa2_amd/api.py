@@ -1,0 +1,158 @@
+"""Thin Python binding of the CSA2 C ABI (include/csa2.h).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: PyTorch device tensors are passed as raw pointers, the stream is
+PyTorch's current stream.  Every step of the computation runs in libcsa2.so;
+a non-OK status raises Csa2Error with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import CSA2_BF16, CSA2_F32, CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, Csa2Error  # noqa: F401
+
+MODES = {"F": CSA2_FULL, "R": CSA2_REINDEX, "U": CSA2_REUSE}
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA2_F32
+    if t.dtype == torch.bfloat16:
+        return CSA2_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class Fp4Cache:
+    """FP4 main-KV cache planes: codes[rows][D/2] u8, scales[rows][D/16] u8.
+    Contiguous (page_table None, seq_stride entries per sequence) or paged."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    D: int
+    seq_stride: int = 0
+    page_table: torch.Tensor | None = None
+    page_size: int = 0
+
+    def view(self) -> _lib.Fp4KV:
+        mp = 0 if self.page_table is None else self.page_table.shape[1]
+        return _lib.Fp4KV(self.codes.data_ptr(), self.scales.data_ptr(), _ptr(self.page_table), self.page_size, mp,
+                          self.seq_stride, self.D)
+
+
+@dataclass
+class IndexerK:
+    """Indexer K plane k[rows][D_i] bf16, addressed like the FP4 cache."""
+    k: torch.Tensor
+    D_i: int
+    seq_stride: int = 0
+    page_table: torch.Tensor | None = None
+    page_size: int = 0
+
+    def view(self) -> _lib.IdxK:
+        mp = 0 if self.page_table is None else self.page_table.shape[1]
+        return _lib.IdxK(self.k.data_ptr(), _ptr(self.page_table), self.page_size, mp, self.seq_stride, self.D_i)
+
+
+def csa2_abi_version() -> int:
+    return _lib.load().csa2_abi_version()
+
+
+def csa2_fp4_quantize(x, codes, scales, stream=None):
+    rows, D = x.shape
+    _lib.check(_lib.load().csa2_fp4_quantize(_ptr(x), _dtype(x), rows, D, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def csa2_fp4_dequantize(codes, scales, y, stream=None):
+    rows, D = y.shape
+    _lib.check(_lib.load().csa2_fp4_dequantize(_ptr(codes), _ptr(scales), rows, D, _ptr(y), _stream(stream)))
+
+
+def csa2_fp4_append(x, pos, cache: Fp4Cache, stream=None):
+    v = cache.view()
+    _lib.check(_lib.load().csa2_fp4_append(_ptr(x), _dtype(x), x.shape[0], _ptr(pos), ctypes.byref(v),
+                                           _stream(stream)))
+
+
+def csa2_index_full(q_idx, kview: IndexerK, n_vis, n_max, scores, block_max=None, stream=None):
+    B, Q, H_i, _ = q_idx.shape
+    v = kview.view()
+    _lib.check(_lib.load().csa2_index_full(_ptr(q_idx), B, Q, H_i, ctypes.byref(v), _ptr(n_vis), n_max, _ptr(scores),
+                                           _ptr(block_max), _stream(stream)))
+
+
+def csa2_index_reindex(q_idx, kview: IndexerK, n_vis, pool_blocks, pool_scores, stream=None):
+    B, Q, H_i, _ = q_idx.shape
+    v = kview.view()
+    _lib.check(_lib.load().csa2_index_reindex(_ptr(q_idx), B, Q, H_i, ctypes.byref(v), _ptr(n_vis),
+                                              _ptr(pool_blocks), pool_blocks.shape[-1], _ptr(pool_scores),
+                                              _stream(stream)))
+
+
+def csa2_topk_workspace_size(rows, n, k) -> int:
+    return _lib.load().csa2_topk_workspace_size(rows, n, k)
+
+
+def csa2_topk(scores, k, out_idx, pool_blocks=None, ws=None, stream=None):
+    rows, n = scores.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().csa2_topk(_ptr(scores), rows, n, k, _ptr(pool_blocks), _ptr(out_idx), _ptr(ws), nbytes,
+                                     _stream(stream)))
+
+
+def csa2_attn_workspace_size(B, Q, H, D) -> int:
+    return _lib.load().csa2_attn_workspace_size(B, Q, H, D)
+
+
+def csa2_sparse_attn_fp4(q, cache: Fp4Cache, idx, sm_scale, o, lse, ws=None, stream=None):
+    B, Q, H, _ = q.shape
+    v = cache.view()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().csa2_sparse_attn_fp4(_ptr(q), _dtype(q), B, Q, H, ctypes.byref(v), _ptr(idx),
+                                                idx.shape[-1], float(sm_scale), _ptr(o), _ptr(lse), _ptr(ws), nbytes,
+                                                _stream(stream)))
+
+
+def csa2_swa_attn(q, swa_kv, q_slot, window, sm_scale, merge, o, lse, ws=None, stream=None):
+    B, Q, H, D = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(_lib.load().csa2_swa_attn(_ptr(q), _dtype(q), B, Q, H, D, _ptr(swa_kv), swa_kv.shape[1], _ptr(q_slot),
+                                         window, float(sm_scale), int(merge), _ptr(o), _ptr(lse), _ptr(ws), nbytes,
+                                         _stream(stream)))
+
+
+def csa2_layer_workspace_size(B, Q, H, D, n_max, K, P) -> int:
+    return _lib.load().csa2_layer_workspace_size(B, Q, H, D, n_max, K, P)
+
+
+class GroupState:
+    """Device buffers + host flags shared by the layers of one pattern."""
+
+    def __init__(self, rows: int, K: int, P: int, device):
+        self.idx = torch.empty(rows, K, dtype=torch.int32, device=device)
+        self.pool = torch.empty(rows, max(P, 1), dtype=torch.int32, device=device)
+        self.c = _lib.GroupState(self.idx.data_ptr(), self.pool.data_ptr(), 0, 0)
+
+
+def csa2_layer_forward(mode: str, *, q, q_idx, swa_kv, q_slot, window, sm_scale, o, lse, cache: Fp4Cache,
+                       kview: IndexerK, n_vis, n_max, K, P, build_pool, ws, state: GroupState, stream=None):
+    B, Q, H, _ = q.shape
+    H_i = 0 if q_idx is None else q_idx.shape[2]
+    kv, kk = cache.view(), kview.view()
+    a = _lib.LayerArgs(B, Q, H, H_i, K, P, q.data_ptr(), _dtype(q), _ptr(q_idx), swa_kv.data_ptr(), swa_kv.shape[1],
+                       q_slot.data_ptr(), window, float(sm_scale), o.data_ptr(), lse.data_ptr(), ctypes.pointer(kv),
+                       ctypes.pointer(kk), _ptr(n_vis), n_max, int(build_pool), ws.data_ptr(),
+                       ws.numel() * ws.element_size())
+    _lib.check(_lib.load().csa2_layer_forward(MODES[mode], ctypes.byref(a), ctypes.byref(state.c), _stream(stream)))

@@ -184,6 +184,35 @@ def attention(q: np.ndarray, codes: np.ndarray | None, scales: np.ndarray | None
 
 
 # ----------------------------------------------------------------------------- layer schedule
+def select_stack(pattern: str, K_idx: np.ndarray, n_vis: int, q_idx: list, K: int = 512, pool_blocks: int = 2048):
+    """Selection half of the layer schedule for one query row: the Top-K index
+    list each layer attends with (and the pool built by the Full layer).
+
+    Full scores every visible entry and selects a new Top-K (plus the pool of
+    the best ``pool_blocks`` 8-entry blocks when the pattern holds a Reindex
+    layer); Reindex scores only the pool positions with its own indexer query
+    and selects a new Top-K; Reuse takes the most recent selection."""
+    need_pool = "R" in pattern
+    idx, pool, out = None, None, []
+    for mode, qi in zip(pattern, q_idx):
+        if mode == "F":
+            s = index_scores(qi, K_idx, n_vis)
+            idx = topk(s, K)
+            if need_pool:
+                pool = build_pool(s, pool_blocks)
+        elif mode == "R":
+            if pool is None:
+                raise ValueError("Reindex layer before any Full layer built a pool")
+            idx = topk(reindex_scores(qi, K_idx, n_vis, pool), K, pool)
+        elif mode == "U":
+            if idx is None:
+                raise ValueError("Reuse layer before any selection")
+        else:
+            raise ValueError(f"unknown mode {mode!r}")
+        out.append(idx)
+    return out, pool
+
+
 def run_stack(pattern: str, seq: dict, layers: list[dict], K: int = 512, pool_blocks: int = 2048,
               window: int = 128, sm_scale: float | None = None, attn_heads: slice | None = None):
     """Run a static Full/Reindex/Reuse pattern (characters F, R, U) for ONE
@@ -204,28 +233,13 @@ def run_stack(pattern: str, seq: dict, layers: list[dict], K: int = 512, pool_bl
     D = seq["codes"].shape[1] * 2
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(D)
-    need_pool = "R" in pattern
-    out, idx, pool = [], None, None
-    for mode, L in zip(pattern, layers):
-        rec = {}
-        if mode == "F":
-            s = index_scores(L["q_idx"], seq["K_idx"], n_vis)
-            idx = topk(s, K)
-            if need_pool:
-                pool = build_pool(s, pool_blocks)
-                rec["pool"] = pool
-        elif mode == "R":
-            if pool is None:
-                raise ValueError("Reindex layer before any Full layer built a pool")
-            ps = reindex_scores(L["q_idx"], seq["K_idx"], n_vis, pool)
-            idx = topk(ps, K, pool)
-        elif mode == "U":
-            if idx is None:
-                raise ValueError("Reuse layer before any selection")
-        else:
-            raise ValueError(f"unknown mode {mode!r}")
+    sel, pool = select_stack(pattern, seq["K_idx"], n_vis, [L.get("q_idx") for L in layers], K, pool_blocks)
+    out = []
+    for mode, L, idx in zip(pattern, layers, sel):
         q = L["q"] if attn_heads is None else L["q"][attn_heads]
         o, lse = attention(q, seq["codes"], seq["scales"], idx, L["swa"], L["slot"], window, sm_scale)
-        rec.update(idx=idx.copy(), o=o, lse=lse)
+        rec = dict(idx=idx.copy(), o=o, lse=lse)
+        if mode == "F" and pool is not None:
+            rec["pool"] = pool
         out.append(rec)
     return out

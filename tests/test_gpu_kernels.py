@@ -1,0 +1,261 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle on seeded inputs:
+bit-exact FP4 codes, scores, Top-K and pool indices; attention within the
+row-wise 2e-3 tolerance.  Sizes span several tiles plus ragged tails."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_kv_cache_csa2_amd import api, inputs
+from gpu_common import assert_attn_close, case, require_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    oracle.build(force=False)
+
+
+# --------------------------------------------------------------------------- FP4 codec
+def _codec_inputs(rows, D, tag):
+    x = inputs.normal((rows, D), tag)
+    # spread group magnitudes over the whole E4M3 range, incl. subnormal scales and saturation
+    mag = torch.exp(inputs.uniform((rows, D // 16), tag + "/mag") * 40 - 25).float()
+    x = x * mag.repeat_interleave(16, 1)
+    x[0, :16] = 0.0
+    x[0, 16:32] = -0.0
+    x[1, :16] = torch.tensor([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0,
+                              0.5])  # exact E2M1 ties at scale 1
+    x[2, :16] = 1e30  # saturated scale
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fp4_quantize_bit_exact(dtype):
+    rows, D = 1037, 512
+    x = _codec_inputs(rows, D, "codec").to(dtype)
+    case(f"fp4_quantize rows={rows} D={D} {dtype}")
+    codes = torch.empty(rows, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(rows, D // 16, dtype=torch.uint8, device=DEV)
+    api.csa2_fp4_quantize(x.to(DEV), codes, scales)
+    y = torch.empty(rows, D, dtype=torch.float32, device=DEV)
+    api.csa2_fp4_dequantize(codes, scales, y)
+    torch.cuda.synchronize()
+    rc, rs = oracle.fp4_encode(x.float().numpy())
+    np.testing.assert_array_equal(to_np(scales), rs)
+    np.testing.assert_array_equal(to_np(codes), rc)
+    np.testing.assert_array_equal(to_np(y).astype(np.float64), oracle.fp4_decode(rc, rs))
+
+
+def test_fp4_append_paged():
+    B, D, ps = 5, 256, 64
+    lengths = np.array([100, 64, 3, 200, 128])
+    table, n_pages = inputs.random_page_table(lengths, ps, "app")
+    codes = torch.zeros(n_pages * ps, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(n_pages * ps, D // 16, dtype=torch.uint8, device=DEV)
+    cache = api.Fp4Cache(codes, scales, D, 0, torch.from_numpy(table).to(DEV), ps)
+    x = inputs.normal((B, D), "appx")
+    pos = np.array([99, 0, 2, 150, 127], np.int32)
+    case("fp4_append paged")
+    api.csa2_fp4_append(x.to(DEV), torch.from_numpy(pos).to(DEV), cache)
+    torch.cuda.synchronize()
+    rc, rs = oracle.fp4_encode(x.numpy())
+    for b in range(B):
+        r = table[b, pos[b] // ps] * ps + pos[b] % ps
+        np.testing.assert_array_equal(to_np(codes[r]), rc[b])
+        np.testing.assert_array_equal(to_np(scales[r]), rs[b])
+    assert int(codes.count_nonzero()) <= B * D // 2  # nothing else written
+
+
+# --------------------------------------------------------------------------- indexer
+def _k_view(B, n_max, D_i, tag, paged):
+    K = inputs.normal((B, n_max, D_i), tag, dtype=torch.bfloat16)
+    if not paged:
+        return K, api.IndexerK(K.reshape(B * n_max, D_i).to(DEV), D_i, n_max)
+    ps = 64
+    table, n_pages = inputs.random_page_table(np.full(B, n_max), ps, tag + "/pt")
+    phys = torch.zeros(n_pages * ps, D_i, dtype=torch.bfloat16)
+    for b in range(B):
+        for j0 in range(0, n_max, ps):
+            r = table[b, j0 // ps] * ps
+            phys[r:r + min(ps, n_max - j0)] = K[b, j0:j0 + ps]
+    return K, api.IndexerK(phys.to(DEV), D_i, 0, torch.from_numpy(table).to(DEV), ps)
+
+
+@pytest.mark.parametrize("D_i,H_i,paged", [(128, 8, False), (64, 4, False), (128, 8, True)])
+def test_index_full_bit_exact(D_i, H_i, paged):
+    B, Q, n_max = 2, 3, 5000
+    K, kview = _k_view(B, n_max, D_i, f"ifK{D_i}{paged}", paged)
+    q = inputs.normal((B, Q, H_i, D_i), f"ifq{D_i}", dtype=torch.bfloat16)
+    n_vis = np.array([[5000, 4999, 0], [1, 257, 3333]], np.int32)
+    scores = torch.empty(B * Q, n_max, device=DEV)
+    nb = (n_max + 7) // 8
+    bmax = torch.empty(B * Q, nb, device=DEV)
+    case(f"index_full D_i={D_i} paged={paged}")
+    api.csa2_index_full(q.to(DEV), kview, torch.from_numpy(n_vis).to(DEV), n_max, scores, bmax)
+    torch.cuda.synchronize()
+    s, bm = to_np(scores), to_np(bmax)
+    for b in range(B):
+        Kb = inputs.bf16_bits(K[b])
+        for qq in range(Q):
+            ref = oracle.index_scores(inputs.bf16_bits(q[b, qq]), Kb, n_vis[b, qq])
+            np.testing.assert_array_equal(s[b * Q + qq], ref)
+            np.testing.assert_array_equal(bm[b * Q + qq], oracle.block_max(ref))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_index_reindex_bit_exact(paged):
+    B, n_max, D_i, H_i, P = 2, 40000, 128, 8, 700
+    K, kview = _k_view(B, n_max, D_i, f"riK{paged}", paged)
+    q = inputs.normal((B, 1, H_i, D_i), "riq", dtype=torch.bfloat16)
+    n_vis = np.array([[40000], [39990]], np.int32)
+    pool = np.full((B, P), -1, np.int32)
+    rng = np.random.default_rng(0)
+    pool[0, :600] = np.sort(rng.choice(5000, 600, replace=False))
+    pool[1, :P] = np.sort(rng.choice(5000, P, replace=False))
+    pool[1, -1] = 4999  # block 4999 holds entries 39992.. -> partly invisible
+    ps = torch.empty(B, 8 * P, device=DEV)
+    case(f"index_reindex paged={paged}")
+    api.csa2_index_reindex(q.to(DEV), kview, torch.from_numpy(n_vis).to(DEV), torch.from_numpy(pool).to(DEV), ps)
+    torch.cuda.synchronize()
+    got = to_np(ps)
+    for b in range(B):
+        ref = oracle.reindex_scores(inputs.bf16_bits(q[b, 0]), inputs.bf16_bits(K[b]), n_vis[b, 0], pool[b])
+        np.testing.assert_array_equal(got[b], ref)
+
+
+# --------------------------------------------------------------------------- Top-K
+def _topk_case(rows, n, k, kind, tag):
+    if kind == "normal":
+        s = inputs.normal((rows, n), tag).numpy() * 30
+    elif kind == "ties":
+        s = inputs.small_ints((rows, n), tag, -40, 40, dtype=torch.float32).numpy()
+    else:  # "flat": one value everywhere -> the threshold bin overflows any candidate buffer
+        s = np.full((rows, n), 1.5, np.float32)
+        s[:, ::5] = 2.5
+    s[:, ::11] = -np.inf
+    if rows > 1:
+        s[1, 100:] = -np.inf  # a row with few valid entries
+    return s
+
+
+@pytest.mark.parametrize("rows,n,k,kind", [
+    (3, 1, 512, "normal"), (4, 700, 512, "ties"), (2, 16384, 512, "normal"), (5, 16384, 2048, "ties"),
+    (3, 16385, 512, "normal"), (4, 100000, 512, "ties"), (4, 100000, 1, "normal"), (2, 300000, 2048, "normal"),
+    (2, 70000, 512, "flat"), (1, 1 << 20, 512, "normal")])
+def test_topk_bit_exact(rows, n, k, kind):
+    s = _topk_case(rows, n, k, kind, f"tk{rows}_{n}_{k}_{kind}")
+    out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
+    nbytes = api.csa2_topk_workspace_size(rows, n, k)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    case(f"topk rows={rows} n={n} k={k} {kind}")
+    api.csa2_topk(torch.from_numpy(s).to(DEV), k, out, ws=ws)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], oracle.topk(s[r], k), err_msg=f"row {r}")
+
+
+def test_topk_with_pool_map():
+    rows, P, k = 3, 2048, 512
+    n = 8 * P
+    s = inputs.normal((rows, n), "tkpool").numpy()
+    pool = np.full((rows, P), -1, np.int32)
+    rng = np.random.default_rng(1)
+    for r in range(rows):
+        nb = [2048, 1500, 10][r]
+        pool[r, :nb] = np.sort(rng.choice(200000, nb, replace=False))
+        s[r, 8 * nb:] = -np.inf
+    out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
+    case("topk pool map")
+    api.csa2_topk(torch.from_numpy(s).to(DEV), k, out, pool_blocks=torch.from_numpy(pool).to(DEV))
+    torch.cuda.synchronize()
+    for r in range(rows):
+        np.testing.assert_array_equal(to_np(out)[r], oracle.topk(s[r], k, pool[r]))
+
+
+def test_topk_deterministic_and_workspace_reuse():
+    rows, n, k = 4, 200000, 512
+    s = torch.from_numpy(_topk_case(rows, n, k, "ties", "det")).to(DEV)
+    ws = torch.empty(api.csa2_topk_workspace_size(rows, n, k), dtype=torch.uint8, device=DEV)
+    outs = []
+    case("topk determinism")
+    for _ in range(3):
+        o = torch.empty(rows, k, dtype=torch.int32, device=DEV)
+        api.csa2_topk(s, k, o, ws=ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+# --------------------------------------------------------------------------- attention
+def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
+    lat = inputs.normal((B, n, D), tag + "/lat")
+    codes = torch.empty(B * n, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(B * n, D // 16, dtype=torch.uint8, device=DEV)
+    api.csa2_fp4_quantize(lat.reshape(B * n, D).to(DEV), codes, scales)
+    cache = api.Fp4Cache(codes, scales, D, n)
+    q = inputs.normal((B, Q, H, D), tag + "/q", dtype=qdtype)
+    idx = inputs.small_ints((B, Q, K), tag + "/idx", -1, n - 1, dtype=torch.int32)
+    swa = inputs.normal((B, T, D), tag + "/swa", dtype=torch.bfloat16)
+    slot = inputs.small_ints((B, Q), tag + "/slot", 0, T - 1, dtype=torch.int32)
+    rc, rs = oracle.fp4_encode(lat.reshape(B * n, D).numpy())
+    return cache, q, idx, swa, slot, rc.reshape(B, n, -1), rs.reshape(B, n, -1)
+
+
+@pytest.mark.parametrize("B,Q,H,D,K,qdtype", [
+    (2, 1, 64, 512, 512, torch.bfloat16), (1, 1, 16, 128, 512, torch.float32), (3, 2, 32, 256, 100, torch.bfloat16),
+    (600, 1, 16, 128, 48, torch.bfloat16)])
+def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype):
+    n, T, window = 3000, 200, 128
+    cache, q, idx, swa, slot, rc, rs = _attn_inputs(B, Q, H, D, n, K, T, qdtype, f"at{B}{H}{D}{K}")
+    sc = 1 / math.sqrt(D)
+    o = torch.empty(B, Q, H, D, device=DEV)
+    lse = torch.empty(B, Q, H, device=DEV)
+    ws = torch.empty(max(api.csa2_attn_workspace_size(B, Q, H, D), 16), dtype=torch.uint8, device=DEV)
+    case(f"sparse_attn B={B} Q={Q} H={H} D={D} K={K}")
+    api.csa2_sparse_attn_fp4(q.to(DEV), cache, idx.to(DEV), sc, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    o1, l1 = to_np(o), to_np(lse)
+    case("swa_attn merge")
+    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), slot.to(DEV), window, sc, 1, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    o2, l2 = to_np(o), to_np(lse)
+    qn = q.double().numpy()
+    sw = swa.double().numpy()
+    worst = 0.0
+    for b in range(B):
+        for qq in range(Q):
+            ra, la = oracle.attention(qn[b, qq], rc[b], rs[b], idx[b, qq].numpy(), None, 0, 0, sc)
+            worst = max(worst, assert_attn_close(o1[b, qq], l1[b, qq], ra, la, "sparse"))
+            ru, lu = oracle.attention(qn[b, qq], rc[b], rs[b], idx[b, qq].numpy(), sw[b], int(slot[b, qq]), window, sc)
+            worst = max(worst, assert_attn_close(o2[b, qq], l2[b, qq], ru, lu, "merged"))
+    print(f"worst row-relative error {worst:.2e}")
+
+
+def test_swa_only_short_window_and_empty_sparse():
+    B, Q, H, D, T = 2, 1, 64, 512, 128
+    cache, q, idx, swa, slot, rc, rs = _attn_inputs(B, Q, H, D, 100, 16, T, torch.bfloat16, "swo")
+    slot = torch.tensor([[0], [5]], dtype=torch.int32)  # first tokens: windows of 1 and 6 rows
+    idx[:] = -1  # no selected entries at all
+    sc = 0.05
+    o = torch.empty(B, Q, H, D, device=DEV)
+    lse = torch.empty(B, Q, H, device=DEV)
+    ws = torch.empty(api.csa2_attn_workspace_size(B, Q, H, D), dtype=torch.uint8, device=DEV)
+    case("sparse with empty selection")
+    api.csa2_sparse_attn_fp4(q.to(DEV), cache, idx.to(DEV), sc, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(lse)) and torch.all(o == 0)
+    case("swa merge after empty sparse")
+    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), slot.to(DEV), 128, sc, 1, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref, lr = oracle.attention(q[b, 0].double().numpy(), None, None, None, swa[b].double().numpy(),
+                                   int(slot[b, 0]), 128, sc)
+        assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ref, lr, "swa-only")
