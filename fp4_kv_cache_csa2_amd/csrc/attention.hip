@@ -18,7 +18,7 @@
 // MFMA, so P never leaves registers.  Softmax is online (running max / sum in
 // the log2 domain).  Few rows (decode) split the keys over several workgroups
 // whose normalised partials (o, lse) are merged by a second kernel.
-#include "common.h"
+#include "internal.h"
 
 namespace csa2 {
 namespace {
@@ -69,23 +69,119 @@ __device__ __forceinline__ float e2m1_val(uint32_t code) {
 // byte offset of V^T[d][key 4kq] inside the padded transposed tile
 __device__ __forceinline__ int vt_off(int d, int kq) { return d * 32 + (d >> 3) * 16 + kq * 8; }
 
-template <int D, bool QF32>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+constexpr int MAX_CPS = 64;  // chunks per split (keys per workgroup <= 1024)
+
+// Raw data of one dequantisation item (4 keys x 8 channels): FP4 code words and
+// scale bytes, or 4 x 8 bf16 window channels.
+struct RawItem {
+    uint4 w[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_item(const AttnParams& p, bool sparse, const int64_t* krow, int kq, int co,
+                                          RawItem& raw) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = krow[4 * kq + i];
+        if (r < 0) {
+            raw.w[i] = make_uint4(0, 0, 0, 0);
+        } else if (sparse) {
+            raw.w[i].x = *reinterpret_cast<const uint32_t*>(p.codes + r * (D / 2) + co * 4);
+            raw.w[i].y = p.scales[r * (D / 16) + (co >> 1)];
+        } else {
+            raw.w[i] = *reinterpret_cast<const uint4*>(p.swa + r * D + co * 8);
+        }
+    }
+}
+
+// Dequantise one item into the K tile (bf16, row-major, swizzled) and the V^T
+// tile (fp16, transposed, padded).
+template <int D>
+__device__ __forceinline__ void store_item(bool sparse, const RawItem& raw, int kq, int co, uint4* ktile,
+                                           uint8_t* vtile) {
+    constexpr int CPR = D / 8;
+    uint32_t kb16[4][4];
+    uint16_t vh[8][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v[8];
+        if (sparse) {
+            const uint32_t cw = raw.w[i].x;
+            const float s = e4m3_val(raw.w[i].y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = e2m1_val((cw >> (4 * e)) & 15u) * s;
+        } else {
+            const uint32_t wv[4] = {raw.w[i].x, raw.w[i].y, raw.w[i].z, raw.w[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = bf16_lo(wv[e]);
+                v[2 * e + 1] = bf16_hi(wv[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            kb16[i][e] = (__float_as_uint(v[2 * e]) >> 16) | (__float_as_uint(v[2 * e + 1]) & 0xFFFF0000u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const _Float16 h = (_Float16)v[e];
+            vh[e][i] = *reinterpret_cast<const uint16_t*>(&h);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = 4 * kq + i;
+        ktile[key * CPR + (co ^ (key & 15))] = make_uint4(kb16[i][0], kb16[i][1], kb16[i][2], kb16[i][3]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int d = 8 * co + e;
+        *reinterpret_cast<uint2*>(vtile + vt_off(d, kq)) =
+            make_uint2((uint32_t)vh[e][0] | ((uint32_t)vh[e][1] << 16), (uint32_t)vh[e][2] | ((uint32_t)vh[e][3] << 16));
+    }
+}
+
+template <int D, bool QF32, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     constexpr int NBLK = D / 32;  // 32-channel blocks of the S MFMA
     constexpr int NDT = D / 16;   // 16-channel tiles of the O MFMA
     constexpr int CPR = D / 8;    // 16-byte chunks per bf16 key row
+    constexpr int NT = 64 * NW;
+    constexpr int ITEMS = 4 * CPR;                       // dequantisation items per chunk
+    constexpr int IPT = (ITEMS + NT - 1) / NT;           // items per thread
     __shared__ uint4 ktile[CHUNK_KEYS * CPR];
     __shared__ __attribute__((aligned(16))) uint8_t vtile[D * 32 + (D / 8) * 16];
-    __shared__ int64_t krow[CHUNK_KEYS];
-    __shared__ uint32_t kvalid;
+    __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
 
-    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t row = blockIdx.y;
     const int split = blockIdx.x;
     const int b = (int)(row / p.Q);
     const int head = 16 * w + c16;
+
+    const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
+    const int c_lo = split * p.cps;
+    const int c_hi = min(nchunks, c_lo + p.cps);
+    const int slot = p.Wp ? p.q_slot[row] : 0;
+    const int wlo = max(0, slot - p.window + 1);
+
+    // ---- physical rows of every key of this split (-1: none)
+    const int nk = max(0, c_hi - c_lo) * CHUNK_KEYS;
+    for (int i = tid; i < nk; i += NT) {
+        const int kpos = c_lo * CHUNK_KEYS + i;
+        int64_t r = -1;
+        if (kpos < p.Kp) {
+            if (kpos < p.K) {
+                const int32_t e = p.idx[row * p.K + kpos];
+                if (e >= 0) r = phys_row(p.kvmap, b, e);
+            }
+        } else {
+            const int t = wlo + (kpos - p.Kp);
+            if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
+        }
+        krow[i] = r;
+    }
 
     // ---- Q operand (B of S^T = K Q^T): Q[head][32*blk + 8g .. +8]
     bf16x8 qhi[NBLK];
@@ -113,89 +209,42 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         for (int blk = 0; blk < NBLK; ++blk)
             qhi[blk] = *reinterpret_cast<const bf16x8*>(qr + 32 * blk + 8 * g);
     }
+    __syncthreads();
 
     f32x4 oacc[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
-    const int c_lo = split * p.cps;
-    const int c_hi = min(nchunks, c_lo + p.cps);
-    const int slot = p.Wp ? p.q_slot[row] : 0;
-    const int wlo = max(0, slot - p.window + 1);
-
+    RawItem raw[IPT];
+    if (c_lo < c_hi) {
+        const bool sp = c_lo * CHUNK_KEYS < p.Kp;
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int item = it * NT + tid;
+            if (item < ITEMS) load_item<D>(p, sp, krow, item / CPR, item % CPR, raw[it]);
+        }
+    }
     for (int ch = c_lo; ch < c_hi; ++ch) {
         const int kb = ch * CHUNK_KEYS;
         const bool sparse = kb < p.Kp;
-        // ---- rows of the 16 keys of this chunk
-        if (tid < CHUNK_KEYS) {
-            int64_t r = -1;
-            if (sparse) {
-                const int pos = kb + tid;
-                if (pos < p.K) {
-                    const int32_t e = p.idx[row * p.K + pos];
-                    if (e >= 0) r = phys_row(p.kvmap, b, e);
-                }
-            } else {
-                const int t = wlo + (kb - p.Kp) + tid;
-                if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
-            }
-            krow[tid] = r;
-        }
-        if (tid == 0) kvalid = 0;
-        __syncthreads();
-        if (tid < CHUNK_KEYS && krow[tid] >= 0) atomicOr(&kvalid, 1u << tid);
-        // ---- gather + dequantise: item = (4 keys, 8 channels)
-        for (int item = tid; item < 4 * CPR; item += nthreads) {
-            const int kq = item / CPR, co = item % CPR;
-            uint32_t kb16[4][4];   // bf16 pairs for 4 keys x 8 channels
-            uint16_t vh[8][4];     // fp16 [channel][key]
+        const int64_t* kr = krow + (ch - c_lo) * CHUNK_KEYS;
+        // ---- dequantise the prefetched chunk into the LDS tiles
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t r = krow[4 * kq + i];
-                float v[8];
-                if (r < 0) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-                } else if (sparse) {
-                    const uint32_t cw = *reinterpret_cast<const uint32_t*>(p.codes + r * (D / 2) + co * 4);
-                    const float s = e4m3_val(p.scales[r * (D / 16) + (co >> 1)]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = e2m1_val((cw >> (4 * e)) & 15u) * s;
-                } else {
-                    const uint4 raw = *reinterpret_cast<const uint4*>(p.swa + r * D + co * 8);
-                    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[2 * e] = bf16_lo(wv[e]);
-                        v[2 * e + 1] = bf16_hi(wv[e]);
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    kb16[i][e] = (__float_as_uint(v[2 * e]) >> 16) | (__float_as_uint(v[2 * e + 1]) & 0xFFFF0000u);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const _Float16 h = (_Float16)v[e];
-                    vh[e][i] = *reinterpret_cast<const uint16_t*>(&h);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = 4 * kq + i;
-                ktile[key * CPR + (co ^ (key & 15))] = make_uint4(kb16[i][0], kb16[i][1], kb16[i][2], kb16[i][3]);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 8 * co + e;
-                *reinterpret_cast<uint2*>(vtile + vt_off(d, kq)) =
-                    make_uint2((uint32_t)vh[e][0] | ((uint32_t)vh[e][1] << 16),
-                               (uint32_t)vh[e][2] | ((uint32_t)vh[e][3] << 16));
-            }
+        for (int it = 0; it < IPT; ++it) {
+            const int item = it * NT + tid;
+            if (item < ITEMS) store_item<D>(sparse, raw[it], item / CPR, item % CPR, ktile, vtile);
         }
         __syncthreads();
-
+        // ---- the next chunk's loads fly during this chunk's MFMAs
+        if (ch + 1 < c_hi) {
+            const bool sp = (ch + 1) * CHUNK_KEYS < p.Kp;
+#pragma unroll
+            for (int it = 0; it < IPT; ++it) {
+                const int item = it * NT + tid;
+                if (item < ITEMS) load_item<D>(p, sp, kr + CHUNK_KEYS, item / CPR, item % CPR, raw[it]);
+            }
+        }
         // ---- S^T[key][head] = sum_d K[key][d] Q[head][d]
         f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -206,12 +255,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
             if (QF32) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[QF32 ? blk : 0], s, 0, 0, 0);
         }
         // ---- online softmax for head `head` over keys 4g..4g+3 of this chunk
-        const uint32_t vm = kvalid;
         float z[4];
         float mloc = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = ((vm >> (4 * g + i)) & 1u) ? s[i] * p.scale_log2 : -INFINITY;
+            z[i] = (kr[4 * g + i] >= 0) ? s[i] * p.scale_log2 : -INFINITY;
             mloc = fmaxf(mloc, z[i]);
         }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
@@ -291,36 +339,38 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 }
 
 // Merge the split partials of one (row, head): exact log-sum-exp combination,
-// optionally together with the (o, lse) already in the output.
-__global__ void attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse, int nsplit,
-                                  int H, int D, int merge, float* __restrict__ o, float* __restrict__ lse) {
+// optionally together with the (o, lse) already in the output.  All loads are
+// issued before any arithmetic.
+template <int NS>
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_lse, int nsplit, int H, int D,
+                                                         int merge, float* __restrict__ o, float* __restrict__ lse) {
     const int64_t row = blockIdx.x;
     const int h = blockIdx.y;
     const int c = threadIdx.x * 4;
-    float L = merge ? lse[row * H + h] : -INFINITY;
-    for (int s = 0; s < nsplit; ++s) L = fmaxf(L, part_lse[(row * nsplit + s) * H + h]);
+    float ls[NS + 1];
+    float4 ov[NS + 1];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        ls[s] = s < nsplit ? part_lse[(row * nsplit + s) * H + h] : -INFINITY;
+        ov[s] = s < nsplit ? *reinterpret_cast<const float4*>(part_o + ((row * nsplit + s) * H + h) * D + c)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    ls[NS] = merge ? lse[row * H + h] : -INFINITY;
+    ov[NS] = merge ? *reinterpret_cast<const float4*>(o + (row * H + h) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = -INFINITY;
+#pragma unroll
+    for (int s = 0; s <= NS; ++s) L = fmaxf(L, ls[s]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float tot = 0.0f;
     if (L != -INFINITY) {
-        if (merge) {
-            const float wv = expf(lse[row * H + h] - L);
-            if (wv != 0.0f) {
-                const float4 v = *reinterpret_cast<const float4*>(o + (row * H + h) * D + c);
-                acc.x += wv * v.x;
-                acc.y += wv * v.y;
-                acc.z += wv * v.z;
-                acc.w += wv * v.w;
-            }
-            tot += wv;
-        }
-        for (int s = 0; s < nsplit; ++s) {
-            const float wv = expf(part_lse[(row * nsplit + s) * H + h] - L);
-            if (wv == 0.0f) continue;
-            const float4 v = *reinterpret_cast<const float4*>(part_o + ((row * nsplit + s) * H + h) * D + c);
-            acc.x += wv * v.x;
-            acc.y += wv * v.y;
-            acc.z += wv * v.z;
-            acc.w += wv * v.w;
+#pragma unroll
+        for (int s = 0; s <= NS; ++s) {
+            const float wv = (ls[s] == -INFINITY) ? 0.0f : expf(ls[s] - L);
+            acc.x += wv * ov[s].x;
+            acc.y += wv * ov[s].y;
+            acc.z += wv * ov[s].z;
+            acc.w += wv * ov[s].w;
             tot += wv;
         }
     }
@@ -338,7 +388,8 @@ int choose_nsplit(int64_t rows, int nchunks) {
     int64_t by_chunks = (nchunks + 1) / 2;   // at least two chunks per split
     int64_t s = want < by_chunks ? want : by_chunks;
     if (s > MAX_SPLIT) s = MAX_SPLIT;
-    return s < 1 ? 1 : (int)s;
+    if (s < 1) s = 1;
+    return (int)s;
 }
 
 size_t attn_ws_bytes(int64_t rows, int H, int D) {
@@ -399,6 +450,8 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
     p.nsplit = choose_nsplit(rows, nchunks);
     p.cps = nchunks > 0 ? (nchunks + p.nsplit - 1) / p.nsplit : 0;
+    CSA2_REQUIRE(p.cps <= MAX_CPS, CSA2_EUNSUPPORTED, "%s: %d keys per query need more than %d splits", what,
+                 nchunks * CHUNK_KEYS, MAX_SPLIT);
     if (p.nsplit > 1) {
         const size_t need = (size_t)(rows * p.nsplit * H) * (size_t)(D + 1) * 4;
         CSA2_REQUIRE(ws != nullptr && ws_bytes >= need, CSA2_EWORKSPACE,
@@ -410,20 +463,34 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     const dim3 grid((unsigned)p.nsplit, (unsigned)rows);
     const dim3 block((unsigned)(4 * H));
     const bool f32 = qt == CSA2_F32;
-#define CSA2_ATTN(DD)                                                        \
-    if (D == DD) {                                                           \
-        if (f32)                                                             \
-            attn_kernel<DD, true><<<grid, block, 0, stream>>>(p);            \
-        else                                                                 \
-            attn_kernel<DD, false><<<grid, block, 0, stream>>>(p);           \
+    const int nw = H / 16;
+#define CSA2_ATTN_NW(DD, F, NWV) \
+    if (nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
+#define CSA2_ATTN(DD)                                                                                   \
+    if (D == DD) {                                                                                      \
+        if (f32) {                                                                                      \
+            CSA2_ATTN_NW(DD, true, 1) CSA2_ATTN_NW(DD, true, 2) CSA2_ATTN_NW(DD, true, 3)               \
+            CSA2_ATTN_NW(DD, true, 4)                                                                   \
+        } else {                                                                                        \
+            CSA2_ATTN_NW(DD, false, 1) CSA2_ATTN_NW(DD, false, 2) CSA2_ATTN_NW(DD, false, 3)            \
+            CSA2_ATTN_NW(DD, false, 4)                                                                  \
+        }                                                                                               \
     }
     CSA2_ATTN(128)
     CSA2_ATTN(256)
     CSA2_ATTN(512)
 #undef CSA2_ATTN
-    if (p.nsplit > 1)
-        attn_merge_kernel<<<dim3((unsigned)rows, (unsigned)H), dim3((unsigned)(D / 4)), 0, stream>>>(
-            p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o, lse);
+#undef CSA2_ATTN_NW
+    if (p.nsplit > 1) {
+        const dim3 mg((unsigned)rows, (unsigned)H), mb((unsigned)(D / 4));
+        if (p.nsplit <= 4)
+            attn_merge_kernel<4><<<mg, mb, 0, stream>>>(p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o, lse);
+        else if (p.nsplit <= 8)
+            attn_merge_kernel<8><<<mg, mb, 0, stream>>>(p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o, lse);
+        else
+            attn_merge_kernel<MAX_SPLIT><<<mg, mb, 0, stream>>>(p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o,
+                                                                lse);
+    }
     return launch_status(what);
 }
 

@@ -7,21 +7,15 @@
 //   Reuse   : no indexer; the latest Top-K is attended again.
 // Every layer then attends with its own main query over the selected FP4
 // entries and its own window rows in one fused kernel.
-#include "common.h"
+#include "internal.h"
 
 namespace csa2 {
-csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
-                        const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,
-                        const int32_t* q_slot, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
-                        void* ws, size_t ws_bytes, hipStream_t stream, const char* what);
-size_t attn_workspace_bytes(int64_t rows, int H, int D);
-
 namespace {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct LayerWs {
-    size_t scores, block_max, pool_scores, topk, attn, total;
+    size_t scores, block_max, pool_scores, topk, rhist, rstate, attn, total;
     size_t topk_bytes, attn_bytes;
 };
 
@@ -35,14 +29,16 @@ LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
     off = align256(off + (size_t)(rows * nblocks) * 4);
     w.pool_scores = off;
     off = align256(off + (size_t)(rows * 8 * (int64_t)P) * 4);
-    size_t tk = csa2_topk_workspace_size((int32_t)rows, (int32_t)n_max, K);
-    const size_t tk2 = csa2_topk_workspace_size((int32_t)rows, (int32_t)nblocks, P);
-    const size_t tk3 = csa2_topk_workspace_size((int32_t)rows, 8 * P, K);
-    if (tk2 > tk) tk = tk2;
-    if (tk3 > tk) tk = tk3;
+    // two selections (entries, pool blocks) may run side by side
+    const size_t tk = (n_max > TOPK_SMALL_N || 8 * (int64_t)P > TOPK_SMALL_N) ? 2 * topk_large_ws_bytes(rows) : 0;
     w.topk = off;
     w.topk_bytes = tk;
     off = align256(off + tk);
+    // first-digit histogram of the Reindex pool scores (kept zeroed between uses)
+    w.rhist = off;
+    off = align256(off + (size_t)rows * NBINS1 * 4);
+    w.rstate = off;
+    off = align256(off + (size_t)rows * sizeof(TopkRowState));
     w.attn = off;
     w.attn_bytes = attn_workspace_bytes(rows, H, D);
     off = align256(off + w.attn_bytes);
@@ -83,7 +79,11 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     if (indexer) CSA2_ARG(a->q_idx != nullptr && a->n_vis != nullptr, "layer_forward: null q_idx / n_vis");
     const int64_t rows = (int64_t)a->B * a->Q;
     if (rows == 0) return CSA2_OK;
-    const LayerWs w = layer_ws(rows, a->H, a->kv->D, a->n_max, a->K, pool ? a->P : 0);
+    // the layout depends only on the shapes, never on the mode: every layer of a
+    // group passes the same P and shares the workspace (and the zeroed Reindex
+    // histogram kept in it)
+    CSA2_ARG(a->P >= 0 && a->P <= 2048, "layer_forward: P=%d must be in [0, 2048]", a->P);
+    const LayerWs w = layer_ws(rows, a->H, a->kv->D, a->n_max, a->K, a->P);
     CSA2_REQUIRE(a->ws != nullptr && a->ws_bytes >= w.total, CSA2_EWORKSPACE,
                  "layer_forward: workspace of %zu bytes required, %zu given", w.total,
                  a->ws ? a->ws_bytes : (size_t)0);
@@ -93,20 +93,61 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     float* block_max = reinterpret_cast<float*>(ws + w.block_max);
     float* pool_scores = reinterpret_cast<float*>(ws + w.pool_scores);
     void* tk = ws + w.topk;
+    uint32_t* rhist = reinterpret_cast<uint32_t*>(ws + w.rhist);
+    TopkRowState* rstate = reinterpret_cast<TopkRowState*>(ws + w.rstate);
+    (void)w.topk_bytes;
     void* aw = ws + w.attn;
     const int rows32 = (int)rows;
     csa2_status s = CSA2_OK;
     if (mode == CSA2_FULL) {
-        s = csa2_index_full(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, a->n_max, scores,
-                            a->build_pool ? block_max : nullptr, stream);
-        if (s == CSA2_OK) s = csa2_topk(scores, rows32, a->n_max, a->K, nullptr, st->idx, tk, w.topk_bytes, stream);
-        if (s == CSA2_OK && a->build_pool)
-            s = csa2_topk(block_max, rows32, (int32_t)((a->n_max + 7) / 8), a->P, nullptr, st->pool, tk,
-                          w.topk_bytes, stream);
+        // Top-K entries and pool blocks: large selections share the zero /
+        // split / finish launches; their first-digit histograms come out of the scan
+        const int32_t n = a->n_max, nb = (int32_t)((a->n_max + 7) / 8);
+        const bool e_large = n > TOPK_SMALL_N;
+        const bool b_large = a->build_pool && nb > TOPK_SMALL_N;  // implies e_large
+        TopkSegs segs{};
+        segs.rows = rows32;
+        TopkSeg* se = nullptr;
+        TopkSeg* sb = nullptr;
+        if (e_large) {
+            se = &segs.seg[segs.nseg++];
+            *se = TopkSeg{scores, n, a->K, nullptr, st->idx};
+            topk_carve(tk, rows, se);
+        }
+        if (b_large) {
+            sb = &segs.seg[segs.nseg++];
+            *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool};
+            topk_carve(static_cast<char*>(tk) + topk_large_ws_bytes(rows), rows, sb);
+        }
+        ZeroRanges z{};
+        for (int i = 0; i < segs.nseg; ++i) {
+            z.ptr[z.n] = segs.seg[i].hist;
+            z.count[z.n++] = rows * NBINS1;
+            z.ptr[z.n] = reinterpret_cast<uint32_t*>(segs.seg[i].state);
+            z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
+        }
+        if (a->build_pool) {  // the Reindex layers that follow start from a clean histogram
+            z.ptr[z.n] = rhist;
+            z.count[z.n++] = rows * NBINS1;
+            z.ptr[z.n] = reinterpret_cast<uint32_t*>(rstate);
+            z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
+        }
+        launch_zero_ranges(z, stream);
+        s = index_full_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, n, scores,
+                            a->build_pool ? block_max : nullptr, se ? se->hist : nullptr, se ? se->state : nullptr,
+                            sb ? sb->hist : nullptr, sb ? sb->state : nullptr, stream);
+        if (s != CSA2_OK) return s;
+        if (segs.nseg) topk_launch_select(segs, stream);
+        if (!e_large) topk_launch_small(scores, rows32, n, a->K, nullptr, st->idx, stream);
+        if (a->build_pool && !b_large) topk_launch_small(block_max, rows32, nb, a->P, nullptr, st->pool, stream);
+        s = launch_status("layer_forward");
     } else if (mode == CSA2_REINDEX) {
-        s = csa2_index_reindex(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, st->pool, a->P, pool_scores, stream);
-        if (s == CSA2_OK)
-            s = csa2_topk(pool_scores, rows32, 8 * a->P, a->K, st->pool, st->idx, tk, w.topk_bytes, stream);
+        s = index_reindex_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, st->pool, a->P, pool_scores, rhist,
+                               rstate, stream);
+        if (s == CSA2_OK) {
+            topk_launch_small(pool_scores, rows32, 8 * a->P, a->K, st->pool, st->idx, stream, rhist, rstate);
+            s = launch_status("layer_forward");
+        }
     }
     if (s != CSA2_OK) return s;
     if (mode == CSA2_FULL) {

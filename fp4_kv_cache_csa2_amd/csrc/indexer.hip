@@ -10,17 +10,20 @@
 // definition: the Top-K that follows is an integer result decided by these
 // fp32 values, so it must be reproduced exactly, not approximately.
 //
-// Work decomposition: a 256-thread workgroup takes tiles of 256 entries.  The
-// tile (64 KB at D_i = 128) is read with fully coalesced 16-byte loads and
-// written to LDS with a 16-byte XOR swizzle; each thread then reads back one
-// whole entry (conflict-free) and runs its FMA chain.  8 consecutive lanes hold
-// an aligned 8-entry block, so the block max for the pool is three lane shuffles.
-#include "common.h"
+// Work decomposition: every wavefront streams its own blocks of 64 entries
+// (16 KB at D_i = 128) with no workgroup barrier in the loop.  A block is
+// read with fully coalesced 16-byte loads into registers, written to the
+// wave's private LDS tile with a 16-byte XOR swizzle, and read back one whole
+// entry per lane (conflict-free); the loads of the wave's next block are in
+// flight while the current one is scored.  8 consecutive lanes hold an
+// aligned 8-entry block, so the block max for the pool is three lane shuffles.
+#include "internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int TILE = 256;
+constexpr int WAVES = 4;      // wavefronts per workgroup
+constexpr int EPB = 64;       // entries per wave block (one per lane)
 
 struct IndexParams {
     const uint16_t* q_idx;     // [rows][H_i][DI]
@@ -33,17 +36,80 @@ struct IndexParams {
     int32_t P;
     float* scores;             // [rows][n_pos]
     float* block_max;          // [rows][ceil(n_pos/8)] or null (Full)
-    int64_t tiles_per_row;
+    int64_t blocks_per_row;    // ceil(n_pos / 64)
+    // optional first-digit histograms for the Top-K that follows (Full only)
+    uint32_t* hist_e;          // [rows][NBINS1] of the entry scores
+    TopkRowState* state_e;
+    uint32_t* hist_b;          // [rows][NBINS1] of the block maxima
+    TopkRowState* state_b;
 };
 
-template <int DI, bool REINDEX>
-__global__ __launch_bounds__(TILE, 2) void index_kernel(IndexParams p) {
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr uint32_t NOROW = 0xFFFFFFFFu;
+
+// Physical row of position pos of row r (NOROW: not visible).  A K plane
+// holds fewer than 2^32 - 1 rows (it would exceed device memory otherwise).
+template <bool REINDEX>
+__device__ __forceinline__ uint32_t entry_row(const IndexParams& p, int r, int b, int64_t nv, int64_t pos) {
+    if (pos >= p.n_pos) return NOROW;
+    int64_t j = pos;
+    if (REINDEX) {
+        const int32_t blk = p.pool[(int64_t)r * p.P + (pos >> 3)];
+        if (blk < 0) return NOROW;
+        j = (int64_t)blk * 8 + (pos & 7);
+    }
+    if (j >= nv) return NOROW;
+    return (uint32_t)phys_row(p.kmap, b, j);
+}
+
+// Issue the loads of one wave block into registers.  Load i of lane l covers
+// 16-byte chunk c of entry e with i*64 + l = e*CH + c.
+template <int DI, bool REINDEX, bool CONTIG>
+__device__ __forceinline__ void load_block(const IndexParams& p, int r, int b, int64_t nv, int64_t blk, int lane,
+                                           uint32_t myrow, uint4 (&v)[DI / 8]) {
+    constexpr int CH = DI / 8;
+    const int64_t p0 = blk * EPB;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int L = i * 64 + lane;
+        const int e = L / CH, c = L % CH;
+        // loads are unconditional (an invisible entry reads row 0 of the plane,
+        // which always exists, and is zeroed after): no divergent branches
+        bool ok;
+        uint64_t row;
+        if (CONTIG) {
+            const int64_t pos = p0 + e;
+            ok = pos < nv && pos < p.n_pos;
+            row = ok ? (uint64_t)((int64_t)b * p.kmap.seq_stride + pos) : 0u;
+        } else {
+            const uint32_t r32 = (uint32_t)__shfl((int)myrow, e);
+            ok = r32 != NOROW;
+            row = ok ? (uint64_t)r32 : 0u;
+        }
+        const uint4 x = *reinterpret_cast<const uint4*>(p.k + row * DI + c * 8);
+        // the mask is opaque to the compiler, so it keeps the load unconditional
+        uint32_t m;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(m) : "v"(ok ? 0xFFFFFFFFu : 0u));
+        v[i] = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+    }
+}
+
+template <int DI, bool REINDEX, bool CONTIG>
+__global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(IndexParams p) {
     constexpr int CH = DI / 8;  // 16-byte chunks per entry
-    __shared__ uint4 tile[TILE * CH];
-    __shared__ int64_t rowtab[TILE];
+    __shared__ uint4 tile[WAVES][EPB * CH];
     __shared__ float4 qbar_s[DI / 4];
+    // 16-bit bin counters, two per word; a workgroup scores at most 65535
+    // positions (the launch guarantees it), so a half never overflows
+    __shared__ uint32_t hist_s[2][NBINS1 / 2];
 
     const int t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
     const int r = blockIdx.y;
     const int b = r / p.Q;
     const int64_t nv = min((int64_t)p.n_vis[r], p.kmap.capacity);
@@ -55,61 +121,103 @@ __global__ __launch_bounds__(TILE, 2) void index_kernel(IndexParams p) {
         for (int h = 0; h < p.H_i; ++h) acc = acc + __uint_as_float((uint32_t)qr[(int64_t)h * DI] << 16);
         reinterpret_cast<float*>(qbar_s)[t] = acc;
     }
+    const bool hist = p.hist_e != nullptr;
+    const bool hist_b = !REINDEX && hist && p.hist_b != nullptr;
+    if (hist)
+        for (int i = t; i < NBINS1; i += WAVES * 64) (&hist_s[0][0])[i] = 0u;
     __syncthreads();
 
-    const int64_t nblocks = (p.n_pos + 7) / 8;
-    for (int64_t ti = blockIdx.x; ti < p.tiles_per_row; ti += gridDim.x) {
-        const int64_t p0 = ti * TILE;
-        // 1. physical row of every entry of the tile (-1 = not visible)
-        const int64_t pos = p0 + t;
-        int64_t j = -1;
-        if (pos < p.n_pos) {
-            if (REINDEX) {
-                int32_t blk = p.pool[(int64_t)r * p.P + (pos >> 3)];
-                if (blk >= 0) j = (int64_t)blk * 8 + (pos & 7);
-            } else {
-                j = pos;
-            }
-        }
-        const bool valid = j >= 0 && j < nv;
-        rowtab[t] = valid ? phys_row(p.kmap, b, j) : -1;
-        __syncthreads();
-        // 2. coalesced load of the tile into swizzled LDS
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+    int64_t blk = (int64_t)blockIdx.x * WAVES + w;
+    const int64_t nblocks8 = (p.n_pos + 7) / 8;
+    uint4* my = tile[w];
+    uint32_t n_valid = 0, n_valid_b = 0;  // lane counts for the histograms
+
+    uint32_t row_next = (CONTIG || blk >= p.blocks_per_row) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
+    uint4 v[CH];
+    if (blk < p.blocks_per_row) load_block<DI, REINDEX, CONTIG>(p, r, b, nv, blk, lane, row_next, v);
+    for (; blk < p.blocks_per_row; blk += stride) {
+        const int64_t pos = blk * EPB + lane;
+        const bool valid = CONTIG ? (pos < nv && pos < p.n_pos) : (row_next != NOROW);
+        // An opaque zero, fresh every block: LDS addresses are recomputed each
+        // block (two ALU ops each) instead of being hoisted into ~48 registers.
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const int lz = lane + z;
+        // stage the block in this wave's LDS tile
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int L = i * TILE + t;
+            const int L = i * 64 + lz;
             const int e = L / CH, c = L % CH;
-            const int64_t row = rowtab[e];
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row >= 0) v = *reinterpret_cast<const uint4*>(p.k + row * DI + c * 8);
-            tile[e * CH + (c ^ (e & (CH - 1)))] = v;
+            my[e * CH + (c ^ (e & (CH - 1)))] = v[i];
         }
-        __syncthreads();
-        // 3. one entry per thread: sequential FMA chain over channels
+        wave_sync();
+        // next block's loads fly while this one is scored
+        const int64_t nxt = blk + stride;
+        if (nxt < p.blocks_per_row) {
+            if (!CONTIG) row_next = entry_row<REINDEX>(p, r, b, nv, nxt * EPB + lane);
+            load_block<DI, REINDEX, CONTIG>(p, r, b, nv, nxt, lane, row_next, v);
+        }
+        // one entry per lane: sequential FMA chain over channels.  qbar is
+        // re-read from LDS (a broadcast) each block rather than held in 128
+        // registers: the opaque zero keeps the compiler from hoisting it.
+        const float4* qb_s = qbar_s + z;
+        const uint4* mine = my + lz * CH;
+        const int sw = lz & (CH - 1);
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const uint4 v = tile[t * CH + (c ^ (t & (CH - 1)))];
-            const float4 qa = qbar_s[2 * c], qb = qbar_s[2 * c + 1];  // same address in every lane: broadcast
-            acc = fmaf(qa.x, bf16_lo(v.x), acc);
-            acc = fmaf(qa.y, bf16_hi(v.x), acc);
-            acc = fmaf(qa.z, bf16_lo(v.y), acc);
-            acc = fmaf(qa.w, bf16_hi(v.y), acc);
-            acc = fmaf(qb.x, bf16_lo(v.z), acc);
-            acc = fmaf(qb.y, bf16_hi(v.z), acc);
-            acc = fmaf(qb.z, bf16_lo(v.w), acc);
-            acc = fmaf(qb.w, bf16_hi(v.w), acc);
+            const uint4 k4 = mine[c ^ sw];
+            const float4 qa = qb_s[2 * c], qb = qb_s[2 * c + 1];  // same address in every lane: broadcast
+            acc = fmaf(qa.x, bf16_lo(k4.x), acc);
+            acc = fmaf(qa.y, bf16_hi(k4.x), acc);
+            acc = fmaf(qa.z, bf16_lo(k4.y), acc);
+            acc = fmaf(qa.w, bf16_hi(k4.y), acc);
+            acc = fmaf(qb.x, bf16_lo(k4.z), acc);
+            acc = fmaf(qb.y, bf16_hi(k4.z), acc);
+            acc = fmaf(qb.z, bf16_lo(k4.w), acc);
+            acc = fmaf(qb.w, bf16_hi(k4.w), acc);
         }
+        wave_sync();  // the tile is rewritten by the next iteration
         const float s = valid ? acc : -INFINITY;
         if (pos < p.n_pos) p.scores[(int64_t)r * p.n_pos + pos] = s;
+        if (hist && valid) {
+            const uint32_t d = key32(s) >> 21;
+            atomicAdd(&hist_s[0][d >> 1], 1u << (16 * (d & 1)));
+            ++n_valid;
+        }
         if (!REINDEX && p.block_max != nullptr) {
             float m = s;
             m = fmaxf(m, __shfl_xor(m, 1));
             m = fmaxf(m, __shfl_xor(m, 2));
             m = fmaxf(m, __shfl_xor(m, 4));
-            if ((t & 7) == 0 && (pos >> 3) < nblocks) p.block_max[(int64_t)r * nblocks + (pos >> 3)] = m;
+            if ((lane & 7) == 0 && (pos >> 3) < nblocks8) {
+                p.block_max[(int64_t)r * nblocks8 + (pos >> 3)] = m;
+                if (hist_b && m != -INFINITY) {
+                    const uint32_t d = key32(m) >> 21;
+                    atomicAdd(&hist_s[1][d >> 1], 1u << (16 * (d & 1)));
+                    ++n_valid_b;
+                }
+            }
         }
-        // the next iteration rewrites rowtab/tile only after its own barrier
+    }
+    if (hist) {
+        // valid counts: one atomic per wave; bins: only the non-empty ones
+        for (int off = 32; off > 0; off >>= 1) {
+            n_valid += __shfl_xor(n_valid, off);
+            n_valid_b += __shfl_xor(n_valid_b, off);
+        }
+        if (lane == 0 && n_valid) atomicAdd(&p.state_e[r].valid, n_valid);
+        if (hist_b && lane == 0 && n_valid_b) atomicAdd(&p.state_b[r].valid, n_valid_b);
+        __syncthreads();
+        for (int i = t; i < NBINS1; i += WAVES * 64) {
+            const uint32_t ce = (hist_s[0][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+            if (ce) atomicAdd(&p.hist_e[(int64_t)r * NBINS1 + i], ce);
+            if (hist_b) {
+                const uint32_t cb = (hist_s[1][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                if (cb) atomicAdd(&p.hist_b[(int64_t)r * NBINS1 + i], cb);
+            }
+        }
     }
 }
 
@@ -127,25 +235,31 @@ csa2_status check_common(const char* what, const uint16_t* q_idx, int32_t B, int
 }
 
 csa2_status launch_index(IndexParams& p, int rows, int D_i, bool reindex, hipStream_t stream, const char* what) {
-    p.tiles_per_row = (p.n_pos + TILE - 1) / TILE;
-    if (p.tiles_per_row == 0 || rows == 0) return CSA2_OK;
-    // enough workgroups to fill 256 CUs x 2 several times over; each loops over tiles
-    int64_t gx = p.tiles_per_row;
-    const int64_t target = 4096;
+    p.blocks_per_row = (p.n_pos + EPB - 1) / EPB;
+    if (p.blocks_per_row == 0 || rows == 0) return CSA2_OK;
+    // about two resident workgroups per CU on 256 CUs; every wave loops over its blocks
+    int64_t gx = (p.blocks_per_row + WAVES - 1) / WAVES;
+    const int64_t target = 512;
     if (gx * rows > target) gx = (target + rows - 1) / rows;
+    // with histograms, a workgroup may score at most 65535 positions (16-bit bins)
+    const int64_t min_gx = (p.blocks_per_row + (65535 / (WAVES * EPB)) * WAVES - 1) / ((65535 / (WAVES * EPB)) * WAVES);
+    if (gx < min_gx) gx = min_gx;
     if (gx < 1) gx = 1;
-    dim3 grid((unsigned)gx, (unsigned)rows);
-    if (D_i == 128) {
-        if (reindex)
-            index_kernel<128, true><<<grid, TILE, 0, stream>>>(p);
-        else
-            index_kernel<128, false><<<grid, TILE, 0, stream>>>(p);
-    } else {
-        if (reindex)
-            index_kernel<64, true><<<grid, TILE, 0, stream>>>(p);
-        else
-            index_kernel<64, false><<<grid, TILE, 0, stream>>>(p);
+    const dim3 grid((unsigned)gx, (unsigned)rows);
+    const dim3 block(WAVES * 64);
+    const bool contig = !reindex && p.kmap.page_table == nullptr;
+#define CSA2_IDX(DD)                                                                   \
+    if (D_i == DD) {                                                                   \
+        if (reindex)                                                                   \
+            index_kernel<DD, true, false><<<grid, block, 0, stream>>>(p);              \
+        else if (contig)                                                               \
+            index_kernel<DD, false, true><<<grid, block, 0, stream>>>(p);              \
+        else                                                                           \
+            index_kernel<DD, false, false><<<grid, block, 0, stream>>>(p);             \
     }
+    CSA2_IDX(128)
+    CSA2_IDX(64)
+#undef CSA2_IDX
     return launch_status(what);
 }
 
@@ -154,10 +268,10 @@ csa2_status launch_index(IndexParams& p, int rows, int D_i, bool reindex, hipStr
 
 using namespace csa2;
 
-extern "C" csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i,
-                                       const csa2_idx_k* k, const int32_t* n_vis, int32_t n_max, float* scores,
-                                       float* block_max, hipStream_t stream) {
-    clear_error();
+csa2_status csa2::index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
+                                  const int32_t* n_vis, int32_t n_max, float* scores, float* block_max,
+                                  uint32_t* hist_e, TopkRowState* st_e, uint32_t* hist_b, TopkRowState* st_b,
+                                  hipStream_t stream) {
     CSA2_ARG(n_max >= 0, "index_full: n_max=%d < 0", n_max);
     RowMap map;
     csa2_status st = check_common("index_full", q_idx, B, Q, H_i, k, n_vis, n_max, &map);
@@ -173,18 +287,29 @@ extern "C" csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t
     p.n_pos = n_max;
     p.scores = scores;
     p.block_max = block_max;
+    p.hist_e = hist_e;
+    p.state_e = st_e;
+    p.hist_b = block_max ? hist_b : nullptr;
+    p.state_b = st_b;
     return launch_index(p, B * Q, k->D_i, false, stream, "index_full");
 }
 
-extern "C" csa2_status csa2_index_reindex(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i,
-                                          const csa2_idx_k* k, const int32_t* n_vis, const int32_t* pool_blocks,
-                                          int32_t P, float* pool_scores, hipStream_t stream) {
+extern "C" csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i,
+                                       const csa2_idx_k* k, const int32_t* n_vis, int32_t n_max, float* scores,
+                                       float* block_max, hipStream_t stream) {
     clear_error();
+    return index_full_hist(q_idx, B, Q, H_i, k, n_vis, n_max, scores, block_max, nullptr, nullptr, nullptr, nullptr,
+                           stream);
+}
+
+csa2_status csa2::index_reindex_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
+                                     const int32_t* n_vis, const int32_t* pool_blocks, int32_t P, float* pool_scores,
+                                     uint32_t* hist, TopkRowState* st, hipStream_t stream) {
     CSA2_ARG(P >= 0 && P <= (1 << 27), "index_reindex: P=%d out of range", P);
     RowMap map;
     // the pool may name any block of the sequence; the view is checked for one page at least
-    csa2_status st = check_common("index_reindex", q_idx, B, Q, H_i, k, n_vis, 1, &map);
-    if (st != CSA2_OK || (int64_t)B * Q == 0 || P == 0) return st;
+    csa2_status s = check_common("index_reindex", q_idx, B, Q, H_i, k, n_vis, 1, &map);
+    if (s != CSA2_OK || (int64_t)B * Q == 0 || P == 0) return s;
     CSA2_ARG(pool_blocks && pool_scores, "index_reindex: null pointer");
     IndexParams p{};
     p.q_idx = q_idx;
@@ -197,5 +322,14 @@ extern "C" csa2_status csa2_index_reindex(const uint16_t* q_idx, int32_t B, int3
     p.pool = pool_blocks;
     p.P = P;
     p.scores = pool_scores;
+    p.hist_e = hist;
+    p.state_e = st;
     return launch_index(p, B * Q, k->D_i, true, stream, "index_reindex");
+}
+
+extern "C" csa2_status csa2_index_reindex(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i,
+                                          const csa2_idx_k* k, const int32_t* n_vis, const int32_t* pool_blocks,
+                                          int32_t P, float* pool_scores, hipStream_t stream) {
+    clear_error();
+    return index_reindex_hist(q_idx, B, Q, H_i, k, n_vis, pool_blocks, P, pool_scores, nullptr, nullptr, stream);
 }

@@ -1,278 +1,353 @@
 // Top-K selection by (score descending, position ascending), as a radix select
 // over a 64-bit composite key  key32(score) << 32 | ~position.  All composites
 // are distinct, so "the K largest composites" is exactly the selection and the
-// result is independent of thread scheduling (aprilzz.com V4.1 Flash article,
+// result does not depend on thread scheduling (aprilzz.com V4.1 Flash article,
 // section "CSA2：在层的维度上共享缓存": every Full layer selects a new Top-512;
 // the same routine selects the 2048 pool blocks, gkm0120.cn section 2.2.3).
 //
 // key32 maps fp32 to an order-preserving unsigned integer (-0 folded into +0);
 // -inf marks an invalid position and maps to 0, which is never selected.
+// Digits of the composite: key bits 31..21, 20..10, 9..0, then the same on
+// ~position; a pass stops refining as soon as its bin holds exactly the
+// number of elements still needed.
 //
 // Two paths:
 //  * n <= 16384 (Reindex pools, short contexts): one 1024-thread workgroup per
-//    row caches the row's keys in LDS and runs the whole radix select there.
-//  * larger n: (1) zero the per-row state, (2) many workgroups per row build a
-//    4096-bin histogram of the top 12 key bits, (3) the same grid splits the
-//    row: positions above the threshold bin go straight to the selection,
-//    positions inside it to a candidate list, (4) one workgroup per row
-//    finishes the select on the candidates (or, if the bin overflows the
-//    candidate buffer, on the whole row) and writes the sorted result.
-#include "common.h"
+//    row holds 16 consecutive keys per thread in registers, runs every pass
+//    with an LDS histogram, and writes the selection in position order with
+//    one block-wide prefix sum (no sort).
+//  * larger n: a per-row 2048-bin histogram of the top 11 key bits (fused into
+//    the Full-mode scan, or built by its own pass), then a grid-wide pass that
+//    sends positions above the threshold bin straight to the selection and
+//    positions inside it to a candidate list, then one workgroup per row that
+//    selects among the candidates (or, if the bin overflowed the candidate
+//    buffer, among the whole row) and sorts the result.
+// Several independent selections (the Top-K entries and the pool blocks of a
+// Full layer) run in the same launches as separate segments.
+#include "internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int NBINS = 4096;     // widest digit: 12 bits
 constexpr int WG = 1024;        // single-row workgroup
-constexpr int KMAX = 2048;
-constexpr int SMALL_N = 16384;  // rows cached in LDS
-constexpr int CAP = 8192;       // candidate capacity per row
-constexpr int CHUNK = 16384;    // positions per workgroup in the multi-workgroup passes
-constexpr int PWG = 256;        // threads of the multi-workgroup passes
+constexpr int NW = WG / 64;     // its wavefronts
+constexpr int E_SMALL = TOPK_SMALL_N / WG;  // keys per thread in the small path (16)
+constexpr int PWG = 256;        // threads of the grid-wide passes
+constexpr int CHUNK = 4096;     // positions per workgroup in the grid-wide passes (16 per thread)
 
-struct RowState {
-    uint32_t valid;   // number of valid positions
-    uint32_t n_sel;   // positions definitely selected (above the threshold bin)
-    uint32_t n_cand;  // positions in the threshold bin
-    uint32_t digit;   // threshold bin (top 12 bits)
-};
-
-__device__ __forceinline__ uint32_t key32(float s) {
-    if (s == -INFINITY) return 0u;
-    uint32_t u = __float_as_uint(s + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
+    return ((uint64_t)key << 32) | (uint64_t)(~pos);
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup helpers (blockDim.x == WG)
+// Block-wide helpers for a 1024-thread workgroup.
+struct SelectLds {
+    uint32_t hist[NBINS1];
+    uint32_t wsum[NW];
+    uint32_t bin, above, total, nsel;
+};
 
-// Finds the bin d (of nb) such that  above < need <= above + hist[d],  where
-// above = sum of the bins above d.  Result in *d_out / *above_out (LDS).
-__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* scan, uint32_t* d_out,
-                         uint32_t* above_out) {
-    const int t = threadIdx.x, nt = blockDim.x;
-    const int per = nb / nt;  // bins per thread, descending bins: thread 0 owns the top
-    uint32_t local = 0;
-    for (int i = 0; i < per; ++i) local += hist[nb - 1 - (t * per + i)];
-    scan[t] = local;
-    __syncthreads();
-    // inclusive Hillis-Steele scan over threads
-    for (int off = 1; off < nt; off <<= 1) {
-        uint32_t v = (t >= off) ? scan[t - off] : 0u;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
+// Exclusive prefix sum over the threads of the block; *total gets the sum.
+__device__ uint32_t block_excl_scan(uint32_t v, SelectLds& sh, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    uint32_t above = scan[t] - local;
+    if (lane == 63) sh.wsum[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        uint32_t s = lane < NW ? sh.wsum[lane] : 0u;
+#pragma unroll
+        for (int off = 1; off < NW; off <<= 1) {
+            const uint32_t y = __shfl_up(s, off);
+            if (lane >= off) s += y;
+        }
+        if (lane < NW) sh.wsum[lane] = s;
+    }
+    __syncthreads();
+    const uint32_t base = wid ? sh.wsum[wid - 1] : 0u;
+    *total = sh.wsum[NW - 1];
+    __syncthreads();
+    return base + x - v;
+}
+
+// The bin d of hist[0..nb) with  above < need <= above + hist[d]  (above =
+// sum of the bins above d): written to sh.bin / sh.above.
+__device__ void find_bin(SelectLds& sh, int nb, uint32_t need) {
+    const int per = (nb + WG - 1) / WG;  // bins per thread, thread 0 owns the top bins
+    const int t = threadIdx.x;
+    uint32_t local = 0;
     for (int i = 0; i < per; ++i) {
         const int bin = nb - 1 - (t * per + i);
-        const uint32_t h = hist[bin];
+        if (bin >= 0) local += sh.hist[bin];
+    }
+    uint32_t tot;
+    uint32_t above = block_excl_scan(local, sh, &tot);
+    for (int i = 0; i < per; ++i) {
+        const int bin = nb - 1 - (t * per + i);
+        if (bin < 0) break;
+        const uint32_t h = sh.hist[bin];
         if (above < need && need <= above + h) {
-            *d_out = (uint32_t)bin;
-            *above_out = above;
+            sh.bin = (uint32_t)bin;
+            sh.above = above;
         }
         above += h;
     }
     __syncthreads();
 }
 
-__device__ __forceinline__ void append_lds(int* list, uint32_t* count, int value) {
-    uint32_t at = atomicAdd(count, 1u);
-    list[at] = value;
-}
-
-// Source of (key, position) pairs for select_rows.
-struct LdsKeys {  // keys cached in LDS, position = index
-    const uint32_t* keys;
-    int n;
-    __device__ uint32_t key(int i) const { return keys[i]; }
-    __device__ uint32_t pos(int i) const { return (uint32_t)i; }
-};
-struct LdsCands {  // candidate (key, position) pairs in LDS
-    const uint32_t* keys;
-    const uint32_t* pos_;
-    int n;
-    __device__ uint32_t key(int i) const { return keys[i]; }
-    __device__ uint32_t pos(int i) const { return pos_[i]; }
-};
-struct GlobalRow {  // a whole row of scores in global memory
-    const float* s;
-    int n;
-    __device__ uint32_t key(int i) const { return key32(s[i]); }
-    __device__ uint32_t pos(int i) const { return (uint32_t)i; }
-};
-
-// Radix select of the `need` largest composites among the elements of src
-// whose composite matches `prefix` on the bits of `mask` (need >= 1 and at
-// most that many elements).  Digits: key bits 31..20, 19..10, 9..0, then the
-// same on ~position.  Selected positions are appended to sel[] via *n_sel.
-template <class Src>
-__device__ void radix_select(const Src& src, uint32_t need, int first_pass, uint64_t prefix, uint64_t mask,
-                             uint32_t* hist, uint32_t* scan, uint32_t* shared2, int* sel, uint32_t* n_sel) {
-    const int t = threadIdx.x, nt = blockDim.x;
-    const int shifts[6] = {52, 42, 32, 20, 10, 0};
-    const int widths[6] = {12, 10, 10, 12, 10, 10};
+// Radix select over register-resident elements (key 0 = not in the set).
+// On return, element (key, pos) is selected iff key != 0 and
+// (composite & mask) >= prefix; exactly `need` elements qualify.
+template <int E>
+__device__ void select_regs(const uint32_t (&key)[E], const uint32_t (&pos)[E], uint32_t need, int first_pass,
+                            uint64_t& prefix, uint64_t& mask, SelectLds& sh) {
+    const int shifts[6] = {53, 42, 32, 21, 10, 0};
+    const int widths[6] = {11, 11, 10, 11, 11, 10};
     for (int pass = first_pass; pass < 6; ++pass) {
-        const int sh = shifts[pass], wd = widths[pass], nb = 1 << wd;
-        for (int i = t; i < nb; i += nt) hist[i] = 0u;
+        const int sh_ = shifts[pass], nb = 1 << widths[pass];
+        for (int i = threadIdx.x; i < nb; i += WG) sh.hist[i] = 0u;
         __syncthreads();
-        for (int i = t; i < src.n; i += nt) {
-            const uint32_t k = src.key(i);
-            if (k == 0u) continue;
-            const uint64_t c = ((uint64_t)k << 32) | (uint64_t)(~src.pos(i));
-            if ((c & mask) == prefix) atomicAdd(&hist[(uint32_t)(c >> sh) & (uint32_t)(nb - 1)], 1u);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (key[e] == 0u) continue;
+            const uint64_t c = composite(key[e], pos[e]);
+            if ((c & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(c >> sh_) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        find_bin(hist, nb, need, scan, &shared2[0], &shared2[1]);
-        const uint32_t d = shared2[0], above = shared2[1];
-        need -= above;
-        prefix |= (uint64_t)d << sh;
-        mask |= (uint64_t)(nb - 1) << sh;
-        const bool done = (hist[d] == need);
+        find_bin(sh, nb, need);
+        const uint32_t d = sh.bin;
+        need -= sh.above;
+        prefix |= (uint64_t)d << sh_;
+        mask |= (uint64_t)(nb - 1) << sh_;
+        const bool done = sh.hist[d] == need;
         __syncthreads();
         if (done) break;
     }
-    // selected <=> composite restricted to the decided bits >= prefix
-    for (int i = t; i < src.n; i += nt) {
-        const uint32_t k = src.key(i);
-        if (k == 0u) continue;
-        const uint64_t c = ((uint64_t)k << 32) | (uint64_t)(~src.pos(i));
-        if ((c & mask) >= prefix) append_lds(sel, n_sel, (int)src.pos(i));
+}
+
+// Slow general radix select over a row in global memory, restricted to the
+// elements matching prefix/mask (used only when a threshold bin overflows the
+// candidate buffer, e.g. long runs of equal scores).  Appends to sel[].
+__device__ void select_global_row(const float* s, int n, uint32_t need, uint64_t prefix, uint64_t mask,
+                                  SelectLds& sh, int* sel) {
+    const int shifts[6] = {53, 42, 32, 21, 10, 0};
+    const int widths[6] = {11, 11, 10, 11, 11, 10};
+    int pass = 0;
+    while (pass < 6 && ((mask >> shifts[pass]) & 1u)) ++pass;  // skip decided digits
+    for (; pass < 6; ++pass) {
+        const int sh_ = shifts[pass], nb = 1 << widths[pass];
+        for (int i = threadIdx.x; i < nb; i += WG) sh.hist[i] = 0u;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += WG) {
+            const uint32_t k = key32(s[i]);
+            if (k == 0u) continue;
+            const uint64_t c = composite(k, (uint32_t)i);
+            if ((c & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(c >> sh_) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin(sh, nb, need);
+        const uint32_t d = sh.bin;
+        need -= sh.above;
+        prefix |= (uint64_t)d << sh_;
+        mask |= (uint64_t)(nb - 1) << sh_;
+        const bool done = sh.hist[d] == need;
+        __syncthreads();
+        if (done) break;
+    }
+    for (int i = threadIdx.x; i < n; i += WG) {
+        const uint32_t k = key32(s[i]);
+        if (k != 0u && (composite(k, (uint32_t)i) & mask) >= prefix) sel[atomicAdd(&sh.nsel, 1u)] = i;
     }
     __syncthreads();
 }
 
-// Bitonic sort of sel[0..KMAX) ascending (unused slots hold INT32_MAX).
-__device__ void sort_sel(int* sel) {
+// Bitonic sort of sel[0..np) ascending (np a power of two <= TOPK_KMAX;
+// unused slots hold INT32_MAX).  Thread t owns elements t and t + 1024;
+// partner strides below 64 are lane shuffles, 64..512 go through LDS, 1024
+// stays inside the thread.
+__device__ void sort_sel(int* sel, int np) {
     const int t = threadIdx.x;
-    for (int size = 2; size <= KMAX; size <<= 1) {
+    const bool two = np > WG;
+    int a = sel[t], b = two ? sel[t + WG] : 0x7FFFFFFF;
+    __syncthreads();
+    for (int size = 2; size <= np; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = t; i < KMAX / 2; i += blockDim.x) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = ((lo & size) == 0);
-                const int a = sel[lo], c = sel[hi];
-                if ((a > c) == up) {
-                    sel[lo] = c;
-                    sel[hi] = a;
-                }
+            if (stride == WG) {  // pair (t, t + 1024), ascending
+                const int lo = min(a, b), hi = max(a, b);
+                a = lo;
+                b = hi;
+                continue;
             }
-            __syncthreads();
+            const bool upper = (t & stride) != 0;
+            const bool up_a = ((t & size) == 0);
+            const bool up_b = (((t + WG) & size) == 0);
+            int pa, pb = 0;
+            if (stride < 64) {
+                pa = __shfl_xor(a, stride);
+                if (two) pb = __shfl_xor(b, stride);
+            } else {
+                sel[t] = a;
+                if (two) sel[t + WG] = b;
+                __syncthreads();
+                pa = sel[t ^ stride];
+                if (two) pb = sel[(t + WG) ^ stride];
+                __syncthreads();
+            }
+            a = (upper == up_a) ? max(a, pa) : min(a, pa);
+            if (two) b = (upper == up_b) ? max(b, pb) : min(b, pb);
         }
     }
+    sel[t] = a;
+    if (two) sel[t + WG] = b;
+    __syncthreads();
 }
 
-__device__ void write_out(const int* sel, uint32_t total, int k, const int32_t* pool, int64_t row, int nblk,
-                          int32_t* out) {
-    for (int i = threadIdx.x; i < k; i += blockDim.x) {
-        int v = -1;
-        if ((uint32_t)i < total) {
-            const int p = sel[i];
-            v = pool ? pool[row * nblk + (p >> 3)] * 8 + (p & 7) : p;
-        }
-        out[row * (int64_t)k + i] = v;
-    }
+__device__ __forceinline__ int32_t map_pos(int p, const int32_t* pool, int64_t row, int nblk) {
+    return pool ? pool[row * nblk + (p >> 3)] * 8 + (p & 7) : p;
 }
 
 // ---------------------------------------------------------------------------
-// Small path: one workgroup per row, keys cached in LDS.
+// Small path.
+// With hist != NULL the row's first-digit histogram and valid count were
+// built by the scoring kernel: the first pass is read, not recomputed, and
+// the histogram and state are zeroed again for the next use.
 __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict__ scores, int n, int k,
                                                         const int32_t* __restrict__ pool,
-                                                        int32_t* __restrict__ out) {
-    __shared__ uint32_t keys[SMALL_N];
-    __shared__ uint32_t hist[NBINS];
-    __shared__ uint32_t scan[WG];
-    __shared__ int sel[KMAX];
-    __shared__ uint32_t sh[4];
+                                                        int32_t* __restrict__ out, uint32_t* __restrict__ hist,
+                                                        TopkRowState* __restrict__ state) {
+    __shared__ SelectLds sh;
     const int t = threadIdx.x;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * (int64_t)n;
-    if (t == 0) {
-        sh[2] = 0u;  // valid count
-        sh[3] = 0u;  // n_sel
-    }
-    for (int i = t; i < KMAX; i += WG) sel[i] = 0x7FFFFFFF;
-    __syncthreads();
+    uint32_t key[E_SMALL], pos[E_SMALL];
     uint32_t cnt = 0;
-    for (int i = t; i < n; i += WG) {
-        const uint32_t kk = key32(s[i]);
-        keys[i] = kk;
-        cnt += (kk != 0u);
+#pragma unroll
+    for (int e = 0; e < E_SMALL; ++e) {
+        const int i = t * E_SMALL + e;
+        pos[e] = (uint32_t)i;
+        key[e] = i < n ? key32(s[i]) : 0u;
+        cnt += key[e] != 0u;
     }
-    atomicAdd(&sh[2], cnt);
-    __syncthreads();
-    const uint32_t valid = sh[2];
-    if (valid <= (uint32_t)k) {
-        for (int i = t; i < n; i += WG)
-            if (keys[i] != 0u) append_lds(sel, &sh[3], i);
+    uint64_t prefix = 0, mask = 0;
+    uint32_t valid;
+    if (hist != nullptr) {
+        uint32_t* hr = hist + row * NBINS1;
+        for (int i = t; i < NBINS1; i += WG) {
+            sh.hist[i] = hr[i];
+            hr[i] = 0u;
+        }
+        if (t == 0) {
+            sh.total = state[row].valid;
+            state[row] = TopkRowState{0u, 0u, 0u, 0u};
+        }
         __syncthreads();
+        valid = sh.total;
+        if (valid > (uint32_t)k) {
+            find_bin(sh, NBINS1, (uint32_t)k);
+            const uint32_t d = sh.bin;
+            const uint32_t need = (uint32_t)k - sh.above;
+            prefix = (uint64_t)d << 53;
+            mask = (uint64_t)0x7FF << 53;
+            const bool done = sh.hist[d] == need;
+            __syncthreads();
+            if (!done) select_regs<E_SMALL>(key, pos, need, 1, prefix, mask, sh);
+        }
     } else {
-        LdsKeys src{keys, n};
-        radix_select(src, (uint32_t)k, 0, 0ull, 0ull, hist, scan, sh, sel, &sh[3]);
+        block_excl_scan(cnt, sh, &valid);
+        if (valid > (uint32_t)k) select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
     }
-    const uint32_t total = valid < (uint32_t)k ? valid : (uint32_t)k;
-    sort_sel(sel);
-    write_out(sel, total, k, pool, row, n / 8, out);
+    const bool all = valid <= (uint32_t)k;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < E_SMALL; ++e)
+        mine += key[e] != 0u && (all || (composite(key[e], pos[e]) & mask) >= prefix);
+    uint32_t total;
+    uint32_t at = block_excl_scan(mine, sh, &total);
+    const int nblk = n / 8;
+#pragma unroll
+    for (int e = 0; e < E_SMALL; ++e)
+        if (key[e] != 0u && (all || (composite(key[e], pos[e]) & mask) >= prefix))
+            out[row * (int64_t)k + at++] = map_pos((int)pos[e], pool, row, nblk);
+    for (int i = (int)total + t; i < k; i += WG) out[row * (int64_t)k + i] = -1;
 }
 
 // ---------------------------------------------------------------------------
 // Large path.
-__global__ void topk_zero_kernel(uint32_t* __restrict__ hist, RowState* __restrict__ state, int rows) {
+__global__ void topk_zero_kernel(TopkSegs segs) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < (int64_t)rows * NBINS) hist[i] = 0u;
-    if (i < rows) state[i] = RowState{0u, 0u, 0u, 0u};
+    for (int sgi = 0; sgi < segs.nseg; ++sgi) {
+        const TopkSeg& sg = segs.seg[sgi];
+        if (i < (int64_t)segs.rows * NBINS1) sg.hist[i] = 0u;
+        if (i < segs.rows) sg.state[i] = TopkRowState{0u, 0u, 0u, 0u};
+    }
 }
 
-__global__ __launch_bounds__(PWG) void topk_hist_kernel(const float* __restrict__ scores, int n,
-                                                       uint32_t* __restrict__ ghist, RowState* __restrict__ state) {
-    __shared__ uint32_t h[NBINS];
+__global__ __launch_bounds__(PWG) void topk_hist_kernel(TopkSegs segs) {
+    __shared__ uint32_t h[NBINS1];
+    const int sgi = blockIdx.y / segs.rows;
+    const int64_t row = blockIdx.y % segs.rows;
+    const TopkSeg& sg = segs.seg[sgi];
+    if ((int)blockIdx.x * CHUNK >= sg.n) return;
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.y;
-    for (int i = t; i < NBINS; i += PWG) h[i] = 0u;
+    for (int i = t; i < NBINS1; i += PWG) h[i] = 0u;
     __syncthreads();
-    const float* s = scores + row * (int64_t)n;
+    const float* s = sg.scores + row * (int64_t)sg.n;
     const int lo = blockIdx.x * CHUNK;
-    const int hi = min(n, lo + CHUNK);
+    const int hi = min(sg.n, lo + CHUNK);
     uint32_t cnt = 0;
-    for (int i = lo + t; i < hi; i += PWG) {
-        const uint32_t kk = key32(s[i]);
+    float v[CHUNK / PWG];
+#pragma unroll
+    for (int e = 0; e < CHUNK / PWG; ++e) {
+        const int i = lo + e * PWG + t;
+        v[e] = i < hi ? s[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < CHUNK / PWG; ++e) {
+        const uint32_t kk = key32(v[e]);
         if (kk != 0u) {
-            atomicAdd(&h[kk >> 20], 1u);
+            atomicAdd(&h[kk >> 21], 1u);
             ++cnt;
         }
     }
-    // wave reduce the valid count, one atomic per wave
     for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-    if ((t & 63) == 0 && cnt) atomicAdd(&state[row].valid, cnt);
+    if ((t & 63) == 0 && cnt) atomicAdd(&sg.state[row].valid, cnt);
     __syncthreads();
-    uint32_t* gh = ghist + row * NBINS;
-    for (int i = t; i < NBINS; i += PWG)
+    uint32_t* gh = sg.hist + row * NBINS1;
+    for (int i = t; i < NBINS1; i += PWG)
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Threshold bin of a row from its global histogram (PWG threads; 16 bins each).
+// Threshold bin of a row from its global histogram (PWG threads, 8 bins each).
 __device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* scan, uint32_t* d_out,
                               uint32_t* above_out) {
-    const int t = threadIdx.x;
-    constexpr int per = NBINS / PWG;
-    uint32_t local = 0;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    constexpr int per = NBINS1 / PWG;
     uint32_t mine[per];
+    uint32_t local = 0;
+#pragma unroll
     for (int i = 0; i < per; ++i) {
-        mine[i] = gh[NBINS - 1 - (t * per + i)];
+        mine[i] = gh[NBINS1 - 1 - (t * per + i)];
         local += mine[i];
     }
-    scan[t] = local;
-    __syncthreads();
-    for (int off = 1; off < PWG; off <<= 1) {
-        uint32_t v = (t >= off) ? scan[t - off] : 0u;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
+    uint32_t x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    uint32_t above = scan[t] - local;
+    if (lane == 63) scan[wid] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wid; ++w) base += scan[w];
+    uint32_t above = base + x - local;
+#pragma unroll
     for (int i = 0; i < per; ++i) {
         if (above < need && need <= above + mine[i]) {
-            *d_out = (uint32_t)(NBINS - 1 - (t * per + i));
+            *d_out = (uint32_t)(NBINS1 - 1 - (t * per + i));
             *above_out = above;
         }
         above += mine[i];
@@ -280,111 +355,178 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* scan,
     __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
-    const uint64_t m = __ballot(pred);
-    if (m == 0) return 0u;
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, leader);
-    return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
-
-__global__ __launch_bounds__(PWG) void topk_compact_kernel(const float* __restrict__ scores, int n, int k,
-                                                          const uint32_t* __restrict__ ghist,
-                                                          RowState* __restrict__ state, int* __restrict__ gsel,
-                                                          uint32_t* __restrict__ ckey, uint32_t* __restrict__ cpos) {
-    __shared__ uint32_t scan[PWG];
-    __shared__ uint32_t sh[2];
+// Threshold split of one chunk.  Positions above the threshold bin go to the
+// row's selection list, positions inside it to the candidate list; both are
+// gathered in LDS first, so each list costs one global atomic per workgroup.
+__global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
+    __shared__ uint32_t scan[PWG / 64];
+    __shared__ uint32_t sh[6];
+    __shared__ int l_sel[TOPK_KMAX];
+    __shared__ uint32_t l_ck[CHUNK], l_cp[CHUNK];
+    const int sgi = blockIdx.y / segs.rows;
+    const int64_t row = blockIdx.y % segs.rows;
+    const TopkSeg& sg = segs.seg[sgi];
+    if ((int)blockIdx.x * CHUNK >= sg.n) return;
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.y;
-    const uint32_t valid = state[row].valid;
-    const bool all = valid <= (uint32_t)k;
+    const int lo = blockIdx.x * CHUNK;
+    const int hi = min(sg.n, lo + CHUNK);
+    const float* s = sg.scores + row * (int64_t)sg.n;
+    float v[CHUNK / PWG];
+#pragma unroll
+    for (int e = 0; e < CHUNK / PWG; ++e) {
+        const int i = lo + e * PWG + t;
+        v[e] = i < hi ? s[i] : -INFINITY;
+    }
+    if (t < 2) sh[2 + t] = 0u;
+    const uint32_t valid = sg.state[row].valid;
+    const bool all = valid <= (uint32_t)sg.k;
     uint32_t d = 0;
     if (!all) {
-        row_threshold(ghist + row * NBINS, (uint32_t)k, scan, &sh[0], &sh[1]);
+        row_threshold(sg.hist + row * NBINS1, (uint32_t)sg.k, scan, &sh[0], &sh[1]);
         d = sh[0];
-        if (blockIdx.x == 0 && t == 0) state[row].digit = d;
+        if (blockIdx.x == 0 && t == 0) sg.state[row].digit = d;
+    } else {
+        __syncthreads();
     }
-    const float* s = scores + row * (int64_t)n;
-    int* sel = gsel + row * KMAX;
-    uint32_t* ck = ckey + row * CAP;
-    uint32_t* cp = cpos + row * CAP;
-    const int lo = blockIdx.x * CHUNK;
-    const int hi = min(n, lo + CHUNK);
-    // iterate in whole waves so the ballots see every lane
-    for (int base = lo; base < hi; base += PWG) {
-        const int i = base + t;
-        const uint32_t kk = (i < hi) ? key32(s[i]) : 0u;
-        const uint32_t dig = kk >> 20;
-        const bool take = kk != 0u && (all || dig > d);
-        const bool cand = kk != 0u && !all && dig == d;
-        const uint32_t at = wave_append(take, &state[row].n_sel);
-        if (take) sel[at] = i;
-        const uint32_t ca = wave_append(cand, &state[row].n_cand);
-        if (cand && ca < CAP) {
-            ck[ca] = kk;
-            cp[ca] = (uint32_t)i;
+#pragma unroll
+    for (int e = 0; e < CHUNK / PWG; ++e) {
+        const uint32_t kk = key32(v[e]);
+        const uint32_t dig = kk >> 21;
+        if (kk == 0u) continue;
+        if (all || dig > d) {
+            l_sel[atomicAdd(&sh[2], 1u)] = lo + e * PWG + t;
+        } else if (dig == d) {
+            const uint32_t a = atomicAdd(&sh[3], 1u);
+            l_ck[a] = kk;
+            l_cp[a] = (uint32_t)(lo + e * PWG + t);
         }
     }
-}
-
-__global__ __launch_bounds__(WG) void topk_finish_kernel(const float* __restrict__ scores, int n, int k,
-                                                         const int32_t* __restrict__ pool,
-                                                         const RowState* __restrict__ state,
-                                                         const int* __restrict__ gsel,
-                                                         const uint32_t* __restrict__ ckey,
-                                                         const uint32_t* __restrict__ cpos,
-                                                         int32_t* __restrict__ out) {
-    __shared__ uint32_t hist[NBINS];
-    __shared__ uint32_t scan[WG];
-    __shared__ int sel[KMAX];
-    __shared__ uint32_t lk[CAP];
-    __shared__ uint32_t lp[CAP];
-    __shared__ uint32_t sh[4];
-    const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const RowState st = state[row];
-    for (int i = t; i < KMAX; i += WG) sel[i] = (i < (int)st.n_sel) ? gsel[row * KMAX + i] : 0x7FFFFFFF;
-    if (t == 0) sh[3] = st.n_sel;
     __syncthreads();
-    const bool all = st.valid <= (uint32_t)k;
-    if (!all) {
-        const uint32_t need = (uint32_t)k - st.n_sel;
-        const uint64_t prefix = (uint64_t)st.digit << 52;
-        const uint64_t mask = (uint64_t)0xFFF << 52;
-        if (st.n_cand <= (uint32_t)CAP) {
-            for (int i = t; i < (int)st.n_cand; i += WG) {
-                lk[i] = ckey[row * CAP + i];
-                lp[i] = cpos[row * CAP + i];
-            }
-            __syncthreads();
-            LdsCands src{lk, lp, (int)st.n_cand};
-            radix_select(src, need, 1, prefix, mask, hist, scan, sh, sel, &sh[3]);
-        } else {
-            GlobalRow src{scores + row * (int64_t)n, n};
-            radix_select(src, need, 1, prefix, mask, hist, scan, sh, sel, &sh[3]);
-        }
+    const uint32_t ns = sh[2], nc = sh[3];
+    if (t == 0) {
+        sh[4] = ns ? atomicAdd(&sg.state[row].n_sel, ns) : 0u;
+        sh[5] = nc ? atomicAdd(&sg.state[row].n_cand, nc) : 0u;
     }
-    const uint32_t total = all ? st.valid : (uint32_t)k;
-    sort_sel(sel);
-    write_out(sel, total, k, pool, row, n / 8, out);
+    __syncthreads();
+    int* sel = sg.sel + row * TOPK_KMAX + sh[4];
+    for (uint32_t j = t; j < ns; j += PWG) sel[j] = l_sel[j];
+    const uint32_t cb = sh[5];
+    uint32_t* ck = sg.ckey + row * TOPK_CAP;
+    uint32_t* cp = sg.cpos + row * TOPK_CAP;
+    for (uint32_t j = t; j < nc && cb + j < (uint32_t)TOPK_CAP; j += PWG) {
+        ck[cb + j] = l_ck[j];
+        cp[cb + j] = l_cp[j];
+    }
 }
 
-size_t large_ws_bytes(int64_t rows) {
-    return (size_t)rows * (NBINS * 4 + sizeof(RowState) + KMAX * 4 + CAP * 8) + 256;
+constexpr int E_CAND = TOPK_CAP / WG;  // candidates per thread in the finish kernel (8)
+
+__global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
+    __shared__ SelectLds sh;
+    __shared__ int sel[TOPK_KMAX];
+    const int sgi = blockIdx.x / segs.rows;
+    const int64_t row = blockIdx.x % segs.rows;
+    const TopkSeg& sg = segs.seg[sgi];
+    const int t = threadIdx.x;
+    const TopkRowState st = sg.state[row];
+    for (int i = t; i < TOPK_KMAX; i += WG) sel[i] = (i < (int)st.n_sel) ? sg.sel[row * TOPK_KMAX + i] : 0x7FFFFFFF;
+    if (t == 0) sh.nsel = st.n_sel;
+    __syncthreads();
+    const bool all = st.valid <= (uint32_t)sg.k;
+    if (!all) {
+        const uint32_t need = (uint32_t)sg.k - st.n_sel;
+        uint64_t prefix = (uint64_t)st.digit << 53;
+        uint64_t mask = (uint64_t)0x7FF << 53;
+        if (st.n_cand <= (uint32_t)TOPK_CAP) {
+            uint32_t key[E_CAND], pos[E_CAND];
+#pragma unroll
+            for (int e = 0; e < E_CAND; ++e) {
+                const int i = e * WG + t;
+                key[e] = i < (int)st.n_cand ? sg.ckey[row * TOPK_CAP + i] : 0u;
+                pos[e] = i < (int)st.n_cand ? sg.cpos[row * TOPK_CAP + i] : 0u;
+            }
+            select_regs<E_CAND>(key, pos, need, 1, prefix, mask, sh);
+#pragma unroll
+            for (int e = 0; e < E_CAND; ++e)
+                if (key[e] != 0u && (composite(key[e], pos[e]) & mask) >= prefix)
+                    sel[atomicAdd(&sh.nsel, 1u)] = (int)pos[e];
+            __syncthreads();
+        } else {
+            select_global_row(sg.scores + row * (int64_t)sg.n, sg.n, need, prefix, mask, sh, sel);
+        }
+    }
+    const uint32_t total = all ? st.valid : (uint32_t)sg.k;
+    int np = 64;
+    while (np < (int)total) np <<= 1;
+    sort_sel(sel, np);
+    const int nblk = sg.n / 8;
+    for (int i = t; i < sg.k; i += WG)
+        sg.out[row * (int64_t)sg.k + i] = (uint32_t)i < total ? map_pos(sel[i], sg.pool, row, nblk) : -1;
 }
 
 }  // namespace
+
+size_t topk_large_ws_bytes(int64_t rows) {
+    return (size_t)rows * (NBINS1 * 4 + sizeof(TopkRowState) + TOPK_KMAX * 4 + TOPK_CAP * 8) + 256;
+}
+
+void topk_carve(void* ws, int64_t rows, TopkSeg* sg) {
+    char* w = static_cast<char*>(ws);
+    sg->hist = reinterpret_cast<uint32_t*>(w);
+    w += (size_t)rows * NBINS1 * 4;
+    sg->state = reinterpret_cast<TopkRowState*>(w);
+    w += (size_t)rows * sizeof(TopkRowState);
+    sg->sel = reinterpret_cast<int*>(w);
+    w += (size_t)rows * TOPK_KMAX * 4;
+    sg->ckey = reinterpret_cast<uint32_t*>(w);
+    w += (size_t)rows * TOPK_CAP * 4;
+    sg->cpos = reinterpret_cast<uint32_t*>(w);
+}
+
+void topk_launch_zero(const TopkSegs& segs, hipStream_t stream) {
+    const int64_t nz = (int64_t)segs.rows * NBINS1;
+    topk_zero_kernel<<<(unsigned)((nz + 255) / 256), 256, 0, stream>>>(segs);
+}
+
+void topk_launch_hist(const TopkSegs& segs, hipStream_t stream) {
+    int chunks = 0;
+    for (int i = 0; i < segs.nseg; ++i) chunks = max(chunks, (segs.seg[i].n + CHUNK - 1) / CHUNK);
+    topk_hist_kernel<<<dim3((unsigned)chunks, (unsigned)(segs.rows * segs.nseg)), PWG, 0, stream>>>(segs);
+}
+
+void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
+    int chunks = 0;
+    for (int i = 0; i < segs.nseg; ++i) chunks = max(chunks, (segs.seg[i].n + CHUNK - 1) / CHUNK);
+    topk_compact_kernel<<<dim3((unsigned)chunks, (unsigned)(segs.rows * segs.nseg)), PWG, 0, stream>>>(segs);
+    topk_finish_kernel<<<(unsigned)(segs.rows * segs.nseg), WG, 0, stream>>>(segs);
+}
+
+void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
+                       hipStream_t stream, uint32_t* hist, TopkRowState* state) {
+    topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool, out, hist, state);
+}
+
+__global__ void zero_ranges_kernel(ZeroRanges z) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int r = 0; r < z.n; ++r)
+        if (i < z.count[r]) z.ptr[r][i] = 0u;
+}
+
+void launch_zero_ranges(const ZeroRanges& z, hipStream_t stream) {
+    int64_t mx = 0;
+    for (int r = 0; r < z.n; ++r) mx = max(mx, z.count[r]);
+    if (mx == 0) return;
+    zero_ranges_kernel<<<(unsigned)((mx + 255) / 256), 256, 0, stream>>>(z);
+}
+
 }  // namespace csa2
 
 using namespace csa2;
 
 extern "C" size_t csa2_topk_workspace_size(int32_t rows, int32_t n, int32_t k) {
     (void)k;
-    if (rows <= 0 || n <= SMALL_N) return 0;
-    return large_ws_bytes(rows);
+    if (rows <= 0 || n <= TOPK_SMALL_N) return 0;
+    return topk_large_ws_bytes(rows);
 }
 
 extern "C" csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, int32_t k,
@@ -392,34 +534,32 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, i
                                  hipStream_t stream) {
     clear_error();
     CSA2_ARG(rows >= 0 && n >= 0, "topk: rows=%d n=%d must be >= 0", rows, n);
-    CSA2_ARG(k >= 1 && k <= KMAX, "topk: k=%d must be in [1, %d]", k, KMAX);
+    CSA2_ARG(k >= 1 && k <= TOPK_KMAX, "topk: k=%d must be in [1, %d]", k, TOPK_KMAX);
     CSA2_ARG(pool_blocks == nullptr || n % 8 == 0, "topk: with a pool map n=%d must be a multiple of 8", n);
+    CSA2_ARG(rows <= 65535, "topk: rows=%d exceeds 65535", rows);
     if (rows == 0) return CSA2_OK;
     CSA2_ARG(out_idx != nullptr, "topk: null out_idx");
     CSA2_ARG(n == 0 || scores != nullptr, "topk: null scores");
-    if (n <= SMALL_N) {
-        topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool_blocks, out_idx);
+    if (n <= TOPK_SMALL_N) {
+        topk_launch_small(scores, rows, n, k, pool_blocks, out_idx, stream);
         return launch_status("topk");
     }
-    const size_t need = large_ws_bytes(rows);
+    const size_t need = topk_large_ws_bytes(rows);
     CSA2_REQUIRE(ws != nullptr && ws_bytes >= need, CSA2_EWORKSPACE,
                  "topk: workspace of %zu bytes required, %zu given", need, ws ? ws_bytes : (size_t)0);
-    CSA2_ARG(((uintptr_t)ws & 15) == 0, "topk: workspace must be 16-byte aligned");
-    char* w = static_cast<char*>(ws);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(w);
-    w += (size_t)rows * NBINS * 4;
-    RowState* state = reinterpret_cast<RowState*>(w);
-    w += (size_t)rows * sizeof(RowState);
-    int* sel = reinterpret_cast<int*>(w);
-    w += (size_t)rows * KMAX * 4;
-    uint32_t* ckey = reinterpret_cast<uint32_t*>(w);
-    w += (size_t)rows * CAP * 4;
-    uint32_t* cpos = reinterpret_cast<uint32_t*>(w);
-    const int64_t zero_n = (int64_t)rows * NBINS;
-    topk_zero_kernel<<<(unsigned)((zero_n + 255) / 256), 256, 0, stream>>>(hist, state, rows);
-    const dim3 grid((unsigned)((n + CHUNK - 1) / CHUNK), (unsigned)rows);
-    topk_hist_kernel<<<grid, PWG, 0, stream>>>(scores, n, hist, state);
-    topk_compact_kernel<<<grid, PWG, 0, stream>>>(scores, n, k, hist, state, sel, ckey, cpos);
-    topk_finish_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool_blocks, state, sel, ckey, cpos, out_idx);
+    CSA2_ARG(aligned(ws, 16), "topk: workspace must be 16-byte aligned");
+    TopkSegs segs{};
+    segs.nseg = 1;
+    segs.rows = rows;
+    TopkSeg& sg = segs.seg[0];
+    sg.scores = scores;
+    sg.n = n;
+    sg.k = k;
+    sg.pool = pool_blocks;
+    sg.out = out_idx;
+    topk_carve(ws, rows, &sg);
+    topk_launch_zero(segs, stream);
+    topk_launch_hist(segs, stream);
+    topk_launch_select(segs, stream);
     return launch_status("topk");
 }
