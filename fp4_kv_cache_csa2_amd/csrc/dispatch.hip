@@ -15,7 +15,7 @@ namespace {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct LayerWs {
-    size_t scores, block_max, pool_scores, topk, rhist, rstate, attn, total;
+    size_t scores, block_max, pool_scores, topk, attn, total;
     size_t topk_bytes, attn_bytes;
 };
 
@@ -34,11 +34,6 @@ LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
     w.topk = off;
     w.topk_bytes = tk;
     off = align256(off + tk);
-    // first-digit histogram of the Reindex pool scores (kept zeroed between uses)
-    w.rhist = off;
-    off = align256(off + (size_t)rows * NBINS1 * 4);
-    w.rstate = off;
-    off = align256(off + (size_t)rows * sizeof(TopkRowState));
     w.attn = off;
     w.attn_bytes = attn_workspace_bytes(rows, H, D);
     off = align256(off + w.attn_bytes);
@@ -93,8 +88,6 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     float* block_max = reinterpret_cast<float*>(ws + w.block_max);
     float* pool_scores = reinterpret_cast<float*>(ws + w.pool_scores);
     void* tk = ws + w.topk;
-    uint32_t* rhist = reinterpret_cast<uint32_t*>(ws + w.rhist);
-    TopkRowState* rstate = reinterpret_cast<TopkRowState*>(ws + w.rstate);
     (void)w.topk_bytes;
     void* aw = ws + w.attn;
     const int rows32 = (int)rows;
@@ -126,12 +119,6 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             z.ptr[z.n] = reinterpret_cast<uint32_t*>(segs.seg[i].state);
             z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
         }
-        if (a->build_pool) {  // the Reindex layers that follow start from a clean histogram
-            z.ptr[z.n] = rhist;
-            z.count[z.n++] = rows * NBINS1;
-            z.ptr[z.n] = reinterpret_cast<uint32_t*>(rstate);
-            z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
-        }
         launch_zero_ranges(z, stream);
         s = index_full_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, n, scores,
                             a->build_pool ? block_max : nullptr, se ? se->hist : nullptr, se ? se->state : nullptr,
@@ -142,10 +129,12 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
         if (a->build_pool && !b_large) topk_launch_small(block_max, rows32, nb, a->P, nullptr, st->pool, stream);
         s = launch_status("layer_forward");
     } else if (mode == CSA2_REINDEX) {
-        s = index_reindex_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, st->pool, a->P, pool_scores, rhist,
-                               rstate, stream);
+        // (the pool scores' first-digit histogram is built inside the select:
+        // flushing it from the scan's many workgroups with contended atomics costs more)
+        s = index_reindex_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, st->pool, a->P, pool_scores, nullptr,
+                               nullptr, stream);
         if (s == CSA2_OK) {
-            topk_launch_small(pool_scores, rows32, 8 * a->P, a->K, st->pool, st->idx, stream, rhist, rstate);
+            topk_launch_small(pool_scores, rows32, 8 * a->P, a->K, st->pool, st->idx, stream);
             s = launch_status("layer_forward");
         }
     }

@@ -33,7 +33,10 @@ constexpr int WG = 1024;        // single-row workgroup
 constexpr int NW = WG / 64;     // its wavefronts
 constexpr int E_SMALL = TOPK_SMALL_N / WG;  // keys per thread in the small path (16)
 constexpr int PWG = 256;        // threads of the grid-wide passes
-constexpr int CHUNK = 4096;     // positions per workgroup in the grid-wide passes (16 per thread)
+constexpr int CHUNK = 4096;     // positions per workgroup in the histogram pass (16 per thread)
+constexpr int CCHUNK = 16384;   // positions per workgroup in the split pass (64 per thread): few workgroups
+                                // per row keep the two per-row list counters lightly contended
+constexpr int LCAP = 4096;      // candidates a split workgroup can hold in LDS
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
     return ((uint64_t)key << 32) | (uint64_t)(~pos);
@@ -42,7 +45,7 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
 // ---------------------------------------------------------------------------
 // Block-wide helpers for a 1024-thread workgroup.
 struct SelectLds {
-    uint32_t hist[NBINS1];
+    uint32_t hist[2][NBINS1];  // double-buffered: a pass zeroes the buffer of the pass after next
     uint32_t wsum[NW];
     uint32_t bin, above, total, nsel;
 };
@@ -58,38 +61,43 @@ __device__ uint32_t block_excl_scan(uint32_t v, SelectLds& sh, uint32_t* total) 
     }
     if (lane == 63) sh.wsum[wid] = x;
     __syncthreads();
-    if (wid == 0) {
-        uint32_t s = lane < NW ? sh.wsum[lane] : 0u;
+    uint32_t base = 0, tot = 0;
 #pragma unroll
-        for (int off = 1; off < NW; off <<= 1) {
-            const uint32_t y = __shfl_up(s, off);
-            if (lane >= off) s += y;
-        }
-        if (lane < NW) sh.wsum[lane] = s;
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t ws = sh.wsum[w];
+        base += (w < wid) ? ws : 0u;
+        tot += ws;
     }
-    __syncthreads();
-    const uint32_t base = wid ? sh.wsum[wid - 1] : 0u;
-    *total = sh.wsum[NW - 1];
-    __syncthreads();
+    *total = tot;
+    __syncthreads();  // wsum may be rewritten by the next call
     return base + x - v;
 }
 
 // The bin d of hist[0..nb) with  above < need <= above + hist[d]  (above =
-// sum of the bins above d): written to sh.bin / sh.above.
-__device__ void find_bin(SelectLds& sh, int nb, uint32_t need) {
+// sum of the bins above d): written to sh.bin / sh.above.  Two barriers.
+__device__ void find_bin(const uint32_t* hist, SelectLds& sh, int nb, uint32_t need) {
     const int per = (nb + WG - 1) / WG;  // bins per thread, thread 0 owns the top bins
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     uint32_t local = 0;
     for (int i = 0; i < per; ++i) {
         const int bin = nb - 1 - (t * per + i);
-        if (bin >= 0) local += sh.hist[bin];
+        if (bin >= 0) local += hist[bin];
     }
-    uint32_t tot;
-    uint32_t above = block_excl_scan(local, sh, &tot);
+    uint32_t x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) sh.wsum[wid] = x;
+    __syncthreads();
+    uint32_t above = x - local;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) above += (w < wid) ? sh.wsum[w] : 0u;
     for (int i = 0; i < per; ++i) {
         const int bin = nb - 1 - (t * per + i);
         if (bin < 0) break;
-        const uint32_t h = sh.hist[bin];
+        const uint32_t h = hist[bin];
         if (above < need && need <= above + h) {
             sh.bin = (uint32_t)bin;
             sh.above = above;
@@ -102,31 +110,38 @@ __device__ void find_bin(SelectLds& sh, int nb, uint32_t need) {
 // Radix select over register-resident elements (key 0 = not in the set).
 // On return, element (key, pos) is selected iff key != 0 and
 // (composite & mask) >= prefix; exactly `need` elements qualify.
+// Requires sh.hist[first_pass & 1] zeroed on entry; leaves both buffers zeroed.
 template <int E>
 __device__ void select_regs(const uint32_t (&key)[E], const uint32_t (&pos)[E], uint32_t need, int first_pass,
                             uint64_t& prefix, uint64_t& mask, SelectLds& sh) {
     const int shifts[6] = {53, 42, 32, 21, 10, 0};
     const int widths[6] = {11, 11, 10, 11, 11, 10};
+    // the other buffer is zeroed while this pass counts
+    for (int i = threadIdx.x; i < NBINS1; i += WG) sh.hist[(first_pass + 1) & 1][i] = 0u;
     for (int pass = first_pass; pass < 6; ++pass) {
+        uint32_t* h = sh.hist[pass & 1];
         const int sh_ = shifts[pass], nb = 1 << widths[pass];
-        for (int i = threadIdx.x; i < nb; i += WG) sh.hist[i] = 0u;
-        __syncthreads();
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             if (key[e] == 0u) continue;
             const uint64_t c = composite(key[e], pos[e]);
-            if ((c & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(c >> sh_) & (uint32_t)(nb - 1)], 1u);
+            if ((c & mask) == prefix) atomicAdd(&h[(uint32_t)(c >> sh_) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        find_bin(sh, nb, need);
+        find_bin(h, sh, nb, need);
         const uint32_t d = sh.bin;
         need -= sh.above;
         prefix |= (uint64_t)d << sh_;
         mask |= (uint64_t)(nb - 1) << sh_;
-        const bool done = sh.hist[d] == need;
+        const bool done = h[d] == need;
+        // every thread has read h[d] (after find_bin's last barrier read): clear
+        // this buffer for the pass after next; the barrier inside the next
+        // pass's find_bin orders it before that pass's atomics
         __syncthreads();
+        for (int i = threadIdx.x; i < NBINS1; i += WG) h[i] = 0u;
         if (done) break;
     }
+    __syncthreads();
 }
 
 // Slow general radix select over a row in global memory, restricted to the
@@ -138,23 +153,24 @@ __device__ void select_global_row(const float* s, int n, uint32_t need, uint64_t
     const int widths[6] = {11, 11, 10, 11, 11, 10};
     int pass = 0;
     while (pass < 6 && ((mask >> shifts[pass]) & 1u)) ++pass;  // skip decided digits
+    uint32_t* h = sh.hist[0];
     for (; pass < 6; ++pass) {
         const int sh_ = shifts[pass], nb = 1 << widths[pass];
-        for (int i = threadIdx.x; i < nb; i += WG) sh.hist[i] = 0u;
+        for (int i = threadIdx.x; i < nb; i += WG) h[i] = 0u;
         __syncthreads();
         for (int i = threadIdx.x; i < n; i += WG) {
             const uint32_t k = key32(s[i]);
             if (k == 0u) continue;
             const uint64_t c = composite(k, (uint32_t)i);
-            if ((c & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(c >> sh_) & (uint32_t)(nb - 1)], 1u);
+            if ((c & mask) == prefix) atomicAdd(&h[(uint32_t)(c >> sh_) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        find_bin(sh, nb, need);
+        find_bin(h, sh, nb, need);
         const uint32_t d = sh.bin;
         need -= sh.above;
         prefix |= (uint64_t)d << sh_;
         mask |= (uint64_t)(nb - 1) << sh_;
-        const bool done = sh.hist[d] == need;
+        const bool done = h[d] == need;
         __syncthreads();
         if (done) break;
     }
@@ -225,11 +241,29 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     const float* s = scores + row * (int64_t)n;
     uint32_t key[E_SMALL], pos[E_SMALL];
     uint32_t cnt = 0;
+    // thread t owns positions 16t..16t+15 (ordered output); read them as four
+    // 16-byte loads when the row is 16-byte aligned (strided scalar loads
+    // thrash the vector cache and cost several microseconds here)
+    if ((n & 3) == 0 && (((uintptr_t)s) & 15) == 0 && (t + 1) * E_SMALL <= n) {
+        const float4* s4 = reinterpret_cast<const float4*>(s) + t * (E_SMALL / 4);
+#pragma unroll
+        for (int e = 0; e < E_SMALL / 4; ++e) {
+            const float4 v = s4[e];
+            key[4 * e] = key32(v.x);
+            key[4 * e + 1] = key32(v.y);
+            key[4 * e + 2] = key32(v.z);
+            key[4 * e + 3] = key32(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E_SMALL; ++e) {
+            const int i = t * E_SMALL + e;
+            key[e] = i < n ? key32(s[i]) : 0u;
+        }
+    }
 #pragma unroll
     for (int e = 0; e < E_SMALL; ++e) {
-        const int i = t * E_SMALL + e;
-        pos[e] = (uint32_t)i;
-        key[e] = i < n ? key32(s[i]) : 0u;
+        pos[e] = (uint32_t)(t * E_SMALL + e);
         cnt += key[e] != 0u;
     }
     uint64_t prefix = 0, mask = 0;
@@ -237,8 +271,9 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     if (hist != nullptr) {
         uint32_t* hr = hist + row * NBINS1;
         for (int i = t; i < NBINS1; i += WG) {
-            sh.hist[i] = hr[i];
+            sh.hist[0][i] = hr[i];
             hr[i] = 0u;
+            sh.hist[1][i] = 0u;  // select_regs starts at pass 1 with buffer 1
         }
         if (t == 0) {
             sh.total = state[row].valid;
@@ -247,17 +282,18 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
         __syncthreads();
         valid = sh.total;
         if (valid > (uint32_t)k) {
-            find_bin(sh, NBINS1, (uint32_t)k);
+            find_bin(sh.hist[0], sh, NBINS1, (uint32_t)k);
             const uint32_t d = sh.bin;
             const uint32_t need = (uint32_t)k - sh.above;
             prefix = (uint64_t)d << 53;
             mask = (uint64_t)0x7FF << 53;
-            const bool done = sh.hist[d] == need;
+            const bool done = sh.hist[0][d] == need;
             __syncthreads();
             if (!done) select_regs<E_SMALL>(key, pos, need, 1, prefix, mask, sh);
         }
     } else {
-        block_excl_scan(cnt, sh, &valid);
+        for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
+        block_excl_scan(cnt, sh, &valid);  // its barriers also order the zeroing
         if (valid > (uint32_t)k) select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
     }
     const bool all = valid <= (uint32_t)k;
@@ -321,16 +357,20 @@ __global__ __launch_bounds__(PWG) void topk_hist_kernel(TopkSegs segs) {
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Threshold bin of a row from its global histogram (PWG threads, 8 bins each).
-__device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* scan, uint32_t* d_out,
+// Threshold bin of a row from its global histogram (PWG threads, 8 bins
+// each): the histogram is read with coalesced loads into LDS first.
+__device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* lh, uint32_t* scan, uint32_t* d_out,
                               uint32_t* above_out) {
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     constexpr int per = NBINS1 / PWG;
+#pragma unroll
+    for (int i = 0; i < per; ++i) lh[i * PWG + t] = gh[i * PWG + t];
+    __syncthreads();
     uint32_t mine[per];
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
-        mine[i] = gh[NBINS1 - 1 - (t * per + i)];
+        mine[i] = lh[NBINS1 - 1 - (t * per + i)];
         local += mine[i];
     }
     uint32_t x = local;
@@ -362,50 +402,70 @@ __global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
     __shared__ uint32_t scan[PWG / 64];
     __shared__ uint32_t sh[6];
     __shared__ int l_sel[TOPK_KMAX];
-    __shared__ uint32_t l_ck[CHUNK], l_cp[CHUNK];
+    __shared__ uint32_t l_ck[LCAP], l_cp[LCAP];
+    uint32_t* lh = l_ck;  // the row histogram is staged here before the candidates arrive
     const int sgi = blockIdx.y / segs.rows;
     const int64_t row = blockIdx.y % segs.rows;
     const TopkSeg& sg = segs.seg[sgi];
-    if ((int)blockIdx.x * CHUNK >= sg.n) return;
+    if ((int)blockIdx.x * CCHUNK >= sg.n) return;
     const int t = threadIdx.x;
-    const int lo = blockIdx.x * CHUNK;
-    const int hi = min(sg.n, lo + CHUNK);
+    const int lo = blockIdx.x * CCHUNK;
+    const int hi = min(sg.n, lo + CCHUNK);
     const float* s = sg.scores + row * (int64_t)sg.n;
-    float v[CHUNK / PWG];
-#pragma unroll
-    for (int e = 0; e < CHUNK / PWG; ++e) {
-        const int i = lo + e * PWG + t;
-        v[e] = i < hi ? s[i] : -INFINITY;
-    }
     if (t < 2) sh[2 + t] = 0u;
     const uint32_t valid = sg.state[row].valid;
     const bool all = valid <= (uint32_t)sg.k;
     uint32_t d = 0;
     if (!all) {
-        row_threshold(sg.hist + row * NBINS1, (uint32_t)sg.k, scan, &sh[0], &sh[1]);
+        row_threshold(sg.hist + row * NBINS1, (uint32_t)sg.k, lh, scan, &sh[0], &sh[1]);
         d = sh[0];
         if (blockIdx.x == 0 && t == 0) sg.state[row].digit = d;
-    } else {
-        __syncthreads();
     }
+    __syncthreads();  // sh[2..3] initialised; lh free for candidates
+    const bool vec = (sg.n & 3) == 0 && (((uintptr_t)s) & 15) == 0;
+    // 4 rounds of 16 positions per thread: position lo + (r*PWG + t)*4*4 ...
+    for (int rd = 0; rd < CCHUNK / (PWG * 16); ++rd) {
+        float v[16];
+        const int base = lo + rd * PWG * 16;
 #pragma unroll
-    for (int e = 0; e < CHUNK / PWG; ++e) {
-        const uint32_t kk = key32(v[e]);
-        const uint32_t dig = kk >> 21;
-        if (kk == 0u) continue;
-        if (all || dig > d) {
-            l_sel[atomicAdd(&sh[2], 1u)] = lo + e * PWG + t;
-        } else if (dig == d) {
-            const uint32_t a = atomicAdd(&sh[3], 1u);
-            l_ck[a] = kk;
-            l_cp[a] = (uint32_t)(lo + e * PWG + t);
+        for (int e = 0; e < 4; ++e) {
+            const int i = base + (e * PWG + t) * 4;  // 4 consecutive positions
+            if (vec && i + 3 < hi) {
+                const float4 f = *reinterpret_cast<const float4*>(s + i);
+                v[4 * e] = f.x;
+                v[4 * e + 1] = f.y;
+                v[4 * e + 2] = f.z;
+                v[4 * e + 3] = f.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * e + j] = (i + j < hi) ? s[i + j] : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t kk = key32(v[e]);
+            if (kk == 0u) continue;
+            const uint32_t dig = kk >> 21;
+            const int i = base + ((e >> 2) * PWG + t) * 4 + (e & 3);
+            if (all || dig > d) {
+                l_sel[atomicAdd(&sh[2], 1u)] = i;
+            } else if (dig == d) {
+                const uint32_t a = atomicAdd(&sh[3], 1u);
+                if (a < (uint32_t)LCAP) {
+                    l_ck[a] = kk;
+                    l_cp[a] = (uint32_t)i;
+                }
+            }
         }
     }
     __syncthreads();
     const uint32_t ns = sh[2], nc = sh[3];
     if (t == 0) {
         sh[4] = ns ? atomicAdd(&sg.state[row].n_sel, ns) : 0u;
-        sh[5] = nc ? atomicAdd(&sg.state[row].n_cand, nc) : 0u;
+        // a local overflow pushes the row's count past the capacity: the finish
+        // pass then selects from the whole row instead of the candidate list
+        const uint32_t add = nc > (uint32_t)LCAP ? (uint32_t)TOPK_CAP + 1u : nc;
+        sh[5] = add ? atomicAdd(&sg.state[row].n_cand, add) : 0u;
     }
     __syncthreads();
     int* sel = sg.sel + row * TOPK_KMAX + sh[4];
@@ -413,7 +473,7 @@ __global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
     const uint32_t cb = sh[5];
     uint32_t* ck = sg.ckey + row * TOPK_CAP;
     uint32_t* cp = sg.cpos + row * TOPK_CAP;
-    for (uint32_t j = t; j < nc && cb + j < (uint32_t)TOPK_CAP; j += PWG) {
+    for (uint32_t j = t; j < nc && j < (uint32_t)LCAP && cb + j < (uint32_t)TOPK_CAP; j += PWG) {
         ck[cb + j] = l_ck[j];
         cp[cb + j] = l_cp[j];
     }
@@ -430,6 +490,7 @@ __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
     const int t = threadIdx.x;
     const TopkRowState st = sg.state[row];
     for (int i = t; i < TOPK_KMAX; i += WG) sel[i] = (i < (int)st.n_sel) ? sg.sel[row * TOPK_KMAX + i] : 0x7FFFFFFF;
+    for (int i = t; i < NBINS1; i += WG) sh.hist[1][i] = 0u;
     if (t == 0) sh.nsel = st.n_sel;
     __syncthreads();
     const bool all = st.valid <= (uint32_t)sg.k;
@@ -496,7 +557,7 @@ void topk_launch_hist(const TopkSegs& segs, hipStream_t stream) {
 
 void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
     int chunks = 0;
-    for (int i = 0; i < segs.nseg; ++i) chunks = max(chunks, (segs.seg[i].n + CHUNK - 1) / CHUNK);
+    for (int i = 0; i < segs.nseg; ++i) chunks = max(chunks, (segs.seg[i].n + CCHUNK - 1) / CCHUNK);
     topk_compact_kernel<<<dim3((unsigned)chunks, (unsigned)(segs.rows * segs.nseg)), PWG, 0, stream>>>(segs);
     topk_finish_kernel<<<(unsigned)(segs.rows * segs.nseg), WG, 0, stream>>>(segs);
 }
