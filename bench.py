@@ -23,6 +23,72 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+HERE = os.path.dirname(os.path.abspath(__file__))
+SCAN_KERNEL = "index_kernel<128, false, true>"
+SCAN_SOURCES = ("fp4_kv_cache_csa2_amd/csrc/indexer.hip", "fp4_kv_cache_csa2_amd/csrc/internal.h",
+                "fp4_kv_cache_csa2_amd/csrc/common.h")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "index_scan_hbm_traffic.md")
+
+
+def scan_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_per_dispatch(db_path, counter):
+    """{dispatch_id: (kernel_name, grid_size, value in KiB)} for one counter of a rocprofv3 database."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select dispatch_id, kernel_name, grid_size, value from counters_collection "
+                       "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+    con.close()
+    out = {}
+    for d, k, g, v in rows:
+        name, grid, acc = out.get(d, (k, g, 0.0))
+        out[d] = (name, grid, acc + float(v))  # summed over the per-instance records
+    return out
+
+
+def pmc_summary(fetch_db, write_db, copy_mib):
+    """Scale the scan kernel's FETCH_SIZE / WRITE_SIZE by what the same counters
+    read for the plain copy of known size that the run made first."""
+    copy_bytes = copy_mib * 2**20
+    res = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        d = pmc_per_dispatch(db, counter)
+        copies = [v for k, g, v in d.values() if "copyBuffer" in k][:3]
+        scans = [v for k, g, v in d.values() if SCAN_KERNEL in k]
+        if len(copies) < 3 or not scans:
+            raise SystemExit(f"{db}: {len(copies)} calibration copies, {len(scans)} scan dispatches")
+        copy_kib = sum(copies) / len(copies)
+        factor = copy_bytes / (copy_kib * 1024.0)
+        scan_kib = sum(scans) / len(scans)
+        res[counter] = dict(copy_kib=round(copy_kib, 1), factor=round(factor, 5), scan_kib=round(scan_kib, 1),
+                            scan_bytes=round(scan_kib * 1024.0 * factor), dispatches=len(scans))
+    rec = {"kernel": SCAN_KERNEL, "source_hash": scan_source_hash(), "copy_mib": copy_mib,
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "traffic_bytes_per_launch": res["FETCH_SIZE"]["scan_bytes"] + res["WRITE_SIZE"]["scan_bytes"]}
+    return rec
+
+
+def read_traffic():
+    """The scan's measured HBM bytes per launch, if taken on the current kernel sources."""
+    import re
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != scan_source_hash() or rec.get("kernel") != SCAN_KERNEL:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def parse():
@@ -34,6 +100,12 @@ def parse():
     ap.add_argument("--scan-reps", type=int, default=21, help="timed launches of the indexer scan")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run three plain device-to-device copies of this many MiB (the calibration "
+                         "kernel for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="no GPU work: turn two rocprofv3 --pmc databases (FETCH_SIZE, then WRITE_SIZE) of a "
+                         "run made with --copy-probe-mib into the traffic summary")
     return ap.parse_args()
 
 
@@ -91,6 +163,9 @@ def cpu_baseline(inst, budget_s):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_probe_mib), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path",
               file=sys.stderr)
@@ -103,6 +178,13 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     assert w.Q == 1, "the benchmark measures decode"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib * 2**20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inst = workload.make_instance(w)
     run = workload.StackRunner(inst)
     dev = inst.latent.device
@@ -190,7 +272,7 @@ def main():
         "step_hbm_GBps": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "index_kernel<128,false> (Full-mode indexer scan)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(),
                      "alg_bytes_per_launch": ab["full"], "avg_launch_ms": round(scan_avg_ms, 5),
                      "launches_timed": len(scan_ms) - 1},
     }
