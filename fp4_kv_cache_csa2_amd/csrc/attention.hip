@@ -9,15 +9,20 @@
 //
 // One workgroup = one query row x a range of 16-key chunks; wave w owns query
 // heads 16w..16w+15 (heads are the MFMA N dimension, keys the M dimension).
-// Per chunk the workgroup gathers 16 keys once, dequantises them in registers
-// (an E2M1 x E4M3 product has <= 6 significant bits, so it is exact in bf16
-// and fp16) into two LDS tiles: K row-major bf16 for S^T = K Q^T
-// (v_mfma_f32_16x16x32_bf16) and V^T fp16 for O^T = V^T P^T
-// (v_mfma_f32_16x16x16_f16).  The S^T accumulator layout (lane holds keys
+// Per chunk the workgroup gathers 16 keys once and dequantises them in
+// registers into two fp16 LDS tiles: K row-major for S^T = K Q^T
+// (v_mfma_f32_16x16x32_f16) and V^T for O^T = V^T P^T
+// (v_mfma_f32_16x16x16_f16).  An E2M1 x E4M3 product has <= 6 significant
+// bits and lies in [2^-10, 2688], so it is exact in fp16; the E2M1 values come
+// from a byte-permute table.  The query is pre-scaled per head by a power of
+// two so that its largest element sits in [2^14, 2^15) (exact), and the scale
+// is folded into the logit scale.  The S^T accumulator layout (lane holds keys
 // 4g..4g+3 of head lane%16) is exactly the P^T operand layout of the second
-// MFMA, so P never leaves registers.  Softmax is online (running max / sum in
-// the log2 domain).  Few rows (decode) split the keys over several workgroups
-// whose normalised partials (o, lse) are merged by a second kernel.
+// MFMA, so P never leaves registers.  Softmax is online in the log2 domain with
+// a lazy maximum: the running maximum moves (and O is rescaled) only when a
+// chunk exceeds it by more than 2^8, so P <= 256 stays well inside fp16.  Few
+// rows (decode) split the keys over several workgroups whose normalised
+// partials (o, lse) are merged by a second kernel.
 #include "internal.h"
 
 namespace csa2 {
@@ -48,95 +53,165 @@ struct AttnParams {
     float* part_lse;           // [rows][nsplit][H]
 };
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// E2M1 magnitude x 2^8 -> high byte of its fp16 value (the low byte is 0):
+// magnitudes 0, 0.5, 1, 1.5 | 2, 3, 4, 6, times 256
+constexpr uint32_t F16HI_LO = 0x5E5C5800u, F16HI_HI = 0x66646260u;
+
+// E4M3FN scale byte -> fp16 bits of scale x 2^-8, twice (exact: E4M3 and fp16
+// share the mantissa alignment, so the byte shifted into the fp16 exponent /
+// mantissa fields is the scale with its exponent bias off by 8; subnormal
+// scales land on fp16 subnormals).
+__device__ __forceinline__ uint32_t e4m3_f16x2_over256(uint32_t code) { return (code << 7) | (code << 23); }
+
+// 8 FP4 codes (one 32-bit word, channel 2i in the low nibble of byte i) times
+// the scale -> four fp16 pairs (channels 2i, 2i+1).  (E2M1 x 2^8) x (E4M3 x
+// 2^-8) is exact: <= 6 significant bits in [2^-10, 2688].
+__device__ __forceinline__ void fp4x8_to_f16(uint32_t w, uint32_t sc2, uint32_t (&out)[4]) {
+    const uint32_t ev = w & 0x07070707u;         // magnitudes of channels 0, 2, 4, 6
+    const uint32_t od = (w >> 4) & 0x07070707u;  // magnitudes of channels 1, 3, 5, 7
+    const uint32_t hbe = __builtin_amdgcn_perm(F16HI_HI, F16HI_LO, ev) | ((w << 4) & 0x80808080u);
+    const uint32_t hbo = __builtin_amdgcn_perm(F16HI_HI, F16HI_LO, od) | (w & 0x80808080u);
+    const uint32_t sel[4] = {0x040C000Cu, 0x050C010Cu, 0x060C020Cu, 0x070C030Cu};
+    const f16x2 sc = *reinterpret_cast<const f16x2*>(&sc2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t pr = __builtin_amdgcn_perm(hbo, hbe, sel[i]);
+        const f16x2 v = *reinterpret_cast<const f16x2*>(&pr) * sc;
+        out[i] = *reinterpret_cast<const uint32_t*>(&v);
+    }
 }
 
-__device__ __forceinline__ float e4m3_val(uint32_t code) {
-    uint32_t e = (code >> 3) & 15, m = code & 7;
-    if (e == 0) return (float)m * 0.001953125f;
-    return __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
-
-__device__ __forceinline__ float e2m1_val(uint32_t code) {
-    uint32_t mag = code & 7u;
-    float a = (mag < 2u) ? 0.5f * (float)mag : __uint_as_float(((mag >> 1) + 126u) << 23 | (mag & 1u) << 22);
-    return (code & 8u) ? -a : a;
-}
-
-// byte offset of V^T[d][key 4kq] inside the padded transposed tile
+// byte offset of V^T[d][key 4kq] inside the padded transposed tile (rows of
+// 16 keys x fp16 = 32 B, plus 16 B after every 8 rows against bank conflicts)
 __device__ __forceinline__ int vt_off(int d, int kq) { return d * 32 + (d >> 3) * 16 + kq * 8; }
+// the same for d = 16 dt + c16 (c16 < 16), split so that dt becomes an immediate offset
+__device__ __forceinline__ int vt_base(int c16, int kq) { return c16 * 32 + (c16 >> 3) * 16 + kq * 8; }
+constexpr int VT_DT = 16 * 32 + 2 * 16;  // bytes per 16 rows
 
 constexpr int MAX_CPS = 64;  // chunks per split (keys per workgroup <= 1024)
+constexpr int RING = 4;      // chunks whose raw bytes are in flight / staged in LDS at once
 
-// Raw data of one dequantisation item (4 keys x 8 channels): FP4 code words and
-// scale bytes, or 4 x 8 bf16 window channels.
-struct RawItem {
-    uint4 w[4];
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// Asynchronous global -> LDS copies (LDS DMA): lane l of the wave writes its
+// 16 (4) bytes at lds_base + 16 l (4 l); the wave's vmcnt counts the copy until
+// it lands.
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((global_void_ptr)(const_cast<void*>(src)), (lds_void_ptr)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((global_void_ptr)(const_cast<void*>(src)), (lds_void_ptr)lds_base, 4, 0, 0);
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() would also wait for
+// every outstanding LDS copy (they count as vector memory), including the ring
+// refills still in flight; here only this wave's LDS instructions are drained
+// (lgkmcnt 0), copies the caller needs are waited for explicitly, and the
+// compiler may not move memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Raw bytes of one 16-key chunk in an LDS ring slot.  Selected entries: the
+// FP4 code rows [16][D/2] then the scale rows [16][D/16]; window: the bf16
+// rows [16][D].  Copies per chunk (one wave instruction each, spread over the
+// waves round-robin): codes D/128 x 16 B/lane, scales ceil(D/256) x 4 B/lane;
+// window D/32 x 16 B/lane.
+template <int D>
+struct Stage {
+    static constexpr int SLOT = CHUNK_KEYS * 2 * D;
+    static constexpr int SCALE_OFF = CHUNK_KEYS * D / 2;
+    static constexpr int N_CODE = D / 128;
+    static constexpr int N_SCALE = (D + 255) / 256;
+    static constexpr int N_WIN = D / 32;
 };
 
-template <int D>
-__device__ __forceinline__ void load_item(const AttnParams& p, bool sparse, const int64_t* krow, int kq, int co,
-                                          RawItem& raw) {
+// A key without a row copies row 0 instead: its values are finite and its
+// softmax weight is exactly 0, so it adds nothing.
+template <int D, int NW>
+__device__ __forceinline__ void stage_chunk(const AttnParams& p, bool sparse, const int64_t* kr, uint8_t* slot, int w,
+                                            int lane) {
+    using S = Stage<D>;
+    if (sparse) {
+        constexpr int PPK = D / 32;  // 16-byte pieces per code row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t r = krow[4 * kq + i];
-        if (r < 0) {
-            raw.w[i] = make_uint4(0, 0, 0, 0);
-        } else if (sparse) {
-            raw.w[i].x = *reinterpret_cast<const uint32_t*>(p.codes + r * (D / 2) + co * 4);
-            raw.w[i].y = p.scales[r * (D / 16) + (co >> 1)];
-        } else {
-            raw.w[i] = *reinterpret_cast<const uint4*>(p.swa + r * D + co * 8);
+        for (int jj = 0; jj < (S::N_CODE + NW - 1) / NW; ++jj) {
+            const int j = jj * NW + w;
+            if (j >= S::N_CODE) break;
+            const int piece = j * 64 + lane;
+            const int64_t r = max(kr[piece / PPK], (int64_t)0);
+            dma16_to_lds(p.codes + r * (D / 2) + (piece % PPK) * 16, slot + j * 1024);
+        }
+        constexpr int DPK = D / 64;  // 4-byte pieces per scale row
+#pragma unroll
+        for (int k = 0; k < S::N_SCALE; ++k) {
+            if ((S::N_CODE + k) % NW != w) continue;
+            const int piece = k * 64 + lane;  // lanes past the 16 rows land in the slot's unused tail
+            const int64_t r = piece < CHUNK_KEYS * DPK ? max(kr[piece / DPK], (int64_t)0) : 0;
+            dma4_to_lds(p.scales + r * (D / 16) + (piece % DPK) * 4, slot + S::SCALE_OFF + k * 256);
+        }
+    } else {
+        constexpr int PPK = D / 8;  // 16-byte pieces per bf16 row
+#pragma unroll
+        for (int jj = 0; jj < (S::N_WIN + NW - 1) / NW; ++jj) {
+            const int j = jj * NW + w;
+            if (j >= S::N_WIN) break;
+            const int piece = j * 64 + lane;
+            const int64_t r = max(kr[piece / PPK], (int64_t)0);
+            dma16_to_lds(reinterpret_cast<const uint8_t*>(p.swa) + r * (2 * D) + (piece % PPK) * 16,
+                           slot + j * 1024);
         }
     }
 }
 
-// Dequantise one item into the K tile (bf16, row-major, swizzled) and the V^T
-// tile (fp16, transposed, padded).
-template <int D>
-__device__ __forceinline__ void store_item(bool sparse, const RawItem& raw, int kq, int co, uint4* ktile,
-                                           uint8_t* vtile) {
-    constexpr int CPR = D / 8;
-    uint32_t kb16[4][4];
-    uint16_t vh[8][4];
+// Dequantise one item (4 keys x 8 channels) from a staged chunk into the K tile
+// (fp16, rows of D + 8 halves: the pad spreads the 16 rows of an MFMA operand
+// read over all banks) and the V^T tile (fp16, transposed, padded).  Keys
+// without a row hold row 0's finite values; their softmax weight is exactly 0.
+// Window rows are bf16; their fp16 conversion is exact for 2^-14 <= |v| < 65504.
+template <int D, bool SPARSE>
+__device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, uint4* ktile, uint8_t* vtile) {
+    constexpr int KROW = D / 8 + 1;  // uint4 per K-tile row
+    uint32_t kh[4][4];               // fp16 pairs: [key][channel pair]
+    if (SPARSE) {
+        uint32_t cw[4], sb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float v[8];
-        if (sparse) {
-            const uint32_t cw = raw.w[i].x;
-            const float s = e4m3_val(raw.w[i].y);
+        for (int i = 0; i < 4; ++i) {
+            const int key = 4 * kq + i;
+            cw[i] = *reinterpret_cast<const uint32_t*>(slot + key * (D / 2) + co * 4);
+            sb[i] = slot[Stage<D>::SCALE_OFF + key * (D / 16) + (co >> 1)];
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = e2m1_val((cw >> (4 * e)) & 15u) * s;
-        } else {
-            const uint32_t wv[4] = {raw.w[i].x, raw.w[i].y, raw.w[i].z, raw.w[i].w};
+        for (int i = 0; i < 4; ++i) fp4x8_to_f16(cw[i], e4m3_f16x2_over256(sb[i]), kh[i]);
+    } else {
+        uint4 u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const uint4*>(slot + (4 * kq + i) * (2 * D) + co * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wv[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[2 * e] = bf16_lo(wv[e]);
-                v[2 * e + 1] = bf16_hi(wv[e]);
+                const f16x2 v = f16x2{(_Float16)bf16_lo(wv[e]), (_Float16)bf16_hi(wv[e])};
+                kh[i][e] = *reinterpret_cast<const uint32_t*>(&v);
             }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            kb16[i][e] = (__float_as_uint(v[2 * e]) >> 16) | (__float_as_uint(v[2 * e + 1]) & 0xFFFF0000u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const _Float16 h = (_Float16)v[e];
-            vh[e][i] = *reinterpret_cast<const uint16_t*>(&h);
-        }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = 4 * kq + i;
-        ktile[key * CPR + (co ^ (key & 15))] = make_uint4(kb16[i][0], kb16[i][1], kb16[i][2], kb16[i][3]);
-    }
+    for (int i = 0; i < 4; ++i)
+        ktile[(4 * kq + i) * KROW + co] = make_uint4(kh[i][0], kh[i][1], kh[i][2], kh[i][3]);
+    // V^T row d = 8co + e holds channel e of the 4 keys
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int d = 8 * co + e;
-        *reinterpret_cast<uint2*>(vtile + vt_off(d, kq)) =
-            make_uint2((uint32_t)vh[e][0] | ((uint32_t)vh[e][1] << 16), (uint32_t)vh[e][2] | ((uint32_t)vh[e][3] << 16));
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t x01 = __builtin_amdgcn_perm(kh[1][e >> 1], kh[0][e >> 1], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(kh[3][e >> 1], kh[2][e >> 1], sel);
+        *reinterpret_cast<uint2*>(vtile + vt_off(d, kq)) = make_uint2(x01, x23);
     }
 }
 
@@ -144,16 +219,17 @@ template <int D, bool QF32, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     constexpr int NBLK = D / 32;  // 32-channel blocks of the S MFMA
     constexpr int NDT = D / 16;   // 16-channel tiles of the O MFMA
-    constexpr int CPR = D / 8;    // 16-byte chunks per bf16 key row
+    constexpr int CPR = D / 8;    // 16-byte chunks per fp16 key row
     constexpr int NT = 64 * NW;
-    constexpr int ITEMS = 4 * CPR;                       // dequantisation items per chunk
-    constexpr int IPT = (ITEMS + NT - 1) / NT;           // items per thread
-    __shared__ uint4 ktile[CHUNK_KEYS * CPR];
+    constexpr int ITEMS = 4 * CPR;  // dequantisation items per chunk
+    using S = Stage<D>;
+    __shared__ uint4 ktile[CHUNK_KEYS * (CPR + 1)];
     __shared__ __attribute__((aligned(16))) uint8_t vtile[D * 32 + (D / 8) * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[RING * S::SLOT];
     __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t row = blockIdx.y;
     const int split = blockIdx.x;
@@ -161,10 +237,29 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     const int head = 16 * w + c16;
 
     const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
+    const int n_sp_chunks = p.Kp / CHUNK_KEYS;
     const int c_lo = split * p.cps;
     const int c_hi = min(nchunks, c_lo + p.cps);
     const int slot = p.Wp ? p.q_slot[row] : 0;
     const int wlo = max(0, slot - p.window + 1);
+
+    // ---- query loads first: they fly while the key rows are resolved
+    float qf[QF32 ? NBLK : 1][8];
+    uint4 qraw[QF32 ? 1 : NBLK];
+    if (QF32) {
+        const float* qr = static_cast<const float*>(p.q) + (row * p.H + head) * D;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+            const float4 a = *reinterpret_cast<const float4*>(qr + 32 * blk + 8 * g);
+            const float4 c = *reinterpret_cast<const float4*>(qr + 32 * blk + 8 * g + 4);
+            float* f = qf[QF32 ? blk : 0];
+            f[0] = a.x, f[1] = a.y, f[2] = a.z, f[3] = a.w, f[4] = c.x, f[5] = c.y, f[6] = c.z, f[7] = c.w;
+        }
+    } else {
+        const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.H + head) * D;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) qraw[QF32 ? 0 : blk] = *reinterpret_cast<const uint4*>(qr + 32 * blk + 8 * g);
+    }
 
     // ---- physical rows of every key of this split (-1: none)
     const int nk = max(0, c_hi - c_lo) * CHUNK_KEYS;
@@ -182,113 +277,151 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         }
         krow[i] = r;
     }
-
-    // ---- Q operand (B of S^T = K Q^T): Q[head][32*blk + 8g .. +8]
-    bf16x8 qhi[NBLK];
-    bf16x8 qlo[QF32 ? NBLK : 1];
-    if (QF32) {
-        const float* qr = static_cast<const float*>(p.q) + (row * p.H + head) * D;
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-            const float4 a = *reinterpret_cast<const float4*>(qr + 32 * blk + 8 * g);
-            const float4 c = *reinterpret_cast<const float4*>(qr + 32 * blk + 8 * g + 4);
-            const float xs[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-            uint16_t hi[8], lo[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t h = f32_to_bf16_rne(xs[i]);
-                hi[i] = (uint16_t)h;
-                lo[i] = (uint16_t)f32_to_bf16_rne(xs[i] - __uint_as_float(h << 16));
-            }
-            qhi[blk] = *reinterpret_cast<const bf16x8*>(hi);
-            qlo[QF32 ? blk : 0] = *reinterpret_cast<const bf16x8*>(lo);
-        }
-    } else {
-        const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.H + head) * D;
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk)
-            qhi[blk] = *reinterpret_cast<const bf16x8*>(qr + 32 * blk + 8 * g);
-    }
+    // the query and index loads are complete before the copies start (keeps the
+    // copy count the only thing on this wave's vmcnt)
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
     __syncthreads();
+
+    // ---- raw bytes of the first RING chunks start flowing into the LDS ring
+    const int c_pre = min(c_hi, c_lo + RING);
+    for (int ch = c_lo; ch < c_pre; ++ch)
+        stage_chunk<D, NW>(p, ch < n_sp_chunks, krow + (ch - c_lo) * CHUNK_KEYS, ring + ((ch - c_lo) % RING) * S::SLOT,
+                           w, lane);
+
+    // ---- Q operand (B of S^T = K Q^T): Q[head][32*blk + 8g .. +8] in fp16,
+    // pre-scaled by 2^-qs; an fp32 query is split into hi + lo fp16 parts
+    uint32_t qmax = 0;  // largest |q| as an fp32 bit pattern (monotone in |q|)
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+        if (QF32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qmax = max(qmax, __float_as_uint(qf[QF32 ? blk : 0][e]) & 0x7FFFFFFFu);
+        } else {
+            const uint4 u = qraw[QF32 ? 0 : blk];
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qmax = max(qmax, max((wv[e] << 16) & 0x7FFF0000u, wv[e] & 0x7FFF0000u));
+        }
+    }
+    qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 16));
+    qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32));
+    // 2^-qs maps the largest element into [2^14, 2^15)
+    const int qs = qmax == 0 ? 0 : min(113, max(-100, (int)(qmax >> 23) - 127 - 14));
+    const float qscale = __uint_as_float((uint32_t)(127 - qs) << 23);
+    const float zscale = p.scale_log2 * __uint_as_float((uint32_t)(127 + qs) << 23);
+    f16x8 qhi[NBLK];
+    f16x8 qlo[QF32 ? NBLK : 1];
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+        float x[8];
+        if (QF32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = qf[QF32 ? blk : 0][e] * qscale;
+        } else {
+            const uint4 u = qraw[QF32 ? 0 : blk];
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_lo(wv[e]) * qscale;
+                x[2 * e + 1] = bf16_hi(wv[e]) * qscale;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const _Float16 h = (_Float16)x[e];
+            qhi[blk][e] = h;
+            if (QF32) qlo[QF32 ? blk : 0][e] = (_Float16)(x[e] - (float)h);
+        }
+    }
 
     f32x4 oacc[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    RawItem raw[IPT];
-    if (c_lo < c_hi) {
-        const bool sp = c_lo * CHUNK_KEYS < p.Kp;
-#pragma unroll
-        for (int it = 0; it < IPT; ++it) {
-            const int item = it * NT + tid;
-            if (item < ITEMS) load_item<D>(p, sp, krow, item / CPR, item % CPR, raw[it]);
-        }
-    }
+    int c_issued = c_pre;  // chunks [c_lo, c_issued) have been issued
+    const int vb = vt_base(c16, g);
     for (int ch = c_lo; ch < c_hi; ++ch) {
-        const int kb = ch * CHUNK_KEYS;
-        const bool sparse = kb < p.Kp;
+        const bool sparse = ch < n_sp_chunks;
         const int64_t* kr = krow + (ch - c_lo) * CHUNK_KEYS;
-        // ---- dequantise the prefetched chunk into the LDS tiles
+        const uint8_t* st = ring + ((ch - c_lo) % RING) * S::SLOT;
+        // ---- the chunk's copies have landed (all of this wave's copies: the
+        // compiler cannot tell ring slots apart and would wait for them anyway)
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+        lds_barrier();  // every wave's copies have landed; the tiles are free
+        // ---- dequantise the staged chunk into the LDS tiles
+        if (sparse) {
 #pragma unroll
-        for (int it = 0; it < IPT; ++it) {
-            const int item = it * NT + tid;
-            if (item < ITEMS) store_item<D>(sparse, raw[it], item / CPR, item % CPR, ktile, vtile);
-        }
-        __syncthreads();
-        // ---- the next chunk's loads fly during this chunk's MFMAs
-        if (ch + 1 < c_hi) {
-            const bool sp = (ch + 1) * CHUNK_KEYS < p.Kp;
-#pragma unroll
-            for (int it = 0; it < IPT; ++it) {
+            for (int it = 0; it < (ITEMS + NT - 1) / NT; ++it) {
                 const int item = it * NT + tid;
-                if (item < ITEMS) load_item<D>(p, sp, kr + CHUNK_KEYS, item / CPR, item % CPR, raw[it]);
+                if (item < ITEMS) store_item<D, true>(st, item / CPR, item % CPR, ktile, vtile);
             }
+        } else {
+#pragma unroll
+            for (int it = 0; it < (ITEMS + NT - 1) / NT; ++it) {
+                const int item = it * NT + tid;
+                if (item < ITEMS) store_item<D, false>(st, item / CPR, item % CPR, ktile, vtile);
+            }
+        }
+        lds_barrier();
+        // ---- the ring slot is free again: refill it with chunk ch + RING
+        if (c_issued < c_hi) {
+            stage_chunk<D, NW>(p, c_issued < n_sp_chunks, krow + (c_issued - c_lo) * CHUNK_KEYS,
+                               ring + ((c_issued - c_lo) % RING) * S::SLOT, w, lane);
+            ++c_issued;
         }
         // ---- S^T[key][head] = sum_d K[key][d] Q[head][d]
         f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk) {
-            const uint4 a4 = ktile[c16 * CPR + ((4 * blk + g) ^ c16)];
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&a4);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[blk], s, 0, 0, 0);
-            if (QF32) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[QF32 ? blk : 0], s, 0, 0, 0);
+            const uint4 a4 = ktile[c16 * (CPR + 1) + 4 * blk + g];
+            const f16x8 a = *reinterpret_cast<const f16x8*>(&a4);
+            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[blk], s, 0, 0, 0);
+            if (QF32) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? blk : 0], s, 0, 0, 0);
         }
         // ---- online softmax for head `head` over keys 4g..4g+3 of this chunk
         float z[4];
         float mloc = -INFINITY;
+        int64_t kv4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kv4[i] = kr[4 * g + i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = (kr[4 * g + i] >= 0) ? s[i] * p.scale_log2 : -INFINITY;
+            z[i] = (kv4[i] >= 0) ? s[i] * zscale : -INFINITY;
             mloc = fmaxf(mloc, z[i]);
         }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+        // lazy maximum: move it only when this chunk exceeds it by more than 2^8
+        // (nothing to rescale while nothing has been accumulated)
+        float alpha = 1.0f;
+        if (mloc > m_run + 8.0f) {
+            if (l_run > 0.0f) alpha = exp2f(m_run - mloc);
+            m_run = mloc;
+        }
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        }
         float psum = 0.0f;
-        uint16_t ph[4];
+        f16x4 pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float pi = (z[i] == -INFINITY) ? 0.0f : exp2f(z[i] - m_new);
-            const _Float16 h = (_Float16)pi;
+            // z - m_run <= 8: the hardware exp2 needs no range reduction
+            const _Float16 h = (_Float16)((z[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_run));
             psum += (float)h;  // normalise by the weights the MFMA actually applies
-            ph[i] = *reinterpret_cast<const uint16_t*>(&h);
+            pb[i] = h;
         }
         psum += __shfl_xor(psum, 16);
         psum += __shfl_xor(psum, 32);
         l_run = l_run * alpha + psum;
-        m_run = m_new;
-        const f16x4 pb = *reinterpret_cast<const f16x4*>(ph);
-        // ---- O^T[d][head] = alpha * O^T + sum_key V^T[d][key] P^T[key][head]
+        // ---- O^T[d][head] += sum_key V^T[d][key] P^T[key][head]
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const uint2 a2 = *reinterpret_cast<const uint2*>(vtile + vt_off(16 * dt + c16, g));
+            const uint2 a2 = *reinterpret_cast<const uint2*>(vtile + vb + VT_DT * dt);
             const f16x4 a = *reinterpret_cast<const f16x4*>(&a2);
-            f32x4 acc = oacc[dt] * alpha;
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, acc, 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, oacc[dt], 0, 0, 0);
         }
-        __syncthreads();
     }
 
     // ---- normalised partial (o, lse) of this workgroup's key range
@@ -422,7 +555,8 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     if (K > 0) {
         CSA2_ARG(kv && kv->codes && kv->scales && idx, "%s: null cache view or idx", what);
         CSA2_ARG(kv->D == D, "%s: cache D=%d differs from D=%d", what, kv->D, D);
-        CSA2_ARG(aligned(kv->codes, 4), "%s: codes must be 4-byte aligned", what);
+        CSA2_ARG(aligned(kv->codes, 16) && aligned(kv->scales, 4),
+                 "%s: codes must be 16-byte and scales 4-byte aligned", what);
         csa2_status st = make_rowmap(kv->page_table, kv->page_size, kv->max_pages, kv->seq_stride, 1, &p.kvmap, what);
         if (st != CSA2_OK) return st;
         p.codes = kv->codes;

@@ -157,7 +157,11 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, int32_t k, c
  *   o    [B][Q][H][D] fp32 out, normalised over this key set
  *   lse  [B][Q][H]    fp32 out, natural-log sum of exp(sm_scale * q.k) (-inf if empty)
  * H % 16 == 0, H <= 64; D in {128, 256, 512}.  Workspace from
- * csa2_attn_workspace_size (may be 0). */
+ * csa2_attn_workspace_size (may be 0).  codes must be 16-byte and scales
+ * 4-byte aligned, and the cache must hold at least one row (row 0 is read, and
+ * ignored, in place of missing entries).  Errors: CSA2_EINVAL for null or
+ * misaligned pointers and out-of-range sizes, CSA2_EUNSUPPORTED for other H/D,
+ * CSA2_EWORKSPACE for a short workspace; nothing is enqueued on error. */
 size_t csa2_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t D);
 csa2_status csa2_sparse_attn_fp4(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H,
                                  const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, float sm_scale, float* o,
@@ -169,7 +173,9 @@ csa2_status csa2_sparse_attn_fp4(const void* q, csa2_dtype qt, int32_t B, int32_
  *   keys = rows max(0, slot-window+1) .. slot.
  *   merge == 0: write o/lse of this key set.  merge == 1: o/lse already hold a
  *   partial over a disjoint key set; combine both into one softmax (exact
- *   log-sum-exp merge) in place. */
+ *   log-sum-exp merge) in place.
+ * The window rows are converted to fp16 inside the kernel: values must satisfy
+ * |v| < 65504 (smaller than 2^-14 lose precision as fp16 subnormals). */
 csa2_status csa2_swa_attn(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                           const uint16_t* swa_kv, int32_t T, const int32_t* q_slot, int32_t window, float sm_scale,
                           int32_t merge, float* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
