@@ -259,3 +259,38 @@ def test_swa_only_short_window_and_empty_sparse():
         ref, lr = oracle.attention(q[b, 0].double().numpy(), None, None, None, swa[b].double().numpy(),
                                    int(slot[b, 0]), 128, sc)
         assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ref, lr, "swa-only")
+
+
+@pytest.mark.parametrize("qdtype,qlog_lo,qlog_hi,sc", [
+    (torch.bfloat16, -6.0, 1.5, None), (torch.float32, -6.0, 1.5, None),
+    (torch.bfloat16, 3.0, 6.0, 1e-6), (torch.float32, 3.0, 6.0, 1e-6)])
+def test_sparse_attn_extreme_magnitudes(qdtype, qlog_lo, qlog_hi, sc):
+    """Entry rows spanning 10^-2.5 .. 10^1 (many E4M3 scales subnormal) and query
+    heads spanning 10^qlog_lo .. 10^qlog_hi (scaled up or down by a power of two
+    before the fp16 products; a tiny logit scale keeps the large ones' logits
+    moderate): the fp16 datapath must stay within the tolerance."""
+    B, Q, H, D, n, K = 2, 1, 64, 512, 2000, 512
+    rmag = torch.pow(10.0, inputs.uniform((B * n, 1), "xm/rmag").double() * 3.5 - 2.5)
+    lat = (inputs.normal((B * n, D), "xm/lat").double() * rmag).float()
+    codes = torch.empty(B * n, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(B * n, D // 16, dtype=torch.uint8, device=DEV)
+    api.csa2_fp4_quantize(lat.to(DEV), codes, scales)
+    rc, rs = oracle.fp4_encode(lat.numpy())
+    assert np.any((rs > 0) & (rs < 8)), "no subnormal E4M3 scale in the sample"
+    cache = api.Fp4Cache(codes, scales, D, n)
+    qmag = torch.pow(10.0, inputs.uniform((B, Q, H, 1), "xm/qmag").double() * (qlog_hi - qlog_lo) + qlog_lo)
+    q = (inputs.normal((B, Q, H, D), "xm/q").double() * qmag).to(qdtype)
+    idx = inputs.small_ints((B, Q, K), "xm/idx", -1, n - 1, dtype=torch.int32)
+    sc = 1 / math.sqrt(D) if sc is None else sc
+    o = torch.empty(B, Q, H, D, device=DEV)
+    lse = torch.empty(B, Q, H, device=DEV)
+    ws = torch.empty(max(api.csa2_attn_workspace_size(B, Q, H, D), 16), dtype=torch.uint8, device=DEV)
+    case(f"sparse_attn extreme magnitudes q={qdtype}")
+    api.csa2_sparse_attn_fp4(q.to(DEV), cache, idx.to(DEV), sc, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    rc, rs = rc.reshape(B, n, -1), rs.reshape(B, n, -1)
+    worst = 0.0
+    for b in range(B):
+        ra, la = oracle.attention(q[b, 0].double().numpy(), rc[b], rs[b], idx[b, 0].numpy(), None, 0, 0, sc)
+        worst = max(worst, assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ra, la, "extreme"))
+    print(f"worst row-relative error {worst:.2e}")
