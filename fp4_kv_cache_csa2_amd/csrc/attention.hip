@@ -49,8 +49,11 @@ struct AttnParams {
     float* o;                  // [rows][H][D]
     float* lse;                // [rows][H]
     int32_t nsplit, cps;       // splits per row, chunks per split
-    float* part_o;             // [rows][nsplit][H][D]
-    float* part_lse;           // [rows][nsplit][H]
+    // split partials, unnormalised: o in MFMA lane order per 16-head group,
+    // [rows][nsplit][H/16][D/16][64 lanes][4]; running max (log2 domain) and sum
+    float* part_o;
+    float2* part_ml;           // [rows][nsplit][H]
+    float* lse_prev;           // [rows][H]: the output's lse before a merge
 };
 
 // E2M1 magnitude x 2^8 -> high byte of its fp16 value (the low byte is 0):
@@ -371,14 +374,22 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
             ++c_issued;
         }
         // ---- S^T[key][head] = sum_d K[key][d] Q[head][d]
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        // (two accumulator chains halve the dependent MFMA latency)
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
+        for (int blk = 0; blk < NBLK; blk += 2) {
             const uint4 a4 = ktile[c16 * (CPR + 1) + 4 * blk + g];
+            const uint4 b4 = ktile[c16 * (CPR + 1) + 4 * (blk + 1) + g];
             const f16x8 a = *reinterpret_cast<const f16x8*>(&a4);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[blk], s, 0, 0, 0);
-            if (QF32) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? blk : 0], s, 0, 0, 0);
+            const f16x8 bb = *reinterpret_cast<const f16x8*>(&b4);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[blk], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bb, qhi[blk + 1], s1, 0, 0, 0);
+            if (QF32) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? blk : 0], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bb, qlo[QF32 ? blk + 1 : 0], s1, 0, 0, 0);
+            }
         }
+        const f32x4 s = s0 + s1;
         // ---- online softmax for head `head` over keys 4g..4g+3 of this chunk
         float z[4];
         float mloc = -INFINITY;
@@ -424,18 +435,20 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         }
     }
 
-    // ---- normalised partial (o, lse) of this workgroup's key range
-    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-    const float lse_cur = (l_run > 0.0f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
     if (p.nsplit > 1) {
-        float* po = p.part_o + ((row * p.nsplit + split) * p.H + head) * D;
+        // ---- unnormalised partial of this key range, each lane's 4 x D/16
+        // accumulators stored contiguously (full 1 KB per wave instruction)
+        float* po = p.part_o + ((row * p.nsplit + split) * p.H + 16 * w) * D;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
-                make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
-        if (g == 0) p.part_lse[(row * p.nsplit + split) * p.H + head] = lse_cur;
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = oacc[dt];
+        if (g == 0) p.part_ml[(row * p.nsplit + split) * p.H + head] = make_float2(m_run, l_run);
+        // snapshot of the lse to merge with: the merge kernel overwrites it
+        if (p.merge && split == 0 && g == 0) p.lse_prev[row * p.H + head] = p.lse[row * p.H + head];
         return;
     }
+    // ---- normalised output (o, lse) of this key set
+    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    const float lse_cur = (l_run > 0.0f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
     float* orow = p.o + (row * p.H + head) * D;
     float w_cur = 1.0f, w_old = 0.0f, lse_out = lse_cur;
     if (p.merge) {
@@ -471,46 +484,57 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     if (g == 0) p.lse[row * p.H + head] = lse_out;
 }
 
-// Merge the split partials of one (row, head): exact log-sum-exp combination,
-// optionally together with the (o, lse) already in the output.  All loads are
+// Merge the split partials: exact log-sum-exp combination, optionally together
+// with the (o, lse) already in the output.  One workgroup = one row x one
+// 16-head group x 4 of its 16-column tiles; thread = one lane-order float4
+// (head 16 hg + lane % 16, columns 16 dt + 4 (lane / 16) .. +3).  Every load is
 // issued before any arithmetic.
 template <int NS>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_lse, int nsplit, int H, int D,
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float2* __restrict__ part_ml,
+                                                         const float* __restrict__ lse_prev, int nsplit, int H, int D,
                                                          int merge, float* __restrict__ o, float* __restrict__ lse) {
     const int64_t row = blockIdx.x;
-    const int h = blockIdx.y;
-    const int c = threadIdx.x * 4;
-    float ls[NS + 1];
-    float4 ov[NS + 1];
+    const int hg = blockIdx.y;
+    const int t = threadIdx.x, lane = t & 63;
+    const int dt = blockIdx.z * 4 + (t >> 6);
+    const int h = 16 * hg + (lane & 15);
+    const int c = 16 * dt + 4 * (lane >> 4);
+    float2 ml[NS];
+    f32x4 ov[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        ls[s] = s < nsplit ? part_lse[(row * nsplit + s) * H + h] : -INFINITY;
-        ov[s] = s < nsplit ? *reinterpret_cast<const float4*>(part_o + ((row * nsplit + s) * H + h) * D + c)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        ml[s] = s < nsplit ? part_ml[(row * nsplit + s) * H + h] : make_float2(-INFINITY, 0.0f);
+        ov[s] = s < nsplit ? *reinterpret_cast<const f32x4*>(part_o + ((row * nsplit + s) * H + 16 * hg) * D +
+                                                             (dt * 64 + lane) * 4)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    ls[NS] = merge ? lse[row * H + h] : -INFINITY;
-    ov[NS] = merge ? *reinterpret_cast<const float4*>(o + (row * H + h) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = -INFINITY;
+    float* op = o + (row * H + h) * D + c;
+    // the output's own partial: weight e^lse = 2^(lse log2 e), normalised o
+    const float lse_old = merge ? lse_prev[row * H + h] : -INFINITY;
+    const float4 o_old = merge ? *reinterpret_cast<const float4*>(op) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float m_old = lse_old * 1.4426950408889634f;
+    float M = m_old;
 #pragma unroll
-    for (int s = 0; s <= NS; ++s) L = fmaxf(L, ls[s]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float tot = 0.0f;
-    if (L != -INFINITY) {
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[s].x);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float den = 0.0f;
+    if (M != -INFINITY) {
 #pragma unroll
-        for (int s = 0; s <= NS; ++s) {
-            const float wv = (ls[s] == -INFINITY) ? 0.0f : expf(ls[s] - L);
-            acc.x += wv * ov[s].x;
-            acc.y += wv * ov[s].y;
-            acc.z += wv * ov[s].z;
-            acc.w += wv * ov[s].w;
-            tot += wv;
+        for (int s = 0; s < NS; ++s) {
+            const float wv = (ml[s].x == -INFINITY) ? 0.0f : exp2f(ml[s].x - M);
+            acc += wv * ov[s];
+            den += wv * ml[s].y;
         }
+        const float wo = (m_old == -INFINITY) ? 0.0f : exp2f(m_old - M);
+        acc += wo * f32x4{o_old.x, o_old.y, o_old.z, o_old.w};
+        den += wo;
     }
-    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    __syncthreads();  // every thread has read the old o/lse before any is overwritten
-    *reinterpret_cast<float4*>(o + (row * H + h) * D + c) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (threadIdx.x == 0) lse[row * H + h] = tot > 0.0f ? L + logf(tot) : -INFINITY;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    // (each thread rewrites only the o it read; the old lse comes from a snapshot)
+    *reinterpret_cast<float4*>(op) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    if (dt == 0 && (lane >> 4) == 0)
+        lse[row * H + h] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
 constexpr int MAX_SPLIT = 16;
@@ -529,7 +553,7 @@ size_t attn_ws_bytes(int64_t rows, int H, int D) {
     int64_t s = (512 + rows - 1) / rows;
     if (s > MAX_SPLIT) s = MAX_SPLIT;
     if (s <= 1) return 0;
-    return (size_t)(rows * s * H) * (size_t)(D + 1) * 4 + 256;
+    return (size_t)(rows * s * H) * (size_t)(D + 2) * 4 + (size_t)(rows * H) * 4 + 256;
 }
 
 }  // namespace
@@ -587,12 +611,13 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     CSA2_REQUIRE(p.cps <= MAX_CPS, CSA2_EUNSUPPORTED, "%s: %d keys per query need more than %d splits", what,
                  nchunks * CHUNK_KEYS, MAX_SPLIT);
     if (p.nsplit > 1) {
-        const size_t need = (size_t)(rows * p.nsplit * H) * (size_t)(D + 1) * 4;
+        const size_t need = (size_t)(rows * p.nsplit * H) * (size_t)(D + 2) * 4 + (size_t)(rows * H) * 4;
         CSA2_REQUIRE(ws != nullptr && ws_bytes >= need, CSA2_EWORKSPACE,
                      "%s: workspace of %zu bytes required, %zu given", what, need, ws ? ws_bytes : (size_t)0);
         CSA2_ARG(((uintptr_t)ws & 15) == 0, "%s: workspace must be 16-byte aligned", what);
         p.part_o = static_cast<float*>(ws);
-        p.part_lse = p.part_o + rows * p.nsplit * H * (int64_t)D;
+        p.part_ml = reinterpret_cast<float2*>(p.part_o + rows * p.nsplit * H * (int64_t)D);
+        p.lse_prev = reinterpret_cast<float*>(p.part_ml + rows * p.nsplit * H);
     }
     const dim3 grid((unsigned)p.nsplit, (unsigned)rows);
     const dim3 block((unsigned)(4 * H));
@@ -616,14 +641,16 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
 #undef CSA2_ATTN
 #undef CSA2_ATTN_NW
     if (p.nsplit > 1) {
-        const dim3 mg((unsigned)rows, (unsigned)H), mb((unsigned)(D / 4));
+        const dim3 mg((unsigned)rows, (unsigned)(H / 16), (unsigned)(D / 64)), mb(256);
         if (p.nsplit <= 4)
-            attn_merge_kernel<4><<<mg, mb, 0, stream>>>(p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o, lse);
+            attn_merge_kernel<4><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D, p.merge, o,
+                                                         lse);
         else if (p.nsplit <= 8)
-            attn_merge_kernel<8><<<mg, mb, 0, stream>>>(p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o, lse);
+            attn_merge_kernel<8><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D, p.merge, o,
+                                                         lse);
         else
-            attn_merge_kernel<MAX_SPLIT><<<mg, mb, 0, stream>>>(p.part_o, p.part_lse, p.nsplit, H, D, p.merge, o,
-                                                                lse);
+            attn_merge_kernel<MAX_SPLIT><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D,
+                                                                p.merge, o, lse);
     }
     return launch_status(what);
 }
