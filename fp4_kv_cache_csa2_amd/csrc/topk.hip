@@ -21,7 +21,8 @@
 //    sends positions above the threshold bin straight to the selection and
 //    positions inside it to a candidate list, then one workgroup per row that
 //    selects among the candidates (or, if the bin overflowed the candidate
-//    buffer, among the whole row) and sorts the result.
+//    buffer, among the whole row) and writes the result in position order by a
+//    counting sort on the positions' top bits.
 // Several independent selections (the Top-K entries and the pool blocks of a
 // Full layer) run in the same launches as separate segments.
 #include "internal.h"
@@ -181,50 +182,55 @@ __device__ void select_global_row(const float* s, int n, uint32_t need, uint64_t
     __syncthreads();
 }
 
-// Bitonic sort of sel[0..np) ascending (np a power of two <= TOPK_KMAX;
-// unused slots hold INT32_MAX).  Thread t owns elements t and t + 1024;
-// partner strides below 64 are lane shuffles, 64..512 go through LDS, 1024
-// stays inside the thread.
-__device__ void sort_sel(int* sel, int np) {
-    const int t = threadIdx.x;
-    const bool two = np > WG;
-    int a = sel[t], b = two ? sel[t + WG] : 0x7FFFFFFF;
-    __syncthreads();
-    for (int size = 2; size <= np; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride == WG) {  // pair (t, t + 1024), ascending
-                const int lo = min(a, b), hi = max(a, b);
-                a = lo;
-                b = hi;
-                continue;
-            }
-            const bool upper = (t & stride) != 0;
-            const bool up_a = ((t & size) == 0);
-            const bool up_b = (((t + WG) & size) == 0);
-            int pa, pb = 0;
-            if (stride < 64) {
-                pa = __shfl_xor(a, stride);
-                if (two) pb = __shfl_xor(b, stride);
-            } else {
-                sel[t] = a;
-                if (two) sel[t + WG] = b;
-                __syncthreads();
-                pa = sel[t ^ stride];
-                if (two) pb = sel[(t + WG) ^ stride];
-                __syncthreads();
-            }
-            a = (upper == up_a) ? max(a, pa) : min(a, pa);
-            if (two) b = (upper == up_b) ? max(b, pb) : min(b, pb);
-        }
-    }
-    sel[t] = a;
-    if (two) sel[t + WG] = b;
-    __syncthreads();
-}
-
 __device__ __forceinline__ int32_t map_pos(int p, const int32_t* pool, int64_t row, int nblk) {
     return pool ? pool[row * nblk + (p >> 3)] * 8 + (p & 7) : p;
 }
+
+// Write the distinct positions sel[0..total) (each < n) to out[0..total) in
+// ascending order, and -1 to out[total..k): a counting sort on the top 11 bits
+// of the position, then each position's rank among the few in its bin.
+__device__ void emit_sorted(const int* sel, int total, int n, int k, SelectLds& sh, int* tmp, int32_t* out,
+                            const int32_t* pool, int64_t row) {
+    const int t = threadIdx.x;
+    int bits = 0;
+    while (bits < 31 && (1 << bits) < n) ++bits;
+    const int shift = bits > 11 ? bits - 11 : 0;
+    uint32_t* cnt = sh.hist[0];
+    uint32_t* start = sh.hist[1];
+    for (int i = t; i < NBINS1; i += WG) cnt[i] = 0u;
+    __syncthreads();
+    int x[2];
+    uint32_t slot[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = t + j * WG;
+        x[j] = i < total ? sel[i] : 0;
+        slot[j] = i < total ? atomicAdd(&cnt[x[j] >> shift], 1u) : 0u;
+    }
+    __syncthreads();
+    const uint32_t c0 = cnt[2 * t], c1 = cnt[2 * t + 1];
+    uint32_t tot;
+    const uint32_t b0 = block_excl_scan(c0 + c1, sh, &tot);
+    start[2 * t] = b0;
+    start[2 * t + 1] = b0 + c0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (t + j * WG < total) tmp[start[x[j] >> shift] + slot[j]] = x[j];
+    __syncthreads();
+    const int nblk = n / 8;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (t + j * WG >= total) continue;
+        const uint32_t bn = (uint32_t)x[j] >> shift;
+        const uint32_t s0 = start[bn], c = cnt[bn];
+        uint32_t r = 0;
+        for (uint32_t q = 0; q < c; ++q) r += tmp[s0 + q] < x[j];
+        out[row * (int64_t)k + s0 + r] = map_pos(x[j], pool, row, nblk);
+    }
+    for (int i = total + t; i < k; i += WG) out[row * (int64_t)k + i] = -1;
+}
+
 
 // ---------------------------------------------------------------------------
 // Small path.
@@ -441,25 +447,46 @@ __global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
                 for (int j = 0; j < 4; ++j) v[4 * e + j] = (i + j < hi) ? s[i + j] : -INFINITY;
             }
         }
+        // classify, then one packed LDS atomic per wave reserves the slots
+        // (selected count in the low half, candidates in the high half: each
+        // is at most CCHUNK = 16384 per workgroup)
+        uint32_t kk[16];
+        uint32_t fsel = 0, fcand = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const uint32_t kk = key32(v[e]);
-            if (kk == 0u) continue;
-            const uint32_t dig = kk >> 21;
+            kk[e] = key32(v[e]);
+            const uint32_t dig = kk[e] >> 21;
+            const bool ok = kk[e] != 0u;
+            fsel |= (uint32_t)(ok && (all || dig > d)) << e;
+            fcand |= (uint32_t)(ok && !all && dig == d) << e;
+        }
+        const uint32_t mine = (uint32_t)__popc(fsel) | ((uint32_t)__popc(fcand) << 16);
+        uint32_t incl = mine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off);
+            if ((t & 63) >= off) incl += y;
+        }
+        uint32_t wbase = 0;
+        if ((t & 63) == 63) wbase = atomicAdd(&sh[2], incl);
+        wbase = __shfl(wbase, 63);
+        uint32_t at_s = (wbase & 0xFFFFu) + ((incl - mine) & 0xFFFFu);
+        uint32_t at_c = (wbase >> 16) + ((incl - mine) >> 16);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
             const int i = base + ((e >> 2) * PWG + t) * 4 + (e & 3);
-            if (all || dig > d) {
-                l_sel[atomicAdd(&sh[2], 1u)] = i;
-            } else if (dig == d) {
-                const uint32_t a = atomicAdd(&sh[3], 1u);
-                if (a < (uint32_t)LCAP) {
-                    l_ck[a] = kk;
-                    l_cp[a] = (uint32_t)i;
+            if ((fsel >> e) & 1u) l_sel[at_s++] = i;
+            if ((fcand >> e) & 1u) {
+                if (at_c < (uint32_t)LCAP) {
+                    l_ck[at_c] = kk[e];
+                    l_cp[at_c] = (uint32_t)i;
                 }
+                ++at_c;
             }
         }
     }
     __syncthreads();
-    const uint32_t ns = sh[2], nc = sh[3];
+    const uint32_t ns = sh[2] & 0xFFFFu, nc = sh[2] >> 16;
     if (t == 0) {
         sh[4] = ns ? atomicAdd(&sg.state[row].n_sel, ns) : 0u;
         // a local overflow pushes the row's count past the capacity: the finish
@@ -484,6 +511,7 @@ constexpr int E_CAND = TOPK_CAP / WG;  // candidates per thread in the finish ke
 __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
     __shared__ SelectLds sh;
     __shared__ int sel[TOPK_KMAX];
+    __shared__ int tmp[TOPK_KMAX];
     const int sgi = blockIdx.x / segs.rows;
     const int64_t row = blockIdx.x % segs.rows;
     const TopkSeg& sg = segs.seg[sgi];
@@ -517,12 +545,7 @@ __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
         }
     }
     const uint32_t total = all ? st.valid : (uint32_t)sg.k;
-    int np = 64;
-    while (np < (int)total) np <<= 1;
-    sort_sel(sel, np);
-    const int nblk = sg.n / 8;
-    for (int i = t; i < sg.k; i += WG)
-        sg.out[row * (int64_t)sg.k + i] = (uint32_t)i < total ? map_pos(sel[i], sg.pool, row, nblk) : -1;
+    emit_sorted(sel, (int)total, sg.n, sg.k, sh, tmp, sg.out, sg.pool, row);
 }
 
 }  // namespace
