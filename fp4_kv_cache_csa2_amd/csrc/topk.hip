@@ -38,6 +38,8 @@ constexpr int CHUNK = 4096;     // positions per workgroup in the histogram pass
 constexpr int CCHUNK = 16384;   // positions per workgroup in the split pass (64 per thread): few workgroups
                                 // per row keep the two per-row list counters lightly contended
 constexpr int LCAP = 4096;      // candidates a split workgroup can hold in LDS
+constexpr int CWG = 1024;       // threads of the split pass: 16 positions each, four waves per SIMD to
+                                // hide the latency of its short dependent chains
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
     return ((uint64_t)key << 32) | (uint64_t)(~pos);
@@ -242,9 +244,13 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
                                                         int32_t* __restrict__ out, uint32_t* __restrict__ hist,
                                                         TopkRowState* __restrict__ state) {
     __shared__ SelectLds sh;
+    __shared__ int32_t pool_s[TOPK_SMALL_N / 8];  // the row's pool blocks (position -> entry map)
     const int t = threadIdx.x;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * (int64_t)n;
+    const int nblk = n / 8;
+    if (pool)
+        for (int i = t; i < nblk; i += WG) pool_s[i] = pool[row * nblk + i];
     uint32_t key[E_SMALL], pos[E_SMALL];
     uint32_t cnt = 0;
     // thread t owns positions 16t..16t+15 (ordered output); read them as four
@@ -308,12 +314,11 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     for (int e = 0; e < E_SMALL; ++e)
         mine += key[e] != 0u && (all || (composite(key[e], pos[e]) & mask) >= prefix);
     uint32_t total;
-    uint32_t at = block_excl_scan(mine, sh, &total);
-    const int nblk = n / 8;
+    uint32_t at = block_excl_scan(mine, sh, &total);  // (its barriers also publish pool_s)
 #pragma unroll
     for (int e = 0; e < E_SMALL; ++e)
         if (key[e] != 0u && (all || (composite(key[e], pos[e]) & mask) >= prefix))
-            out[row * (int64_t)k + at++] = map_pos((int)pos[e], pool, row, nblk);
+            out[row * (int64_t)k + at++] = pool ? pool_s[pos[e] >> 3] * 8 + (int)(pos[e] & 7u) : (int)pos[e];
     for (int i = (int)total + t; i < k; i += WG) out[row * (int64_t)k + i] = -1;
 }
 
@@ -363,14 +368,15 @@ __global__ __launch_bounds__(PWG) void topk_hist_kernel(TopkSegs segs) {
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Threshold bin of a row from its global histogram (PWG threads, 8 bins
-// each): the histogram is read with coalesced loads into LDS first.
+// Threshold bin of a row from its global histogram (NT threads, NBINS1 / NT
+// bins each): the histogram is read with coalesced loads into LDS first.
+template <int NT>
 __device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* lh, uint32_t* scan, uint32_t* d_out,
                               uint32_t* above_out) {
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    constexpr int per = NBINS1 / PWG;
+    constexpr int per = NBINS1 / NT;
 #pragma unroll
-    for (int i = 0; i < per; ++i) lh[i * PWG + t] = gh[i * PWG + t];
+    for (int i = 0; i < per; ++i) lh[i * NT + t] = gh[i * NT + t];
     __syncthreads();
     uint32_t mine[per];
     uint32_t local = 0;
@@ -404,8 +410,8 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* lh, u
 // Threshold split of one chunk.  Positions above the threshold bin go to the
 // row's selection list, positions inside it to the candidate list; both are
 // gathered in LDS first, so each list costs one global atomic per workgroup.
-__global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
-    __shared__ uint32_t scan[PWG / 64];
+__global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
+    __shared__ uint32_t scan[CWG / 64];
     __shared__ uint32_t sh[6];
     __shared__ int l_sel[TOPK_KMAX];
     __shared__ uint32_t l_ck[LCAP], l_cp[LCAP];
@@ -418,35 +424,44 @@ __global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
     const int lo = blockIdx.x * CCHUNK;
     const int hi = min(sg.n, lo + CCHUNK);
     const float* s = sg.scores + row * (int64_t)sg.n;
+    const bool vec = (sg.n & 3) == 0 && (((uintptr_t)s) & 15) == 0;
+    // every position of this thread is loaded before any is classified: one
+    // memory round trip, overlapping the threshold search; round rd covers
+    // positions lo + rd*CWG*16 + (e*CWG + t)*4 + j
+    constexpr int ROUNDS = CCHUNK / (CWG * 16);
+    float va[ROUNDS][16];
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int base = lo + rd * CWG * 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = base + (e * CWG + t) * 4;  // 4 consecutive positions
+            if (vec && i + 3 < hi) {
+                const float4 f = *reinterpret_cast<const float4*>(s + i);
+                va[rd][4 * e] = f.x;
+                va[rd][4 * e + 1] = f.y;
+                va[rd][4 * e + 2] = f.z;
+                va[rd][4 * e + 3] = f.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) va[rd][4 * e + j] = (i + j < hi) ? s[i + j] : -INFINITY;
+            }
+        }
+    }
     if (t < 2) sh[2 + t] = 0u;
     const uint32_t valid = sg.state[row].valid;
     const bool all = valid <= (uint32_t)sg.k;
     uint32_t d = 0;
     if (!all) {
-        row_threshold(sg.hist + row * NBINS1, (uint32_t)sg.k, lh, scan, &sh[0], &sh[1]);
+        row_threshold<CWG>(sg.hist + row * NBINS1, (uint32_t)sg.k, lh, scan, &sh[0], &sh[1]);
         d = sh[0];
         if (blockIdx.x == 0 && t == 0) sg.state[row].digit = d;
     }
     __syncthreads();  // sh[2..3] initialised; lh free for candidates
-    const bool vec = (sg.n & 3) == 0 && (((uintptr_t)s) & 15) == 0;
-    // 4 rounds of 16 positions per thread: position lo + (r*PWG + t)*4*4 ...
-    for (int rd = 0; rd < CCHUNK / (PWG * 16); ++rd) {
-        float v[16];
-        const int base = lo + rd * PWG * 16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = base + (e * PWG + t) * 4;  // 4 consecutive positions
-            if (vec && i + 3 < hi) {
-                const float4 f = *reinterpret_cast<const float4*>(s + i);
-                v[4 * e] = f.x;
-                v[4 * e + 1] = f.y;
-                v[4 * e + 2] = f.z;
-                v[4 * e + 3] = f.w;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[4 * e + j] = (i + j < hi) ? s[i + j] : -INFINITY;
-            }
-        }
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+        const float* v = va[rd];
+        const int base = lo + rd * CWG * 16;
         // classify, then one packed LDS atomic per wave reserves the slots
         // (selected count in the low half, candidates in the high half: each
         // is at most CCHUNK = 16384 per workgroup)
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
         uint32_t at_c = (wbase >> 16) + ((incl - mine) >> 16);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int i = base + ((e >> 2) * PWG + t) * 4 + (e & 3);
+            const int i = base + ((e >> 2) * CWG + t) * 4 + (e & 3);
             if ((fsel >> e) & 1u) l_sel[at_s++] = i;
             if ((fcand >> e) & 1u) {
                 if (at_c < (uint32_t)LCAP) {
@@ -496,11 +511,11 @@ __global__ __launch_bounds__(PWG) void topk_compact_kernel(TopkSegs segs) {
     }
     __syncthreads();
     int* sel = sg.sel + row * TOPK_KMAX + sh[4];
-    for (uint32_t j = t; j < ns; j += PWG) sel[j] = l_sel[j];
+    for (uint32_t j = t; j < ns; j += CWG) sel[j] = l_sel[j];
     const uint32_t cb = sh[5];
     uint32_t* ck = sg.ckey + row * TOPK_CAP;
     uint32_t* cp = sg.cpos + row * TOPK_CAP;
-    for (uint32_t j = t; j < nc && j < (uint32_t)LCAP && cb + j < (uint32_t)TOPK_CAP; j += PWG) {
+    for (uint32_t j = t; j < nc && j < (uint32_t)LCAP && cb + j < (uint32_t)TOPK_CAP; j += CWG) {
         ck[cb + j] = l_ck[j];
         cp[cb + j] = l_cp[j];
     }
@@ -581,7 +596,7 @@ void topk_launch_hist(const TopkSegs& segs, hipStream_t stream) {
 void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
     int chunks = 0;
     for (int i = 0; i < segs.nseg; ++i) chunks = max(chunks, (segs.seg[i].n + CCHUNK - 1) / CCHUNK);
-    topk_compact_kernel<<<dim3((unsigned)chunks, (unsigned)(segs.rows * segs.nseg)), PWG, 0, stream>>>(segs);
+    topk_compact_kernel<<<dim3((unsigned)chunks, (unsigned)(segs.rows * segs.nseg)), CWG, 0, stream>>>(segs);
     topk_finish_kernel<<<(unsigned)(segs.rows * segs.nseg), WG, 0, stream>>>(segs);
 }
 
