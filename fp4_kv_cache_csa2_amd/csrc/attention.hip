@@ -487,9 +487,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 // Merge the split partials: exact log-sum-exp combination, optionally together
 // with the (o, lse) already in the output.  One workgroup = one row x one
 // 16-head group x 4 of its 16-column tiles; thread = one lane-order float4
-// (head 16 hg + lane % 16, columns 16 dt + 4 (lane / 16) .. +3).  Every load is
-// issued before any arithmetic.
-template <int NS>
+// (head 16 hg + lane % 16, columns 16 dt + 4 (lane / 16) .. +3).  Splits are
+// taken NB at a time (all loads of a batch issued before any arithmetic) with
+// a running maximum across batches.
+template <int NB>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          const float* __restrict__ lse_prev, int nsplit, int H, int D,
@@ -500,35 +501,41 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     const int dt = blockIdx.z * 4 + (t >> 6);
     const int h = 16 * hg + (lane & 15);
     const int c = 16 * dt + 4 * (lane >> 4);
-    float2 ml[NS];
-    f32x4 ov[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        ml[s] = s < nsplit ? part_ml[(row * nsplit + s) * H + h] : make_float2(-INFINITY, 0.0f);
-        ov[s] = s < nsplit ? *reinterpret_cast<const f32x4*>(part_o + ((row * nsplit + s) * H + 16 * hg) * D +
-                                                             (dt * 64 + lane) * 4)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     float* op = o + (row * H + h) * D + c;
     // the output's own partial: weight e^lse = 2^(lse log2 e), normalised o
     const float lse_old = merge ? lse_prev[row * H + h] : -INFINITY;
     const float4 o_old = merge ? *reinterpret_cast<const float4*>(op) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float m_old = lse_old * 1.4426950408889634f;
-    float M = m_old;
+    float M = lse_old * 1.4426950408889634f;
+    f32x4 acc = f32x4{o_old.x, o_old.y, o_old.z, o_old.w};
+    float den = M == -INFINITY ? 0.0f : 1.0f;
+    if (M == -INFINITY) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += NB) {
+        float2 ml[NB];
+        f32x4 ov[NB];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[s].x);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    float den = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const float wv = (ml[s].x == -INFINITY) ? 0.0f : exp2f(ml[s].x - M);
-            acc += wv * ov[s];
-            den += wv * ml[s].y;
+        for (int j = 0; j < NB; ++j) {
+            const int s = s0 + j;
+            ml[j] = s < nsplit ? part_ml[(row * nsplit + s) * H + h] : make_float2(-INFINITY, 0.0f);
+            ov[j] = s < nsplit ? *reinterpret_cast<const f32x4*>(part_o + ((row * nsplit + s) * H + 16 * hg) * D +
+                                                                 (dt * 64 + lane) * 4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        const float wo = (m_old == -INFINITY) ? 0.0f : exp2f(m_old - M);
-        acc += wo * f32x4{o_old.x, o_old.y, o_old.z, o_old.w};
-        den += wo;
+        float Mb = M;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) Mb = fmaxf(Mb, ml[j].x);
+        if (Mb == -INFINITY) continue;
+        if (Mb != M) {
+            const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mb);
+            acc *= r;
+            den *= r;
+            M = Mb;
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const float wv = (ml[j].x == -INFINITY) ? 0.0f : exp2f(ml[j].x - M);
+            acc += wv * ov[j];
+            den += wv * ml[j].y;
+        }
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     // (each thread rewrites only the o it read; the old lse comes from a snapshot)
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
         lse[row * H + h] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
-constexpr int MAX_SPLIT = 16;
+constexpr int MAX_SPLIT = 64;
 
 int choose_nsplit(int64_t rows, int nchunks) {
     if (nchunks <= 1) return 1;
@@ -649,7 +656,7 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
             attn_merge_kernel<8><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D, p.merge, o,
                                                          lse);
         else
-            attn_merge_kernel<MAX_SPLIT><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D,
+            attn_merge_kernel<16><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D,
                                                                 p.merge, o, lse);
     }
     return launch_status(what);
