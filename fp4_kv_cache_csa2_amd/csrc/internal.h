@@ -55,10 +55,9 @@ void topk_launch_zero(const TopkSegs& segs, hipStream_t stream);
 void topk_launch_hist(const TopkSegs& segs, hipStream_t stream);
 // threshold split + candidate select + sorted output
 void topk_launch_select(const TopkSegs& segs, hipStream_t stream);
-// one workgroup per row (n <= TOPK_SMALL_N); hist/state: the first-digit
-// histogram built by the scoring kernel (or NULL), zeroed again after use
+// one workgroup per row (n <= TOPK_SMALL_N)
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
-                       hipStream_t stream, uint32_t* hist = nullptr, TopkRowState* state = nullptr);
+                       hipStream_t stream);
 
 // Zero up to 6 ranges of 32-bit words in one launch.
 struct ZeroRanges {

@@ -13,9 +13,10 @@
 //
 // Two paths:
 //  * n <= 16384 (Reindex pools, short contexts): one 1024-thread workgroup per
-//    row holds 16 consecutive keys per thread in registers, runs every pass
-//    with an LDS histogram, and writes the selection in position order with
-//    one block-wide prefix sum (no sort).
+//    row holds 16 consecutive keys per thread in registers, narrows the
+//    selection to the keys above a sampled lower bound, runs the passes with
+//    an LDS histogram over those, and writes the selection in position order
+//    with one block-wide prefix sum (no sort).
 //  * larger n: a per-row 2048-bin histogram of the top 11 key bits (fused into
 //    the Full-mode scan, or built by its own pass), then a grid-wide pass that
 //    sends positions above the threshold bin straight to the selection and
@@ -236,23 +237,37 @@ __device__ void emit_sorted(const int* sel, int total, int n, int k, SelectLds& 
 
 // ---------------------------------------------------------------------------
 // Small path.
-// With hist != NULL the row's first-digit histogram and valid count were
-// built by the scoring kernel: the first pass is read, not recomputed, and
-// the histogram and state are zeroed again for the next use.
+//
+// A lower bound T on the k-th largest key first limits the selection to few
+// candidates: every thread's largest key m_t is one of its elements, so if at
+// least ceil(k/16) threads of each of the 16 waves have m_t >= T, at least k
+// elements are >= T.  T = the smallest over the waves of the wave's
+// ceil(k/16)-th largest m_t (found bit by bit with ballots).  Elements with
+// key >= T are appended to LDS (one atomic per wave) and the radix select runs
+// over them alone, which avoids the contended 16-per-thread histogram of the
+// whole row; the result is identical because every selected element is >= T.
+// If T cannot be formed (k > 1024) or the candidates overflow, the select runs
+// over all elements.
+constexpr int SCAP = 4096;                  // candidates held in LDS
+constexpr int E_SC = SCAP / WG;             // candidates per thread in the select (4)
+
 __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict__ scores, int n, int k,
                                                         const int32_t* __restrict__ pool,
-                                                        int32_t* __restrict__ out, uint32_t* __restrict__ hist,
-                                                        TopkRowState* __restrict__ state) {
+                                                        int32_t* __restrict__ out) {
     __shared__ SelectLds sh;
     __shared__ int32_t pool_s[TOPK_SMALL_N / 8];  // the row's pool blocks (position -> entry map)
-    const int t = threadIdx.x;
+    __shared__ uint32_t c_key[SCAP], c_pos[SCAP];
+    __shared__ uint32_t wave_t[NW];
+    __shared__ uint32_t counts;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * (int64_t)n;
     const int nblk = n / 8;
     if (pool)
         for (int i = t; i < nblk; i += WG) pool_s[i] = pool[row * nblk + i];
-    uint32_t key[E_SMALL], pos[E_SMALL];
-    uint32_t cnt = 0;
+    for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
+    if (t == 0) counts = 0u;
+    uint32_t key[E_SMALL];
     // thread t owns positions 16t..16t+15 (ordered output); read them as four
     // 16-byte loads when the row is 16-byte aligned (strided scalar loads
     // thrash the vector cache and cost several microseconds here)
@@ -273,52 +288,97 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
             key[e] = i < n ? key32(s[i]) : 0u;
         }
     }
+    // ---- the bound T
+    const int c = (k + NW - 1) / NW;
+    uint32_t T = 0u;
+    if (c <= 64) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int e = 0; e < E_SMALL; ++e) m = max(m, key[e]);
+        uint32_t v = 0u;  // largest V with #{lanes: m >= V} >= c
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = v | (1u << bit);
+            if (__popcll(__ballot(m >= cand)) >= (uint32_t)c) v = cand;
+        }
+        if (lane == 0) wave_t[wid] = v;
+    }
+    __syncthreads();  // also publishes pool_s, the zeroed hist and counts
+    if (c <= 64) {
+        T = wave_t[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) T = min(T, wave_t[w]);
+    }
+    // ---- count valid keys and append the candidates (key >= T) to LDS:
+    // valid count in the low half, candidates in the high half (each <= 16384)
+    uint32_t fc = 0;
+    uint32_t nv = 0;
 #pragma unroll
     for (int e = 0; e < E_SMALL; ++e) {
-        pos[e] = (uint32_t)(t * E_SMALL + e);
-        cnt += key[e] != 0u;
+        nv += key[e] != 0u;
+        fc |= (uint32_t)(key[e] != 0u && key[e] >= T) << e;
     }
-    uint64_t prefix = 0, mask = 0;
-    uint32_t valid;
-    if (hist != nullptr) {
-        uint32_t* hr = hist + row * NBINS1;
-        for (int i = t; i < NBINS1; i += WG) {
-            sh.hist[0][i] = hr[i];
-            hr[i] = 0u;
-            sh.hist[1][i] = 0u;  // select_regs starts at pass 1 with buffer 1
-        }
-        if (t == 0) {
-            sh.total = state[row].valid;
-            state[row] = TopkRowState{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();
-        valid = sh.total;
-        if (valid > (uint32_t)k) {
-            find_bin(sh.hist[0], sh, NBINS1, (uint32_t)k);
-            const uint32_t d = sh.bin;
-            const uint32_t need = (uint32_t)k - sh.above;
-            prefix = (uint64_t)d << 53;
-            mask = (uint64_t)0x7FF << 53;
-            const bool done = sh.hist[0][d] == need;
-            __syncthreads();
-            if (!done) select_regs<E_SMALL>(key, pos, need, 1, prefix, mask, sh);
-        }
-    } else {
-        for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
-        block_excl_scan(cnt, sh, &valid);  // its barriers also order the zeroing
-        if (valid > (uint32_t)k) select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
+    const uint32_t mine = nv | ((uint32_t)__popc(fc) << 16);
+    uint32_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
     }
+    uint32_t wbase = 0u;
+    if (lane == 63) wbase = atomicAdd(&counts, incl);
+    wbase = __shfl(wbase, 63);
+    uint32_t at = (wbase >> 16) + ((incl - mine) >> 16);
+#pragma unroll
+    for (int e = 0; e < E_SMALL; ++e) {
+        if ((fc >> e) & 1u) {
+            if (at < (uint32_t)SCAP) {
+                c_key[at] = key[e];
+                c_pos[at] = (uint32_t)(t * E_SMALL + e);
+            }
+            ++at;
+        }
+    }
+    __syncthreads();
+    const uint32_t valid = counts & 0xFFFFu, ncand = counts >> 16;
     const bool all = valid <= (uint32_t)k;
-    uint32_t mine = 0;
+    const bool use_cand = !all && ncand <= (uint32_t)SCAP;
+    uint64_t prefix = 0, mask = 0;
+    if (!all) {
+        if (use_cand) {
+            uint32_t ck[E_SC], cp[E_SC];
 #pragma unroll
-    for (int e = 0; e < E_SMALL; ++e)
-        mine += key[e] != 0u && (all || (composite(key[e], pos[e]) & mask) >= prefix);
+            for (int e = 0; e < E_SC; ++e) {
+                const int i = e * WG + t;
+                ck[e] = i < (int)ncand ? c_key[i] : 0u;
+                cp[e] = i < (int)ncand ? c_pos[i] : 0u;
+            }
+            select_regs<E_SC>(ck, cp, (uint32_t)k, 0, prefix, mask, sh);
+        } else {
+            uint32_t pos[E_SMALL];
+#pragma unroll
+            for (int e = 0; e < E_SMALL; ++e) pos[e] = (uint32_t)(t * E_SMALL + e);
+            select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
+        }
+    }
+    // ---- selected: valid, (a candidate when the select ran over candidates),
+    // and above the radix boundary; written in position order
+    const uint32_t Tsel = use_cand ? T : 0u;
+    uint32_t fs = 0;
+#pragma unroll
+    for (int e = 0; e < E_SMALL; ++e) {
+        const bool ok = key[e] != 0u && key[e] >= Tsel &&
+                        (all || (composite(key[e], (uint32_t)(t * E_SMALL + e)) & mask) >= prefix);
+        fs |= (uint32_t)ok << e;
+    }
     uint32_t total;
-    uint32_t at = block_excl_scan(mine, sh, &total);  // (its barriers also publish pool_s)
+    uint32_t o = block_excl_scan((uint32_t)__popc(fs), sh, &total);
 #pragma unroll
-    for (int e = 0; e < E_SMALL; ++e)
-        if (key[e] != 0u && (all || (composite(key[e], pos[e]) & mask) >= prefix))
-            out[row * (int64_t)k + at++] = pool ? pool_s[pos[e] >> 3] * 8 + (int)(pos[e] & 7u) : (int)pos[e];
+    for (int e = 0; e < E_SMALL; ++e) {
+        if ((fs >> e) & 1u) {
+            const int p = t * E_SMALL + e;
+            out[row * (int64_t)k + o++] = pool ? pool_s[p >> 3] * 8 + (p & 7) : p;
+        }
+    }
     for (int i = (int)total + t; i < k; i += WG) out[row * (int64_t)k + i] = -1;
 }
 
@@ -601,8 +661,8 @@ void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
 }
 
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
-                       hipStream_t stream, uint32_t* hist, TopkRowState* state) {
-    topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool, out, hist, state);
+                       hipStream_t stream) {
+    topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool, out);
 }
 
 __global__ void zero_ranges_kernel(ZeroRanges z) {
