@@ -104,12 +104,12 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
         TopkSeg* sb = nullptr;
         if (e_large) {
             se = &segs.seg[segs.nseg++];
-            *se = TopkSeg{scores, n, a->K, nullptr, st->idx};
+            *se = TopkSeg{scores, n, a->K, nullptr, st->idx, a->n_vis, 1};
             topk_carve(tk, rows, se);
         }
         if (b_large) {
             sb = &segs.seg[segs.nseg++];
-            *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool};
+            *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool, a->n_vis, 8};
             topk_carve(static_cast<char*>(tk) + topk_large_ws_bytes(rows), rows, sb);
         }
         ZeroRanges z{};
@@ -120,13 +120,15 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
         }
         launch_zero_ranges(z, stream);
+        // scores past a row's n_vis are neither written nor read
         s = index_full_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, n, scores,
                             a->build_pool ? block_max : nullptr, se ? se->hist : nullptr, se ? se->state : nullptr,
-                            sb ? sb->hist : nullptr, sb ? sb->state : nullptr, stream);
+                            sb ? sb->hist : nullptr, sb ? sb->state : nullptr, true, stream);
         if (s != CSA2_OK) return s;
         if (segs.nseg) topk_launch_select(segs, stream);
-        if (!e_large) topk_launch_small(scores, rows32, n, a->K, nullptr, st->idx, stream);
-        if (a->build_pool && !b_large) topk_launch_small(block_max, rows32, nb, a->P, nullptr, st->pool, stream);
+        if (!e_large) topk_launch_small(scores, rows32, n, a->K, nullptr, st->idx, stream, a->n_vis, 1);
+        if (a->build_pool && !b_large)
+            topk_launch_small(block_max, rows32, nb, a->P, nullptr, st->pool, stream, a->n_vis, 8);
         s = launch_status("layer_forward");
     } else if (mode == CSA2_REINDEX) {
         // (the pool scores' first-digit histogram is built inside the select:

@@ -37,6 +37,8 @@ struct IndexParams {
     float* scores;             // [rows][n_pos]
     float* block_max;          // [rows][ceil(n_pos/8)] or null (Full)
     int64_t blocks_per_row;    // ceil(n_pos / 64)
+    int32_t skip_invisible;    // Full: blocks past n_vis are not written at all (their
+                               // readers bound each row by n_vis); else they get -inf
     // optional first-digit histograms for the Top-K that follows (Full only)
     uint32_t* hist_e;          // [rows][NBINS1] of the entry scores
     TopkRowState* state_e;
@@ -136,10 +138,12 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     uint4* my = tile[w];
     uint32_t n_valid = 0, n_valid_b = 0;  // lane counts for the histograms
 
-    uint32_t row_next = (CONTIG || blk >= p.blocks_per_row) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
+    // Full mode: only blocks holding a visible entry are read
+    const int64_t nbv = REINDEX ? p.blocks_per_row : (min(nv, p.n_pos) + EPB - 1) / EPB;
+    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
     uint4 v[CH];
-    if (blk < p.blocks_per_row) load_block<DI, REINDEX, CONTIG>(p, r, b, nv, blk, lane, row_next, v);
-    for (; blk < p.blocks_per_row; blk += stride) {
+    if (blk < nbv) load_block<DI, REINDEX, CONTIG>(p, r, b, nv, blk, lane, row_next, v);
+    for (; blk < nbv; blk += stride) {
         const int64_t pos = blk * EPB + lane;
         const bool valid = CONTIG ? (pos < nv && pos < p.n_pos) : (row_next != NOROW);
         // An opaque zero, fresh every block: LDS addresses are recomputed each
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
         wave_sync();
         // next block's loads fly while this one is scored
         const int64_t nxt = blk + stride;
-        if (nxt < p.blocks_per_row) {
+        if (nxt < nbv) {
             if (!CONTIG) row_next = entry_row<REINDEX>(p, r, b, nv, nxt * EPB + lane);
             load_block<DI, REINDEX, CONTIG>(p, r, b, nv, nxt, lane, row_next, v);
         }
@@ -204,6 +208,15 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
             }
         }
     }
+    // blocks without a visible entry: -inf, unless the readers skip them
+    if (!REINDEX && !p.skip_invisible) {
+        for (; blk < p.blocks_per_row; blk += stride) {
+            const int64_t pos = blk * EPB + lane;
+            if (pos < p.n_pos) p.scores[(int64_t)r * p.n_pos + pos] = -INFINITY;
+            if (p.block_max != nullptr && (lane & 7) == 0 && (pos >> 3) < nblocks8)
+                p.block_max[(int64_t)r * nblocks8 + (pos >> 3)] = -INFINITY;
+        }
+    }
     if (hist) {
         // valid counts: one atomic per wave; bins: only the non-empty ones
         for (int off = 32; off > 0; off >>= 1) {
@@ -240,10 +253,13 @@ csa2_status check_common(const char* what, const uint16_t* q_idx, int32_t B, int
 csa2_status launch_index(IndexParams& p, int rows, int D_i, bool reindex, hipStream_t stream, const char* what) {
     p.blocks_per_row = (p.n_pos + EPB - 1) / EPB;
     if (p.blocks_per_row == 0 || rows == 0) return CSA2_OK;
-    // about two resident workgroups per CU on 256 CUs; every wave loops over its blocks
+    // at least about two resident workgroups per CU on 256 CUs in total, and at
+    // most 32 blocks per wave, so that the longest rows of a ragged batch are
+    // spread over enough CUs (workgroups past a short row's end exit at once)
     int64_t gx = (p.blocks_per_row + WAVES - 1) / WAVES;
     const int64_t target = 512;
-    if (gx * rows > target) gx = (target + rows - 1) / rows;
+    const int64_t per_wave_cap = (p.blocks_per_row + WAVES * 32 - 1) / (WAVES * 32);
+    if (gx * rows > target) gx = max((target + rows - 1) / rows, per_wave_cap);
     // with histograms, a workgroup may score at most 65535 positions (16-bit bins)
     const int64_t min_gx = (p.blocks_per_row + (65535 / (WAVES * EPB)) * WAVES - 1) / ((65535 / (WAVES * EPB)) * WAVES);
     if (gx < min_gx) gx = min_gx;
@@ -274,7 +290,7 @@ using namespace csa2;
 csa2_status csa2::index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
                                   const int32_t* n_vis, int32_t n_max, float* scores, float* block_max,
                                   uint32_t* hist_e, TopkRowState* st_e, uint32_t* hist_b, TopkRowState* st_b,
-                                  hipStream_t stream) {
+                                  bool skip_invisible, hipStream_t stream) {
     CSA2_ARG(n_max >= 0, "index_full: n_max=%d < 0", n_max);
     RowMap map;
     csa2_status st = check_common("index_full", q_idx, B, Q, H_i, k, n_vis, n_max, &map);
@@ -294,6 +310,7 @@ csa2_status csa2::index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, i
     p.state_e = st_e;
     p.hist_b = block_max ? hist_b : nullptr;
     p.state_b = st_b;
+    p.skip_invisible = skip_invisible ? 1 : 0;
     return launch_index(p, B * Q, k->D_i, false, stream, "index_full");
 }
 
@@ -302,7 +319,7 @@ extern "C" csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t
                                        float* block_max, hipStream_t stream) {
     clear_error();
     return index_full_hist(q_idx, B, Q, H_i, k, n_vis, n_max, scores, block_max, nullptr, nullptr, nullptr, nullptr,
-                           stream);
+                           false, stream);
 }
 
 csa2_status csa2::index_reindex_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,

@@ -34,6 +34,8 @@ struct TopkSeg {
     int32_t n, k;
     const int32_t* pool;   // NULL or [rows][n/8] position -> entry map
     int32_t* out;          // [rows][k]
+    const int32_t* lim;    // NULL, or [rows]: positions >= ceil(lim[row] / lim_div) are invalid and unread
+    int32_t lim_div;
     uint32_t* hist;        // [rows][NBINS1]
     TopkRowState* state;   // [rows]
     int* sel;              // [rows][TOPK_KMAX]
@@ -55,9 +57,9 @@ void topk_launch_zero(const TopkSegs& segs, hipStream_t stream);
 void topk_launch_hist(const TopkSegs& segs, hipStream_t stream);
 // threshold split + candidate select + sorted output
 void topk_launch_select(const TopkSegs& segs, hipStream_t stream);
-// one workgroup per row (n <= TOPK_SMALL_N)
+// one workgroup per row (n <= TOPK_SMALL_N); lim as in TopkSeg
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
-                       hipStream_t stream);
+                       hipStream_t stream, const int32_t* lim = nullptr, int lim_div = 1);
 
 // Zero up to 6 ranges of 32-bit words in one launch.
 struct ZeroRanges {
@@ -77,7 +79,8 @@ csa2_status index_reindex_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int3
 // entry scores (hist_e/st_e) and of the block maxima (hist_b/st_b; may be NULL).
 csa2_status index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
                             const int32_t* n_vis, int32_t n_max, float* scores, float* block_max, uint32_t* hist_e,
-                            TopkRowState* st_e, uint32_t* hist_b, TopkRowState* st_b, hipStream_t stream);
+                            TopkRowState* st_e, uint32_t* hist_b, TopkRowState* st_b, bool skip_invisible,
+                            hipStream_t stream);
 
 csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                         const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,

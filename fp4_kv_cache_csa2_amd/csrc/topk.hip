@@ -185,6 +185,13 @@ __device__ void select_global_row(const float* s, int n, uint32_t need, uint64_t
     __syncthreads();
 }
 
+// positions of a row that may hold a valid score
+__device__ __forceinline__ int row_limit(const TopkSeg& sg, int64_t row) {
+    if (sg.lim == nullptr) return sg.n;
+    const int64_t l = ((int64_t)max(sg.lim[row], 0) + sg.lim_div - 1) / sg.lim_div;
+    return (int)min((int64_t)sg.n, l);
+}
+
 __device__ __forceinline__ int32_t map_pos(int p, const int32_t* pool, int64_t row, int nblk) {
     return pool ? pool[row * nblk + (p >> 3)] * 8 + (p & 7) : p;
 }
@@ -253,7 +260,8 @@ constexpr int E_SC = SCAP / WG;             // candidates per thread in the sele
 
 __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict__ scores, int n, int k,
                                                         const int32_t* __restrict__ pool,
-                                                        int32_t* __restrict__ out) {
+                                                        int32_t* __restrict__ out, const int32_t* __restrict__ lim,
+                                                        int lim_div) {
     __shared__ SelectLds sh;
     __shared__ int32_t pool_s[TOPK_SMALL_N / 8];  // the row's pool blocks (position -> entry map)
     __shared__ uint32_t c_key[SCAP], c_pos[SCAP];
@@ -263,6 +271,8 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     const int64_t row = blockIdx.x;
     const float* s = scores + row * (int64_t)n;
     const int nblk = n / 8;
+    // positions at or past nl are invalid and never read
+    const int nl = lim ? (int)min((int64_t)n, ((int64_t)max(lim[row], 0) + lim_div - 1) / lim_div) : n;
     if (pool)
         for (int i = t; i < nblk; i += WG) pool_s[i] = pool[row * nblk + i];
     for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     // thread t owns positions 16t..16t+15 (ordered output); read them as four
     // 16-byte loads when the row is 16-byte aligned (strided scalar loads
     // thrash the vector cache and cost several microseconds here)
-    if ((n & 3) == 0 && (((uintptr_t)s) & 15) == 0 && (t + 1) * E_SMALL <= n) {
+    if ((n & 3) == 0 && (((uintptr_t)s) & 15) == 0 && (t + 1) * E_SMALL <= nl) {
         const float4* s4 = reinterpret_cast<const float4*>(s) + t * (E_SMALL / 4);
 #pragma unroll
         for (int e = 0; e < E_SMALL / 4; ++e) {
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
 #pragma unroll
         for (int e = 0; e < E_SMALL; ++e) {
             const int i = t * E_SMALL + e;
-            key[e] = i < n ? key32(s[i]) : 0u;
+            key[e] = i < nl ? key32(s[i]) : 0u;
         }
     }
     // ---- the bound T
@@ -479,12 +489,13 @@ __global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
     const int sgi = blockIdx.y / segs.rows;
     const int64_t row = blockIdx.y % segs.rows;
     const TopkSeg& sg = segs.seg[sgi];
-    if ((int)blockIdx.x * CCHUNK >= sg.n) return;
+    const int lim = row_limit(sg, row);
+    if ((int)blockIdx.x * CCHUNK >= lim) return;
     const int t = threadIdx.x;
     const int lo = blockIdx.x * CCHUNK;
-    const int hi = min(sg.n, lo + CCHUNK);
+    const int hi = min(lim, lo + CCHUNK);
     const float* s = sg.scores + row * (int64_t)sg.n;
-    const bool vec = (sg.n & 3) == 0 && (((uintptr_t)s) & 15) == 0;
+    const bool vec = (sg.n & 3) == 0 && (((uintptr_t)s) & 15) == 0;  // (i + 3 < hi is checked per load)
     // every position of this thread is loaded before any is classified: one
     // memory round trip, overlapping the threshold search; round rd covers
     // positions lo + rd*CWG*16 + (e*CWG + t)*4 + j
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
                     sel[atomicAdd(&sh.nsel, 1u)] = (int)pos[e];
             __syncthreads();
         } else {
-            select_global_row(sg.scores + row * (int64_t)sg.n, sg.n, need, prefix, mask, sh, sel);
+            select_global_row(sg.scores + row * (int64_t)sg.n, row_limit(sg, row), need, prefix, mask, sh, sel);
         }
     }
     const uint32_t total = all ? st.valid : (uint32_t)sg.k;
@@ -661,8 +672,8 @@ void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
 }
 
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
-                       hipStream_t stream) {
-    topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool, out);
+                       hipStream_t stream, const int32_t* lim, int lim_div) {
+    topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
 }
 
 __global__ void zero_ranges_kernel(ZeroRanges z) {
