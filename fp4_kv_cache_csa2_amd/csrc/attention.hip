@@ -548,7 +548,9 @@ constexpr int MAX_SPLIT = 64;
 
 int choose_nsplit(int64_t rows, int nchunks) {
     if (nchunks <= 1) return 1;
-    int64_t want = (512 + rows - 1) / rows;  // aim at >= 512 workgroups
+    // one resident workgroup per CU (its LDS ring holds one): about 256
+    // workgroups run in a single round, more only add rounds and partials
+    int64_t want = (256 + rows - 1) / rows;
     int64_t by_chunks = (nchunks + 1) / 2;   // at least two chunks per split
     int64_t s = want < by_chunks ? want : by_chunks;
     if (s > MAX_SPLIT) s = MAX_SPLIT;
@@ -557,7 +559,7 @@ int choose_nsplit(int64_t rows, int nchunks) {
 }
 
 size_t attn_ws_bytes(int64_t rows, int H, int D) {
-    int64_t s = (512 + rows - 1) / rows;
+    int64_t s = (256 + rows - 1) / rows;
     if (s > MAX_SPLIT) s = MAX_SPLIT;
     if (s <= 1) return 0;
     return (size_t)(rows * s * H) * (size_t)(D + 2) * 4 + (size_t)(rows * H) * 4 + 256;
