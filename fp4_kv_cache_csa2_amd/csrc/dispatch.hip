@@ -120,11 +120,16 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
         }
         launch_zero_ranges(z, stream);
-        // scores past a row's n_vis are neither written nor read
+        // scores past a row's n_vis are neither written nor read.  Several query
+        // rows per sequence: the scan shares each K block among them and the
+        // first-digit histograms come from their own pass
+        const bool multi = a->Q >= 2;
         s = index_full_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, n, scores,
-                            a->build_pool ? block_max : nullptr, se ? se->hist : nullptr, se ? se->state : nullptr,
-                            sb ? sb->hist : nullptr, sb ? sb->state : nullptr, true, stream);
+                            a->build_pool ? block_max : nullptr, se && !multi ? se->hist : nullptr,
+                            se && !multi ? se->state : nullptr, sb && !multi ? sb->hist : nullptr,
+                            sb && !multi ? sb->state : nullptr, true, stream);
         if (s != CSA2_OK) return s;
+        if (segs.nseg && multi) topk_launch_hist(segs, stream);
         if (segs.nseg) topk_launch_select(segs, stream);
         if (!e_large) topk_launch_small(scores, rows32, n, a->K, nullptr, st->idx, stream, a->n_vis, 1);
         if (a->build_pool && !b_large)

@@ -250,6 +250,122 @@ csa2_status check_common(const char* what, const uint16_t* q_idx, int32_t B, int
     return make_rowmap(k->page_table, k->page_size, k->max_pages, k->seq_stride, n_entries, map, what);
 }
 
+// Full-mode scoring of RB query rows of one sequence per workgroup (several
+// query tokens of a sequence: multi-token decode, prefill).  Every K block is
+// read from memory once for the RB rows; each lane runs RB independent FMA
+// chains over its entry, each in the same channel order as the single-row
+// kernel, so the scores are identical bit for bit.  No fused histograms.
+template <int DI, bool CONTIG, int RB>
+__global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams p) {
+    constexpr int CH = DI / 8;
+    __shared__ uint4 tile[WAVES][EPB * CH];
+    __shared__ float4 qbar_s[RB][DI / 4];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
+    const int gps = (p.Q + RB - 1) / RB;  // row groups per sequence
+    const int b = blockIdx.y / gps;
+    const int q0 = (blockIdx.y % gps) * RB;
+    const int nr = min(RB, p.Q - q0);
+    const int r0 = b * p.Q + q0;
+
+    for (int i = t; i < RB * DI; i += WAVES * 64) {
+        const int rr = i / DI, c = i % DI;
+        float acc = 0.0f;
+        if (rr < nr) {
+            const uint16_t* qr = p.q_idx + (int64_t)(r0 + rr) * p.H_i * DI + c;
+            for (int h = 0; h < p.H_i; ++h) acc = acc + __uint_as_float((uint32_t)qr[(int64_t)h * DI] << 16);
+        }
+        reinterpret_cast<float*>(qbar_s[rr])[c] = acc;
+    }
+    int64_t nvr[RB];
+    int64_t nvmax = 0;
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+        nvr[rr] = rr < nr ? min((int64_t)p.n_vis[r0 + rr], p.kmap.capacity) : 0;
+        nvmax = max(nvmax, nvr[rr]);
+    }
+    __syncthreads();
+
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+    int64_t blk = (int64_t)blockIdx.x * WAVES + w;
+    const int64_t nblocks8 = (p.n_pos + 7) / 8;
+    const int64_t nbv = (min(nvmax, p.n_pos) + EPB - 1) / EPB;
+    uint4* my = tile[w];
+    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<false>(p, r0, b, nvmax, blk * EPB + lane);
+    uint4 v[CH];
+    if (blk < nbv) load_block<DI, false, CONTIG>(p, r0, b, nvmax, blk, lane, row_next, v);
+    for (; blk < nbv; blk += stride) {
+        const int64_t pos = blk * EPB + lane;
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const int lz = lane + z;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int L = i * 64 + lz;
+            const int e = L / CH, c = L % CH;
+            my[e * CH + (c ^ (e & (CH - 1)))] = v[i];
+        }
+        wave_sync();
+        const int64_t nxt = blk + stride;
+        if (nxt < nbv) {
+            if (!CONTIG) row_next = entry_row<false>(p, r0, b, nvmax, nxt * EPB + lane);
+            load_block<DI, false, CONTIG>(p, r0, b, nvmax, nxt, lane, row_next, v);
+        }
+        const uint4* mine = my + lz * CH;
+        const int sw = lz & (CH - 1);
+        float acc[RB];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.0f;
+        // (not fully unrolled: the query broadcasts of a few channels at a time
+        // stay in registers, not all RB x DI of them)
+#pragma unroll 2
+        for (int c = 0; c < CH; ++c) {
+            const uint4 k4 = mine[c ^ sw];
+            const float kf[8] = {bf16_lo(k4.x), bf16_hi(k4.x), bf16_lo(k4.y), bf16_hi(k4.y),
+                                 bf16_lo(k4.z), bf16_hi(k4.z), bf16_lo(k4.w), bf16_hi(k4.w)};
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const float4 qa = qbar_s[rr][2 * c + z], qb = qbar_s[rr][2 * c + 1 + z];  // broadcasts
+                acc[rr] = fmaf(qa.x, kf[0], acc[rr]);
+                acc[rr] = fmaf(qa.y, kf[1], acc[rr]);
+                acc[rr] = fmaf(qa.z, kf[2], acc[rr]);
+                acc[rr] = fmaf(qa.w, kf[3], acc[rr]);
+                acc[rr] = fmaf(qb.x, kf[4], acc[rr]);
+                acc[rr] = fmaf(qb.y, kf[5], acc[rr]);
+                acc[rr] = fmaf(qb.z, kf[6], acc[rr]);
+                acc[rr] = fmaf(qb.w, kf[7], acc[rr]);
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+            if (rr >= nr) break;
+            const int64_t r = r0 + rr;
+            const float s = (pos < nvr[rr] && pos < p.n_pos) ? acc[rr] : -INFINITY;
+            if (pos < p.n_pos) p.scores[r * p.n_pos + pos] = s;
+            if (p.block_max != nullptr) {
+                float m = s;
+                m = fmaxf(m, __shfl_xor(m, 1));
+                m = fmaxf(m, __shfl_xor(m, 2));
+                m = fmaxf(m, __shfl_xor(m, 4));
+                if ((lane & 7) == 0 && (pos >> 3) < nblocks8) p.block_max[r * nblocks8 + (pos >> 3)] = m;
+            }
+        }
+    }
+    if (!p.skip_invisible) {
+        for (; blk < p.blocks_per_row; blk += stride) {
+            const int64_t pos = blk * EPB + lane;
+            for (int rr = 0; rr < nr; ++rr) {
+                const int64_t r = r0 + rr;
+                if (pos < p.n_pos) p.scores[r * p.n_pos + pos] = -INFINITY;
+                if (p.block_max != nullptr && (lane & 7) == 0 && (pos >> 3) < nblocks8)
+                    p.block_max[r * nblocks8 + (pos >> 3)] = -INFINITY;
+            }
+        }
+    }
+}
+
 csa2_status launch_index(IndexParams& p, int rows, int D_i, bool reindex, hipStream_t stream, const char* what) {
     p.blocks_per_row = (p.n_pos + EPB - 1) / EPB;
     if (p.blocks_per_row == 0 || rows == 0) return CSA2_OK;
@@ -264,9 +380,29 @@ csa2_status launch_index(IndexParams& p, int rows, int D_i, bool reindex, hipStr
     const int64_t min_gx = (p.blocks_per_row + (65535 / (WAVES * EPB)) * WAVES - 1) / ((65535 / (WAVES * EPB)) * WAVES);
     if (gx < min_gx) gx = min_gx;
     if (gx < 1) gx = 1;
-    const dim3 grid((unsigned)gx, (unsigned)rows);
     const dim3 block(WAVES * 64);
     const bool contig = !reindex && p.kmap.page_table == nullptr;
+    if (!reindex && p.hist_e == nullptr && p.Q >= 2) {
+        // RB rows of a sequence per workgroup
+        const int rb = p.Q >= 8 ? 8 : (p.Q >= 4 ? 4 : 2);
+        const int groups = (rows / p.Q) * ((p.Q + rb - 1) / rb);
+        int64_t gm = (p.blocks_per_row + WAVES - 1) / WAVES;
+        if (gm * groups > target) gm = max((target + groups - 1) / groups, per_wave_cap);
+        if (gm < 1) gm = 1;
+        const dim3 grid_m((unsigned)gm, (unsigned)groups);
+#define CSA2_IDXM(DD, RBV)                                                                 \
+    if (D_i == DD && rb == RBV) {                                                          \
+        if (contig)                                                                        \
+            index_multi_kernel<DD, true, RBV><<<grid_m, block, 0, stream>>>(p);            \
+        else                                                                               \
+            index_multi_kernel<DD, false, RBV><<<grid_m, block, 0, stream>>>(p);           \
+    }
+        CSA2_IDXM(128, 8) CSA2_IDXM(128, 4) CSA2_IDXM(128, 2)
+        CSA2_IDXM(64, 8) CSA2_IDXM(64, 4) CSA2_IDXM(64, 2)
+#undef CSA2_IDXM
+        return launch_status(what);
+    }
+    const dim3 grid((unsigned)gx, (unsigned)rows);
 #define CSA2_IDX(DD)                                                                   \
     if (D_i == DD) {                                                                   \
         if (reindex)                                                                   \

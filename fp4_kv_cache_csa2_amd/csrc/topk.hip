@@ -408,13 +408,14 @@ __global__ __launch_bounds__(PWG) void topk_hist_kernel(TopkSegs segs) {
     const int sgi = blockIdx.y / segs.rows;
     const int64_t row = blockIdx.y % segs.rows;
     const TopkSeg& sg = segs.seg[sgi];
-    if ((int)blockIdx.x * CHUNK >= sg.n) return;
+    const int lim = row_limit(sg, row);
+    if ((int)blockIdx.x * CHUNK >= lim) return;
     const int t = threadIdx.x;
     for (int i = t; i < NBINS1; i += PWG) h[i] = 0u;
     __syncthreads();
     const float* s = sg.scores + row * (int64_t)sg.n;
     const int lo = blockIdx.x * CHUNK;
-    const int hi = min(sg.n, lo + CHUNK);
+    const int hi = min(lim, lo + CHUNK);
     uint32_t cnt = 0;
     float v[CHUNK / PWG];
 #pragma unroll

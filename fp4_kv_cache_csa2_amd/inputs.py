@@ -126,6 +126,10 @@ WORKLOADS = {
     # 20-layer decoder pattern.
     "ragged_paged_b64": Workload("ragged_paged_b64", B=64, Q=1, N=1 << 20, D=512, H=64, H_i=8, D_i=128,
                                  pattern="FUUU" + "RUUU" * 4, ragged=True),
+    # Multi-token decode (e.g. verifying 4 drafted tokens): the hierarchical
+    # decode shape with 4 causal query tokens per sequence.
+    "multi_decode_b4_q4_n1m": Workload("multi_decode_b4_q4_n1m", B=4, Q=4, N=1 << 20, D=512, H=64, H_i=8,
+                                       D_i=128, pattern="FRRR"),
 }
 
 

@@ -108,6 +108,31 @@ def test_index_full_bit_exact(D_i, H_i, paged):
             np.testing.assert_array_equal(bm[b * Q + qq], oracle.block_max(ref))
 
 
+@pytest.mark.parametrize("Q,paged", [(2, False), (5, True), (8, False), (11, False), (11, True)])
+def test_index_full_multi_row_bit_exact(Q, paged):
+    """Several query rows per sequence share each K block (rows grouped 2/4/8,
+    partial last groups, per-row visibility); scores must equal the oracle's
+    row by row."""
+    B, n_max, D_i, H_i = 2, 20000, 128, 8
+    K, kview = _k_view(B, n_max, D_i, f"imK{Q}{paged}", paged)
+    q = inputs.normal((B, Q, H_i, D_i), f"imq{Q}", dtype=torch.bfloat16)
+    n_vis = inputs.small_ints((B, Q), f"imn{Q}", 0, n_max, dtype=torch.int32).numpy()
+    n_vis[0, 0] = n_max
+    scores = torch.empty(B * Q, n_max, device=DEV)
+    nb = (n_max + 7) // 8
+    bmax = torch.empty(B * Q, nb, device=DEV)
+    case(f"index_full multi-row Q={Q} paged={paged}")
+    api.csa2_index_full(q.to(DEV), kview, torch.from_numpy(n_vis).to(DEV), n_max, scores, bmax)
+    torch.cuda.synchronize()
+    s, bm = to_np(scores), to_np(bmax)
+    for b in range(B):
+        Kb = inputs.bf16_bits(K[b])
+        for qq in range(Q):
+            ref = oracle.index_scores(inputs.bf16_bits(q[b, qq]), Kb, n_vis[b, qq])
+            np.testing.assert_array_equal(s[b * Q + qq], ref)
+            np.testing.assert_array_equal(bm[b * Q + qq], oracle.block_max(ref))
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_index_reindex_bit_exact(paged):
     B, n_max, D_i, H_i, P = 2, 40000, 128, 8, 700

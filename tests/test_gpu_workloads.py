@@ -113,3 +113,11 @@ def test_encoder_prefill_q2k_n32k():
     inst = workload.make_instance(inputs.WORKLOADS["encoder_prefill_q2k_n32k"])
     rows = [0, 1, 2, 100, 1023, 1024, 2046, 2047]
     check_instance(inst, rows, rows[::2], heads=slice(0, 64, 8))
+
+
+def test_multi_decode_b4_q4_n1m():
+    # 4 causal query tokens per sequence: the scan shares K blocks among a
+    # sequence's rows, the pool and Top-K histograms come from their own pass
+    inst = workload.make_instance(inputs.WORKLOADS["multi_decode_b4_q4_n1m"])
+    assert list(inst.n_vis_host[0]) == [inst.n_max - 3, inst.n_max - 2, inst.n_max - 1, inst.n_max]
+    check_instance(inst, range(16), [0, 7, 13], heads=slice(0, 64, 8))
