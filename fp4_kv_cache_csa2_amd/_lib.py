@@ -39,7 +39,7 @@ class LayerArgs(ctypes.Structure):
 
 
 class GroupState(ctypes.Structure):
-    _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32)]
+    _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32), ("ws_clean", i32)]
 
 
 # name -> (restype, argtypes); every symbol declared in include/csa2.h

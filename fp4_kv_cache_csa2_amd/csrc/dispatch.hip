@@ -92,6 +92,7 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     void* aw = ws + w.attn;
     const int rows32 = (int)rows;
     csa2_status s = CSA2_OK;
+    bool topk_ws_used = false;
     if (mode == CSA2_FULL) {
         // Top-K entries and pool blocks: large selections share the zero /
         // split / finish launches; their first-digit histograms come out of the scan
@@ -112,14 +113,19 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool, a->n_vis, 8};
             topk_carve(static_cast<char*>(tk) + topk_large_ws_bytes(rows), rows, sb);
         }
-        ZeroRanges z{};
-        for (int i = 0; i < segs.nseg; ++i) {
-            z.ptr[z.n] = segs.seg[i].hist;
-            z.count[z.n++] = rows * NBINS1;
-            z.ptr[z.n] = reinterpret_cast<uint32_t*>(segs.seg[i].state);
-            z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
+        // the histograms and row states must start at zero: cleared here once
+        // per workspace, then left cleared by the finish pass of every call
+        topk_ws_used = segs.nseg > 0;
+        if (!st->ws_clean && segs.nseg) {
+            ZeroRanges z{};
+            for (int i = 0; i < segs.nseg; ++i) {
+                z.ptr[z.n] = segs.seg[i].hist;
+                z.count[z.n++] = rows * NBINS1;
+                z.ptr[z.n] = reinterpret_cast<uint32_t*>(segs.seg[i].state);
+                z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
+            }
+            launch_zero_ranges(z, stream);
         }
-        launch_zero_ranges(z, stream);
         // scores past a row's n_vis are neither written nor read.  Several query
         // rows per sequence: the scan shares each K block among them and the
         // first-digit histograms come from their own pass
@@ -145,8 +151,12 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             s = launch_status("layer_forward");
         }
     }
-    if (s != CSA2_OK) return s;
+    if (s != CSA2_OK) {
+        st->ws_clean = 0;
+        return s;
+    }
     if (mode == CSA2_FULL) {
+        if (topk_ws_used) st->ws_clean = 1;
         st->has_idx = 1;
         if (a->build_pool) st->has_pool = 1;
     } else if (mode == CSA2_REINDEX) {

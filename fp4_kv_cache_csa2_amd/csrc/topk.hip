@@ -633,6 +633,9 @@ __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
     }
     const uint32_t total = all ? st.valid : (uint32_t)sg.k;
     emit_sorted(sel, (int)total, sg.n, sg.k, sh, tmp, sg.out, sg.pool, row);
+    // leave the row's histogram and state cleared for the next selection
+    for (int i = t; i < NBINS1; i += WG) sg.hist[row * NBINS1 + i] = 0u;
+    if (t == 0) sg.state[row] = TopkRowState{0u, 0u, 0u, 0u};
 }
 
 }  // namespace

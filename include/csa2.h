@@ -218,6 +218,10 @@ typedef struct csa2_group_state {
     int32_t* pool;           /* [B*Q][P] device: pool blocks of the last pool-building FULL */
     int32_t has_idx;         /* host flags, maintained by csa2_layer_forward */
     int32_t has_pool;
+    int32_t ws_clean;        /* host flag: 0 for a fresh (or foreign) workspace.  A FULL layer
+                                clears the workspace's Top-K counters once and sets 1; every
+                                later call leaves them cleared again, so the same workspace must
+                                then stay with this state.  Reset to 0 after an error status. */
 } csa2_group_state;
 
 size_t csa2_layer_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t n_max, int32_t K, int32_t P);

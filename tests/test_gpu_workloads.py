@@ -120,4 +120,12 @@ def test_multi_decode_b4_q4_n1m():
     # sequence's rows, the pool and Top-K histograms come from their own pass
     inst = workload.make_instance(inputs.WORKLOADS["multi_decode_b4_q4_n1m"])
     assert list(inst.n_vis_host[0]) == [inst.n_max - 3, inst.n_max - 2, inst.n_max - 1, inst.n_max]
-    check_instance(inst, range(16), [0, 7, 13], heads=slice(0, 64, 8))
+    run = check_instance(inst, range(16), [0, 7, 13], heads=slice(0, 64, 8))
+    # a second step on the same workspace (its Top-K counters left cleared by the
+    # first, not zeroed again) reproduces every index and output
+    first = [t.clone() for t in run.o] + [t.clone() for t in run.idx]
+    case("multi_decode_b4_q4_n1m: second step")
+    run.step(keep_indices=True)
+    torch.cuda.synchronize()
+    for a, b in zip(first, list(run.o) + list(run.idx)):
+        assert torch.equal(a, b)
