@@ -374,22 +374,28 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
             ++c_issued;
         }
         // ---- S^T[key][head] = sum_d K[key][d] Q[head][d]
-        // (two accumulator chains halve the dependent MFMA latency)
-        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        // four accumulator chains (a dependent MFMA waits for three others);
+        // the operands of the next four blocks are read while these multiply
+        f32x4 sacc[4];
 #pragma unroll
-        for (int blk = 0; blk < NBLK; blk += 2) {
-            const uint4 a4 = ktile[c16 * (CPR + 1) + 4 * blk + g];
-            const uint4 b4 = ktile[c16 * (CPR + 1) + 4 * (blk + 1) + g];
-            const f16x8 a = *reinterpret_cast<const f16x8*>(&a4);
-            const f16x8 bb = *reinterpret_cast<const f16x8*>(&b4);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[blk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bb, qhi[blk + 1], s1, 0, 0, 0);
-            if (QF32) {
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? blk : 0], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bb, qlo[QF32 ? blk + 1 : 0], s1, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 kop[2][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kop[0][j] = ktile[c16 * (CPR + 1) + 4 * j + g];
+#pragma unroll
+        for (int grp = 0; grp < NBLK / 4; ++grp) {
+            if (grp + 1 < NBLK / 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kop[(grp + 1) & 1][j] = ktile[c16 * (CPR + 1) + 4 * (4 * (grp + 1) + j) + g];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f16x8 a = *reinterpret_cast<const f16x8*>(&kop[grp & 1][j]);
+                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[4 * grp + j], sacc[j], 0, 0, 0);
+                if (QF32) sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? 4 * grp + j : 0], sacc[j], 0, 0, 0);
             }
         }
-        const f32x4 s = s0 + s1;
+        const f32x4 s = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
         // ---- online softmax for head `head` over keys 4g..4g+3 of this chunk
         float z[4];
         float mloc = -INFINITY;
@@ -427,11 +433,23 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         psum += __shfl_xor(psum, 32);
         l_run = l_run * alpha + psum;
         // ---- O^T[d][head] += sum_key V^T[d][key] P^T[key][head]
+        // operands read eight tiles ahead of the MFMAs that use them
+        constexpr int PG = NDT < 8 ? NDT : 8;
+        uint2 vop[2][PG];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint2 a2 = *reinterpret_cast<const uint2*>(vtile + vb + VT_DT * dt);
-            const f16x4 a = *reinterpret_cast<const f16x4*>(&a2);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, oacc[dt], 0, 0, 0);
+        for (int j = 0; j < PG; ++j) vop[0][j] = *reinterpret_cast<const uint2*>(vtile + vb + VT_DT * j);
+#pragma unroll
+        for (int grp = 0; grp < NDT / PG; ++grp) {
+            if (grp + 1 < NDT / PG) {
+#pragma unroll
+                for (int j = 0; j < PG; ++j)
+                    vop[(grp + 1) & 1][j] = *reinterpret_cast<const uint2*>(vtile + vb + VT_DT * (PG * (grp + 1) + j));
+            }
+#pragma unroll
+            for (int j = 0; j < PG; ++j) {
+                const f16x4 a = *reinterpret_cast<const f16x4*>(&vop[grp & 1][j]);
+                oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, oacc[PG * grp + j], 0, 0, 0);
+            }
         }
     }
 
@@ -657,9 +675,12 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
         else if (p.nsplit <= 8)
             attn_merge_kernel<8><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D, p.merge, o,
                                                          lse);
-        else
+        else if (p.nsplit <= 16)
             attn_merge_kernel<16><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D,
-                                                                p.merge, o, lse);
+                                                         p.merge, o, lse);
+        else  // one batch up to 24 splits (decode at a few rows)
+            attn_merge_kernel<24><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D,
+                                                         p.merge, o, lse);
     }
     return launch_status(what);
 }
