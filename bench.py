@@ -169,9 +169,10 @@ def main():
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_probe_mib), indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): there is no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
 
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -192,16 +193,27 @@ def main():
     dev = inst.latent.device
     stream = torch.cuda.current_stream()
 
-    # the new tokens' main-KV entries (a1): re-quantised into the last Q slots of each sequence
+    # everything a decode step stores about its new tokens, one launch per token:
+    # the FP4 main-KV entry (re-quantised into the last Q entries of each
+    # sequence), its indexer key, and every layer's window row at the token's
+    # ring slot (the rows already there, so the instance stays unchanged)
     new = []
     for q in range(w.Q if decode else 0):
         last = inst.lengths - w.Q + q
-        new.append((inst.latent[torch.from_numpy(inst.offsets[:-1] + last).to(dev)].contiguous(),
-                    torch.from_numpy(last).to(dev)))
+        rows = torch.from_numpy(inst.offsets[:-1] + last).to(dev)
+        slot_h = inst.q_slot_host[:, q].astype(np.int64)
+        bidx = torch.arange(w.B, device=dev)
+        slot_d = torch.from_numpy(slot_h).to(dev)
+        new.append(dict(x=inst.latent[rows].contiguous(), pos=torch.from_numpy(last).to(dev),
+                        k_new=inst.k_logical[rows].contiguous(),
+                        swa_new=[L["swa"][bidx, slot_d].contiguous() for L in inst.layers],
+                        slot=slot_d.to(torch.int32)))
+    swa_kv = [L["swa"] for L in inst.layers]
 
     def step():
-        for x_new, pos in new:
-            api.csa2_fp4_append(x_new, pos, inst.cache)
+        for a in new:
+            api.csa2_append_token(a["x"], a["pos"], inst.cache, a["k_new"], inst.kview, a["swa_new"], swa_kv,
+                                  a["slot"])
         run.step()
 
     for _ in range(args.warmup):

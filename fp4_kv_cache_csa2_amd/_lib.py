@@ -38,6 +38,12 @@ class LayerArgs(ctypes.Structure):
                 ("build_pool", i32), ("ws", P), ("ws_bytes", sz)]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("B", i32), ("x", P), ("xt", ctypes.c_int), ("pos", P), ("kv", ctypes.POINTER(Fp4KV)),
+                ("k_new", P), ("k", ctypes.POINTER(IdxK)), ("n_layers", i32), ("swa_new", ctypes.POINTER(P)),
+                ("swa_kv", ctypes.POINTER(P)), ("T", i32), ("slot", P)]
+
+
 class GroupState(ctypes.Structure):
     _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32), ("ws_clean", i32)]
 
@@ -50,6 +56,7 @@ SIGNATURES = {
     "csa2_fp4_quantize": (ctypes.c_int, [P, ctypes.c_int, i64, i32, P, P, P]),
     "csa2_fp4_dequantize": (ctypes.c_int, [P, P, i64, i32, P, P]),
     "csa2_fp4_append": (ctypes.c_int, [P, ctypes.c_int, i32, P, ctypes.POINTER(Fp4KV), P]),
+    "csa2_append_token": (ctypes.c_int, [ctypes.POINTER(AppendArgs), P]),
     "csa2_index_full": (ctypes.c_int, [P, i32, i32, i32, ctypes.POINTER(IdxK), P, i32, P, P, P]),
     "csa2_index_reindex": (ctypes.c_int, [P, i32, i32, i32, ctypes.POINTER(IdxK), P, P, i32, P, P]),
     "csa2_topk_workspace_size": (sz, [i32, i32, i32]),

@@ -86,6 +86,24 @@ def csa2_fp4_append(x, pos, cache: Fp4Cache, stream=None):
                                            _stream(stream)))
 
 
+def csa2_append_token(x, pos, cache: Fp4Cache, k_new=None, kview: IndexerK | None = None, swa_new=(), swa_kv=(),
+                      slot=None, stream=None):
+    """One launch per decode step: FP4 entry pos[b] from x[b], indexer-K entry
+    pos[b] from k_new[b], and slot slot[b] of every swa_kv[l] from swa_new[l][b]."""
+    v = cache.view()
+    kv = kview.view() if kview is not None else None
+    n = len(swa_new)
+    if len(swa_kv) != n:
+        raise ValueError("swa_new and swa_kv must have one tensor per layer each")
+    new_arr = (_lib.P * max(n, 1))(*[t.data_ptr() for t in swa_new])
+    kv_arr = (_lib.P * max(n, 1))(*[t.data_ptr() for t in swa_kv])
+    T = swa_kv[0].shape[1] if n else 0
+    a = _lib.AppendArgs(x.shape[0], x.data_ptr(), _dtype(x), pos.data_ptr(), ctypes.pointer(v),
+                        None if k_new is None else k_new.data_ptr(), None if kv is None else ctypes.pointer(kv),
+                        n, new_arr, kv_arr, T, None if slot is None else slot.data_ptr())
+    _lib.check(_lib.load().csa2_append_token(ctypes.byref(a), _stream(stream)))
+
+
 def csa2_index_full(q_idx, kview: IndexerK, n_vis, n_max, scores, block_max=None, stream=None):
     B, Q, H_i, _ = q_idx.shape
     v = kview.view()

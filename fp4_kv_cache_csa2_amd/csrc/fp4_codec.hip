@@ -139,10 +139,110 @@ __global__ __launch_bounds__(64) void fp4_append_kernel(const void* __restrict__
     }
 }
 
+constexpr int APPEND_MAX_LAYERS = 32;
+
+struct AppendParams {
+    const void* x;
+    int32_t D, D_i, B, n_layers, T;
+    const int32_t* pos;
+    const int32_t* slot;
+    RowMap kvmap, kmap;
+    uint8_t* codes;
+    uint8_t* scales;
+    const uint16_t* k_new;
+    uint16_t* k;
+    const uint16_t* swa_new[APPEND_MAX_LAYERS];
+    uint16_t* swa_kv[APPEND_MAX_LAYERS];
+};
+
+// Workgroup (b, role): role 0 quantises the FP4 entry, role 1 copies the
+// indexer key, role 2 + l copies layer l's window row.
+template <bool BF16>
+__global__ __launch_bounds__(64) void append_token_kernel(AppendParams p) {
+    const int b = blockIdx.x, role = blockIdx.y, t = threadIdx.x;
+    if (role == 0) {
+        const int64_t row = phys_row(p.kvmap, b, p.pos[b]);
+        const int gpr = p.D / 16;
+        for (int gi = t; gi < gpr; gi += blockDim.x) {
+            float v[16];
+            load_group<BF16>(p.x, (int64_t)b * gpr + gi, v);
+            uint8_t sc;
+            const uint2 c = quantize_group(v, &sc);
+            reinterpret_cast<uint2*>(p.codes + row * (p.D / 2))[gi] = c;
+            p.scales[row * gpr + gi] = sc;
+        }
+    } else if (role == 1) {
+        if (p.k_new == nullptr) return;
+        const int64_t row = phys_row(p.kmap, b, p.pos[b]);
+        const uint4* src = reinterpret_cast<const uint4*>(p.k_new + (int64_t)b * p.D_i);
+        uint4* dst = reinterpret_cast<uint4*>(p.k + row * p.D_i);
+        for (int i = t; i < p.D_i / 8; i += blockDim.x) dst[i] = src[i];
+    } else {
+        const int l = role - 2;
+        const uint4* src = reinterpret_cast<const uint4*>(p.swa_new[l] + (int64_t)b * p.D);
+        uint4* dst = reinterpret_cast<uint4*>(p.swa_kv[l] + ((int64_t)b * p.T + p.slot[b]) * p.D);
+        for (int i = t; i < p.D / 8; i += blockDim.x) dst[i] = src[i];
+    }
+}
+
 }  // namespace
 }  // namespace csa2
 
 using namespace csa2;
+
+extern "C" csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t stream) {
+    clear_error();
+    CSA2_ARG(a != nullptr && a->kv != nullptr, "append_token: null args or cache view");
+    CSA2_ARG(a->B >= 0, "append_token: B=%d < 0", a->B);
+    CSA2_ARG(a->kv->D > 0 && a->kv->D % 16 == 0, "append_token: D=%d must be a positive multiple of 16", a->kv->D);
+    CSA2_ARG(a->xt == CSA2_F32 || a->xt == CSA2_BF16, "append_token: bad dtype %d", (int)a->xt);
+    CSA2_ARG(a->n_layers >= 0 && a->n_layers <= APPEND_MAX_LAYERS, "append_token: n_layers=%d out of [0, %d]",
+             a->n_layers, APPEND_MAX_LAYERS);
+    if (a->B == 0) return CSA2_OK;
+    CSA2_ARG(a->x && a->pos && a->kv->codes && a->kv->scales, "append_token: null pointer");
+    CSA2_ARG(aligned(a->x, 16) && aligned(a->kv->codes, 8), "append_token: x must be 16-byte and codes 8-byte aligned");
+    AppendParams p{};
+    csa2_status st = make_rowmap(a->kv->page_table, a->kv->page_size, a->kv->max_pages, a->kv->seq_stride, 1,
+                                 &p.kvmap, "append_token");
+    if (st != CSA2_OK) return st;
+    p.x = a->x;
+    p.D = a->kv->D;
+    p.B = a->B;
+    p.pos = a->pos;
+    p.codes = a->kv->codes;
+    p.scales = a->kv->scales;
+    if (a->k_new != nullptr) {
+        CSA2_ARG(a->k != nullptr && a->k->k != nullptr, "append_token: k_new given without an indexer-K view");
+        CSA2_ARG(a->k->D_i > 0 && a->k->D_i % 8 == 0, "append_token: D_i=%d must be a positive multiple of 8",
+                 a->k->D_i);
+        CSA2_ARG(aligned(a->k_new, 16) && aligned(a->k->k, 16), "append_token: k_new and k must be 16-byte aligned");
+        st = make_rowmap(a->k->page_table, a->k->page_size, a->k->max_pages, a->k->seq_stride, 1, &p.kmap,
+                         "append_token");
+        if (st != CSA2_OK) return st;
+        p.k_new = a->k_new;
+        p.k = const_cast<uint16_t*>(a->k->k);
+        p.D_i = a->k->D_i;
+    }
+    if (a->n_layers > 0) {
+        CSA2_ARG(a->swa_new && a->swa_kv && a->slot && a->T > 0, "append_token: null window arrays / slot or T <= 0");
+        for (int l = 0; l < a->n_layers; ++l) {
+            CSA2_ARG(a->swa_new[l] && a->swa_kv[l], "append_token: null window row pointer of layer %d", l);
+            CSA2_ARG(aligned(a->swa_new[l], 16) && aligned(a->swa_kv[l], 16),
+                     "append_token: window rows of layer %d must be 16-byte aligned", l);
+            p.swa_new[l] = a->swa_new[l];
+            p.swa_kv[l] = a->swa_kv[l];
+        }
+        p.n_layers = a->n_layers;
+        p.T = a->T;
+        p.slot = a->slot;
+    }
+    const dim3 grid((unsigned)a->B, (unsigned)(2 + a->n_layers));
+    if (a->xt == CSA2_BF16)
+        append_token_kernel<true><<<grid, 64, 0, stream>>>(p);
+    else
+        append_token_kernel<false><<<grid, 64, 0, stream>>>(p);
+    return launch_status("append_token");
+}
 
 extern "C" csa2_status csa2_fp4_quantize(const void* x, csa2_dtype xt, int64_t rows, int32_t D, uint8_t* codes,
                                          uint8_t* scales, hipStream_t stream) {

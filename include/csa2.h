@@ -110,6 +110,37 @@ csa2_status csa2_fp4_dequantize(const uint8_t* codes, const uint8_t* scales, int
 csa2_status csa2_fp4_append(const void* x, csa2_dtype xt, int32_t B, const int32_t* pos, const csa2_fp4_kv* kv,
                             hipStream_t stream);
 
+/* Per-step append of one decode token per sequence, in one launch: everything
+ * the layer stack reads about the new token.
+ *   x       [B][D] fp32/bf16: main-KV latent of the new entry, FP4-quantised
+ *           into logical entry pos[b] of sequence b of kv (as csa2_fp4_append)
+ *   k_new   [B][D_i] bf16 or NULL: indexer key of the new entry, copied to
+ *           entry pos[b] of the indexer-K view k
+ *   swa_new [n_layers] host array of device pointers to [B][D] bf16 rows: each
+ *           layer's window row of the new token, copied to slot slot[b] of the
+ *           layer's swa_kv[l] ([B][T][D] bf16; a 128-slot ring when T = window:
+ *           the window is a set, so slot order does not matter)
+ * pos and slot are device [B] int32; every pos[b] must address an allocated row
+ * of both views and 0 <= slot[b] < T.  0 <= n_layers <= 32.  Alignment: x,
+ * k_new, k and every window pointer 16 bytes, codes 8.  Rows are written
+ * in place; the caller orders this call before the layers that read them
+ * (aprilzz.com, sections "FP4 KV 与部署层的几个改动" and "把 prefill 砍掉一半"). */
+typedef struct csa2_append_args {
+    int32_t B;
+    const void* x;
+    csa2_dtype xt;
+    const int32_t* pos;
+    const csa2_fp4_kv* kv;
+    const uint16_t* k_new;
+    const csa2_idx_k* k;
+    int32_t n_layers;
+    const uint16_t* const* swa_new;
+    uint16_t* const* swa_kv;
+    int32_t T;
+    const int32_t* slot;
+} csa2_append_args;
+csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Full-mode indexer scoring (gkm0120.cn section 2.2.2; aprilzz.com CSA2 section).
  *   q_idx  [B][Q][H_i][D_i] bf16 indexer queries (row r = b*Q + q)

@@ -72,6 +72,51 @@ def test_fp4_append_paged():
     assert int(codes.count_nonzero()) <= B * D // 2  # nothing else written
 
 
+@pytest.mark.parametrize("paged,n_layers,with_k,xdtype", [(True, 4, True, torch.bfloat16),
+                                                         (False, 3, True, torch.float32),
+                                                         (False, 0, False, torch.bfloat16),
+                                                         (True, 32, True, torch.bfloat16)])
+def test_append_token(paged, n_layers, with_k, xdtype):
+    B, D, D_i, T, ps = 5, 512, 128, 128, 64
+    lengths = np.array([100, 64, 3, 200, 128])
+    pos = np.array([99, 0, 2, 150, 127], np.int32)
+    slot = (pos % T).astype(np.int32)
+    tag = f"apt{paged}{n_layers}"
+    if paged:
+        table, n_pages = inputs.random_page_table(lengths, ps, tag)
+        n_rows, tab_d, stride = n_pages * ps, torch.from_numpy(table).to(DEV), 0
+    else:
+        n_rows, tab_d, stride = B * 256, None, 256
+    codes = torch.zeros(n_rows, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(n_rows, D // 16, dtype=torch.uint8, device=DEV)
+    cache = api.Fp4Cache(codes, scales, D, stride, tab_d, ps if paged else 0)
+    kbuf = torch.zeros(n_rows, D_i, dtype=torch.bfloat16, device=DEV)
+    kview = api.IndexerK(kbuf, D_i, stride, tab_d, ps if paged else 0) if with_k else None
+    x = inputs.normal((B, D), tag + "x", dtype=xdtype)
+    k_new = inputs.normal((B, D_i), tag + "k", dtype=torch.bfloat16)
+    swa_new = [inputs.normal((B, D), f"{tag}s{l}", dtype=torch.bfloat16).to(DEV) for l in range(n_layers)]
+    swa_kv = [torch.zeros(B, T, D, dtype=torch.bfloat16, device=DEV) for _ in range(n_layers)]
+    case(f"append_token paged={paged} n_layers={n_layers} k={with_k} {xdtype}")
+    api.csa2_append_token(x.to(DEV), torch.from_numpy(pos).to(DEV), cache,
+                          k_new.to(DEV) if with_k else None, kview, swa_new, swa_kv,
+                          torch.from_numpy(slot).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oracle.fp4_encode(x.float().numpy())
+    rows = [(table[b, pos[b] // ps] * ps + pos[b] % ps) if paged else b * stride + pos[b] for b in range(B)]
+    for b in range(B):
+        np.testing.assert_array_equal(to_np(codes[rows[b]]), rc[b])
+        np.testing.assert_array_equal(to_np(scales[rows[b]]), rs[b])
+        if with_k:
+            assert torch.equal(kbuf[rows[b]].cpu(), k_new[b])
+        for l in range(n_layers):
+            assert torch.equal(swa_kv[l][b, slot[b]].cpu(), swa_new[l][b].cpu())
+    # nothing else written
+    assert int(codes.count_nonzero()) <= B * D // 2
+    assert int((kbuf != 0).any(dim=1).sum()) == (B if with_k else 0)
+    for l in range(n_layers):
+        assert int((swa_kv[l] != 0).any(dim=2).sum()) == B
+
+
 # --------------------------------------------------------------------------- indexer
 def _k_view(B, n_max, D_i, tag, paged):
     K = inputs.normal((B, n_max, D_i), tag, dtype=torch.bfloat16)
