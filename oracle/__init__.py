@@ -19,6 +19,12 @@ Functions and the passages they follow (full citations in ``csa2_oracle.c``):
                                and the CSA2 section (own main Q and SWA KV per layer).
   run_stack                    gkm0120.cn section 2.2.2 mode table; aprilzz.com CSA2
                                section (group patterns, latest Top-K reused).
+  bf16_round / swa_replay      aprilzz.com sections "把 prefill 砍掉一半" and
+                               "FP4 KV 与部署层的几个改动" (a missing window is rebuilt
+                               from the last 128 tokens); gkm0120.cn section 2.1
+                               (SWA Bounded Replay); aimodeling.com "第三层".  The
+                               projection itself is a reading: kv_p = bf16(h_p W^T),
+                               one rounding.
 
 Parity-unpinned readings (pinned only by the workload text, never by the
 pages): the score has no ReLU / head weights / scale; the pool ranks 8-entry
@@ -70,6 +76,9 @@ def _load():
         lib.oracle_block_max.argtypes = [P, i64, P]
         lib.oracle_topk.argtypes = [P, i64, i32, P, P]
         lib.oracle_attention.argtypes = [P, i32, i32, P, P, P, i32, P, i32, i32, i32, ctypes.c_double, P, P]
+        lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_round.restype = ctypes.c_uint16
+        lib.oracle_swa_replay.argtypes = [P, P, i32, i32, i32, i64, i32, P]
         _lib = lib
     return _lib
 
@@ -181,6 +190,26 @@ def attention(q: np.ndarray, codes: np.ndarray | None, scales: np.ndarray | None
     _load().oracle_attention(_ptr(q), H, D, _ptr(codes), _ptr(scales), _ptr(idx_a), K, _ptr(swa_a), T, int(slot),
                              int(window), float(sm_scale), _ptr(o), _ptr(lse))
     return o, lse
+
+
+# ----------------------------------------------------------------------------- window replay
+def bf16_round(v: float) -> int:
+    """fp64 -> bf16 bits, nearest / ties to even, in one rounding."""
+    return int(_load().oracle_bf16_round(float(v)))
+
+
+def swa_replay(h: np.ndarray, W: np.ndarray, t_end: int, T: int, ring: np.ndarray | None = None) -> np.ndarray:
+    """h[n][d_model] and W[D][d_model] bf16 bits (uint16): the window rows of
+    positions t_end-n+1 .. t_end, bf16(h_p W^T), written to rows p mod T of a
+    copy of ring[T][D] (zeros when None), which is returned."""
+    h = _c(h, np.uint16)
+    W = _c(W, np.uint16)
+    n, dm = h.shape
+    D, dm2 = W.shape
+    assert dm == dm2 and n <= T and t_end >= n - 1
+    out = np.zeros((T, D), np.uint16) if ring is None else _c(ring, np.uint16).copy()
+    _load().oracle_swa_replay(_ptr(h), _ptr(W), n, dm, D, int(t_end), T, _ptr(out))
+    return out
 
 
 # ----------------------------------------------------------------------------- layer schedule

@@ -341,3 +341,51 @@ void oracle_attention(const double* q, int32_t H, int32_t D, const uint8_t* code
     free(z);
     free(keys);
 }
+
+/* ------------------------------------------------------------------------ */
+/* SWA Bounded Replay                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* fp64 -> bf16 bit pattern, round to nearest, ties to even, in one step (no
+ * intermediate fp32 rounding).  bf16 = 1 sign, 8 exponent (bias 127), 7
+ * fraction bits; below 2^-126 the spacing stays 2^-133 (subnormals);
+ * magnitudes that round past the largest finite value become infinity. */
+uint16_t oracle_bf16_round(double v) {
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return 0x7FC0u;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7F80u;
+    if (a == 0.0) return sign;
+    int e = ilogb(a);                 /* 2^e <= a < 2^(e+1) */
+    if (e < -126) e = -126;           /* subnormal range: fixed spacing */
+    const int q = e - 7;              /* spacing of bf16 values near a */
+    const double r = rint(ldexp(a, -q)); /* default rounding mode: nearest, ties to even */
+    const double y = ldexp(r, q);
+    if (y >= ldexp(1.0, 128)) return sign | 0x7F80u;
+    const float f = (float)y;         /* exact: y has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | ((u >> 16) & 0x7FFFu));
+}
+
+/* Rebuild a layer's window rows by replaying its last n tokens.  Reading
+ * (the pages state only that the missing window state is rebuilt from the
+ * last n_win = 128 tokens [P4 "把 prefill 砍掉一半", "FP4 KV 与部署层的几个改动"]):
+ * the window row of token p is the layer's window projection of its input at
+ * p, kv_p[d] = sum_c h_p[c] * W[d][c] (W output-major [D][d_model]), rounded
+ * once to bf16.  h[n][d_model] holds the inputs of positions
+ * t_end-n+1 .. t_end in order; token p goes to ring row p mod T.  Rows of the
+ * ring that no replayed token maps to are left as they are. */
+void oracle_swa_replay(const uint16_t* h, const uint16_t* W, int32_t n, int32_t dm, int32_t D, int64_t t_end,
+                       int32_t T, uint16_t* ring) {
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t p = t_end - n + 1 + i;
+        const int64_t slot = p % T;
+        for (int32_t d = 0; d < D; ++d) {
+            double acc = 0.0; /* each product is exact in fp64 (8 + 8 significant bits) */
+            for (int32_t c = 0; c < dm; ++c)
+                acc += (double)bf16_to_float(h[(int64_t)i * dm + c]) * (double)bf16_to_float(W[(int64_t)d * dm + c]);
+            ring[slot * D + d] = oracle_bf16_round(acc);
+        }
+    }
+}
