@@ -124,6 +124,84 @@ def alg_bytes(w, n_entries_total):
     return dict(full=full, reindex=reindex, attn=attn, append=append, total=full + reindex + attn + append)
 
 
+REPLAY = dict(name="swa_replay_b4_l20", L=20, B=4, n=128, d_model=4096, D=512, T=128, t_end=(1 << 20) - 1)
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def bench_replay(args):
+    """SWA Bounded Replay of 128-token windows: 20 layers x 4 sequences, one
+    launch per step (inputs resident in HBM)."""
+    import numpy as np
+    import torch
+
+    from fp4_kv_cache_csa2_amd import api, inputs
+
+    r = REPLAY
+    L, B, n, dm, D, T = r["L"], r["B"], r["n"], r["d_model"], r["D"], r["T"]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    scale = 2.0 ** -round(np.log2(np.sqrt(dm)))
+    h = [inputs.normal((B, n, dm), f"{r['name']}/h{l}", 0, dev, torch.bfloat16) for l in range(L)]
+    W = [(inputs.normal((D, dm), f"{r['name']}/W{l}", 0, dev) * scale).to(torch.bfloat16) for l in range(L)]
+    rings = [torch.zeros(B, T, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    t_end = torch.full((B,), r["t_end"], dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        api.csa2_swa_replay(h, W, rings, t_end)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.csa2_swa_replay(h, W, rings, t_end)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = sum(ms) / len(ms)
+    flops = 2.0 * L * B * n * D * dm
+    hbm = L * (B * n * dm * 2 + D * dm * 2 + B * n * D * 2)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "SWA bounded replay: window rows rebuilt/s; achieved MFMA TFLOP/s vs peak",
+        "value": round(L * B * n / (ms_step * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) layer inputs, N(0,1)/64 projections)",
+        "config": {"workload": r["name"], "layers": L, "B": B, "tokens": n, "d_model": dm, "D": D, "T": T},
+        "step_alg_bytes": hbm,
+        "step_hbm_GBps": round(hbm / (ms_step * 1e-3) / 1e9, 1),
+    }
+    # the roofline is whichever of HBM bytes and MFMA flops needs more time at peak
+    gbps = hbm / (ms_step * 1e-3) / 1e9
+    if hbm / (HBM_PEAK_GBPS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    out["roofline"] = dict(roof, kernel="swa_replay_kernel (bf16 GEMM, fp32 accumulate)", traffic=None,
+                           alg_bytes_per_launch=hbm, alg_flops_per_launch=flops, mfma_tflops=round(tflops, 1),
+                           mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), avg_launch_ms=round(ms_step, 5),
+                           launches_timed=len(ms))
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        hb = h[0][0].view(torch.int16).cpu().numpy().view(np.uint16)
+        Wb = W[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        done = 0
+        while done < n and (done == 0 or time.perf_counter() - t0 < args.cpu_seconds):
+            oracle.swa_replay(hb[done:done + 1], Wb, done, T)
+            done += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(done / dt, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} window rows of one layer (d_model {dm}, D {D}), fp64, one thread"}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inst, budget_s):
     """Time the CPU oracle on whole query rows of the same workload until the
     budget is used (at least one row)."""
@@ -172,10 +250,13 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): there is no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    if args.workload == REPLAY["name"]:
+        bench_replay(args)
+        return
     import numpy as np
     import torch
 
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from fp4_kv_cache_csa2_amd import api, inputs, workload
 
     w = inputs.WORKLOADS[args.workload]

@@ -44,6 +44,11 @@ class AppendArgs(ctypes.Structure):
                 ("swa_kv", ctypes.POINTER(P)), ("T", i32), ("slot", P)]
 
 
+class ReplayArgs(ctypes.Structure):
+    _fields_ = [("B", i32), ("n", i32), ("d_model", i32), ("D", i32), ("T", i32), ("t_end", P), ("n_layers", i32),
+                ("h", ctypes.POINTER(P)), ("W", ctypes.POINTER(P)), ("swa_kv", ctypes.POINTER(P))]
+
+
 class GroupState(ctypes.Structure):
     _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32), ("ws_clean", i32)]
 
@@ -57,6 +62,7 @@ SIGNATURES = {
     "csa2_fp4_dequantize": (ctypes.c_int, [P, P, i64, i32, P, P]),
     "csa2_fp4_append": (ctypes.c_int, [P, ctypes.c_int, i32, P, ctypes.POINTER(Fp4KV), P]),
     "csa2_append_token": (ctypes.c_int, [ctypes.POINTER(AppendArgs), P]),
+    "csa2_swa_replay": (ctypes.c_int, [ctypes.POINTER(ReplayArgs), P]),
     "csa2_index_full": (ctypes.c_int, [P, i32, i32, i32, ctypes.POINTER(IdxK), P, i32, P, P, P]),
     "csa2_index_reindex": (ctypes.c_int, [P, i32, i32, i32, ctypes.POINTER(IdxK), P, P, i32, P, P]),
     "csa2_topk_workspace_size": (sz, [i32, i32, i32]),

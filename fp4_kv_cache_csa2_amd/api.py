@@ -104,6 +104,22 @@ def csa2_append_token(x, pos, cache: Fp4Cache, k_new=None, kview: IndexerK | Non
     _lib.check(_lib.load().csa2_append_token(ctypes.byref(a), _stream(stream)))
 
 
+def csa2_swa_replay(h, W, swa_kv, t_end, stream=None):
+    """Rebuild window rows: h[l] [B][n][d_model], W[l] [D][d_model] bf16,
+    swa_kv[l] [B][T][D] bf16 (written), t_end [B] int32 on the device."""
+    L = len(h)
+    if len(W) != L or len(swa_kv) != L:
+        raise ValueError("h, W and swa_kv must have one tensor per layer each")
+    if L == 0:
+        return
+    B, n, dm = h[0].shape
+    D = W[0].shape[0]
+    T = swa_kv[0].shape[1]
+    arr = lambda ts: (_lib.P * L)(*[t.data_ptr() for t in ts])
+    a = _lib.ReplayArgs(B, n, dm, D, T, t_end.data_ptr(), L, arr(h), arr(W), arr(swa_kv))
+    _lib.check(_lib.load().csa2_swa_replay(ctypes.byref(a), _stream(stream)))
+
+
 def csa2_index_full(q_idx, kview: IndexerK, n_vis, n_max, scores, block_max=None, stream=None):
     B, Q, H_i, _ = q_idx.shape
     v = kview.view()

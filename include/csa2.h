@@ -142,6 +142,35 @@ typedef struct csa2_append_args {
 csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * SWA Bounded Replay: rebuild window rows from the last n tokens instead of
+ * keeping them (gkm0120.cn section 2.1; aprilzz.com sections "把 prefill 砍掉一半"
+ * and "FP4 KV 与部署层的几个改动"; aimodeling.com "第三层").  For every layer l
+ * and sequence b, token i (0 <= i < n) of the replay has position
+ * p = t_end[b] - n + 1 + i and its window row is
+ *   swa_kv[l][b][p mod T][d] = bf16( sum_c h[l][b][i][c] * W[l][d][c] )
+ * accumulated in fp32 and rounded to nearest-even once.  Positions p < 0 are
+ * skipped; other ring rows are left as they are.
+ *   h      [n_layers] host array of device [B][n][d_model] bf16 (layer inputs)
+ *   W      [n_layers] host array of device [D][d_model] bf16 (output-major)
+ *   swa_kv [n_layers] host array of device [B][T][D] bf16 rings (written)
+ *   t_end  [B] device int32
+ * 0 <= n <= T; d_model % 32 == 0; D % 16 == 0; 0 <= n_layers <= 48; h and W
+ * 16-byte aligned, swa_kv 8-byte aligned.  B*n == 0 or n_layers == 0: no-op. */
+typedef struct csa2_replay_args {
+    int32_t B;
+    int32_t n;
+    int32_t d_model;
+    int32_t D;
+    int32_t T;
+    const int32_t* t_end;
+    int32_t n_layers;
+    const uint16_t* const* h;
+    const uint16_t* const* W;
+    uint16_t* const* swa_kv;
+} csa2_replay_args;
+csa2_status csa2_swa_replay(const csa2_replay_args* a, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Full-mode indexer scoring (gkm0120.cn section 2.2.2; aprilzz.com CSA2 section).
  *   q_idx  [B][Q][H_i][D_i] bf16 indexer queries (row r = b*Q + q)
  *   k      indexer-K view of B sequences, shared by all heads and layers

@@ -125,3 +125,26 @@ def test_layer_workspace_size_covers_parts(lib):
     total = lib.csa2_layer_workspace_size(rows, 1, 64, 512, n, 512, 2048)
     assert total >= rows * n * 4 + lib.csa2_topk_workspace_size(rows, n, 512) + lib.csa2_attn_workspace_size(
         rows, 1, 64, 512)
+
+
+def test_replay_and_append_argument_errors(lib):
+    arr = (_lib.P * 1)(FAKE.value)
+    a = _lib.ReplayArgs(2, 8, 100, 512, 128, FAKE.value, 1, arr, arr, arr)  # d_model not a multiple of 32
+    assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_EINVAL
+    assert "multiple of 32" in _err(lib)
+    a = _lib.ReplayArgs(2, 200, 128, 512, 128, FAKE.value, 1, arr, arr, arr)  # n > T
+    assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_EINVAL
+    a = _lib.ReplayArgs(2, 8, 128, 500, 128, FAKE.value, 1, arr, arr, arr)  # D not a multiple of 16
+    assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_EINVAL
+    a = _lib.ReplayArgs(2, 8, 128, 512, 128, FAKE.value, 49, arr, arr, arr)  # too many layers
+    assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_EINVAL
+    a = _lib.ReplayArgs(0, 8, 128, 512, 128, None, 1, None, None, None)  # nothing to do
+    assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_OK
+    kv = _lib.Fp4KV(FAKE.value, FAKE.value, None, 0, 0, 4096, 24)  # D not a multiple of 16
+    ap = _lib.AppendArgs(1, FAKE.value, 0, FAKE.value, ctypes.pointer(kv), None, None, 0, None, None, 0, None)
+    assert lib.csa2_append_token(ctypes.byref(ap), None) == _lib.CSA2_EINVAL
+    kv = _lib.Fp4KV(FAKE.value, FAKE.value, None, 0, 0, 4096, 512)
+    ap = _lib.AppendArgs(1, FAKE.value, 0, FAKE.value, ctypes.pointer(kv), None, None, 33, arr, arr, 128, FAKE.value)
+    assert lib.csa2_append_token(ctypes.byref(ap), None) == _lib.CSA2_EINVAL  # too many layers
+    ap = _lib.AppendArgs(1, FAKE.value, 0, FAKE.value, ctypes.pointer(kv), FAKE.value, None, 0, None, None, 0, None)
+    assert lib.csa2_append_token(ctypes.byref(ap), None) == _lib.CSA2_EINVAL  # key without a K view
