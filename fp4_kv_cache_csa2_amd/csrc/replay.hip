@@ -9,21 +9,29 @@
 // C^T[D][M] = W[D][d_model] . h[M][d_model]^T (M = B x n tokens) on
 // v_mfma_f32_16x16x32_bf16 with fp32 accumulation; computing C^T puts four
 // consecutive output columns of one token in each lane, stored as 8 bytes.
-// Workgroup tile: 128 output columns x 128 tokens, 4 waves of 64 x 64.  The
-// operand tiles (32 channels deep) stream global -> LDS by LDS DMA through a
-// 4-deep ring of separate LDS arrays (three k-steps in flight while one is
+// Workgroup tile: 256 output columns x 128 tokens, 8 waves of 64 x 64, one
+// workgroup per CU.  Each k-step copies one 128-byte line (64 channels) of
+// every W and h row of the tile global -> LDS by LDS DMA (whole-line requests
+// move about 1.4x the bytes per second of half-line ones here) through a
+// 3-deep ring of separate LDS arrays (two k-steps in flight while one is
 // multiplied); 16-byte chunks are XOR-swizzled so that each 16-lane operand
-// read hits 16 distinct bank groups.
+// read hits 16 distinct bank groups.  The tile is as large as the LDS ring
+// allows: every workgroup pulls its rows through its CU's path from L2, so
+// bytes per CU, not HBM, bound this kernel at these sizes.
 #include "internal.h"
 
 namespace csa2 {
 namespace {
 
 constexpr int RP_MAX_LAYERS = 48;
-constexpr int RP_TILE = 128;   // output columns (D) and tokens (M) per workgroup
-constexpr int RP_KS = 32;      // channels per k-step (one MFMA deep)
-constexpr int RP_NST = 4;      // ring depth
-constexpr int RP_HALF = RP_TILE * RP_KS * 2;  // bytes of one operand tile per k-step (8 KB)
+constexpr int RP_TN = 256;     // output columns (D, rows of W) per workgroup
+constexpr int RP_TM = 128;     // tokens (rows of h) per workgroup
+constexpr int RP_KS = 64;      // channels per k-step: one 128-byte line of every row
+constexpr int RP_NST = 3;      // ring depth (two k-steps in flight while one is multiplied)
+constexpr int RP_WAVES = 8;    // 4 x 2 waves of 64 x 64
+constexpr int RP_STAGE = (RP_TN + RP_TM) * RP_KS * 2;  // 48 KB per k-step
+constexpr int RP_H_OFF = RP_TN * RP_KS * 2;            // h rows after the W rows
+constexpr int RP_NJ = RP_STAGE / 1024 / RP_WAVES;      // DMA instructions per wave per k-step (6)
 
 struct ReplayParams {
     int32_t M, n, dm, D, T;
@@ -36,6 +44,7 @@ struct ReplayParams {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void rp_dma16(const void* src, void* lds_base) {
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(const_cast<void*>(src)), (lds_ptr_t)lds_base, 16, 0, 0);
@@ -56,17 +65,50 @@ __device__ __forceinline__ void rp_wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+// The eight MFMA operands of one 32-channel half k-step: four W rows and four
+// h rows 2 KB apart.  Written as one asm block that also waits for the reads:
+// the compiler cannot tell the ring slots apart and would otherwise make every
+// read wait for all LDS copies still in flight.
+__device__ __forceinline__ void read_operands(uint32_t aw, uint32_t ah, bf16x8 (&wa)[4], bf16x8 (&hb)[4]) {
+    u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:2048\n"
+        "ds_read_b128 %2, %8 offset:4096\n"
+        "ds_read_b128 %3, %8 offset:6144\n"
+        "ds_read_b128 %4, %9\n"
+        "ds_read_b128 %5, %9 offset:2048\n"
+        "ds_read_b128 %6, %9 offset:4096\n"
+        "ds_read_b128 %7, %9 offset:6144\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(aw), "v"(ah)
+        : "memory");
+    wa[0] = __builtin_bit_cast(bf16x8, r0);
+    wa[1] = __builtin_bit_cast(bf16x8, r1);
+    wa[2] = __builtin_bit_cast(bf16x8, r2);
+    wa[3] = __builtin_bit_cast(bf16x8, r3);
+    hb[0] = __builtin_bit_cast(bf16x8, r4);
+    hb[1] = __builtin_bit_cast(bf16x8, r5);
+    hb[2] = __builtin_bit_cast(bf16x8, r6);
+    hb[3] = __builtin_bit_cast(bf16x8, r7);
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
     const uint32_t u = __float_as_uint(x);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__global__ __launch_bounds__(256, 2) void swa_replay_kernel(ReplayParams p) {
-    // ring of k-steps: [W tile 128 x 32 | h tile 128 x 32] bf16, swizzled chunks
-    __shared__ __attribute__((aligned(16))) uint8_t st0[2 * RP_HALF];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[2 * RP_HALF];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[2 * RP_HALF];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[2 * RP_HALF];
+__global__ __launch_bounds__(64 * RP_WAVES, 1) void swa_replay_kernel(ReplayParams p) {
+    // ring of k-steps: [W tile 256 x 64 | h tile 128 x 64] bf16, one 128-byte
+    // row each, 16-byte chunks swizzled
+    __shared__ __attribute__((aligned(16))) uint8_t st0[RP_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[RP_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[RP_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,37 +121,38 @@ __global__ __launch_bounds__(256, 2) void swa_replay_kernel(ReplayParams p) {
     const int per = G / 8, rem = G % 8;
     const int lin = xcd * per + min(xcd, rem) + k;
     const int nt = lin % p.n_tiles, mt = (lin / p.n_tiles) % p.m_tiles, layer = lin / (p.n_tiles * p.m_tiles);
-    const int n0 = nt * RP_TILE, m0 = mt * RP_TILE;
+    const int n0 = nt * RP_TN, m0 = mt * RP_TM;
     const uint16_t* __restrict__ Wl = p.W[layer];
     const uint16_t* __restrict__ hl = p.h[layer];
 
-    // ---- this lane's four DMA sources per k-step: wave w copies 16-byte chunk
-    // positions (4w + j) * 64 + lane of the 1024 in a k-step (W tile first)
-    const char* src[4];
+    // ---- this lane's DMA sources: wave w copies 16-byte chunk positions
+    // (6w + j) * 64 + lane of the 3072 in a k-step (2048 of W, then 1024 of h);
+    // position (r, c') holds channel chunk c = c' ^ ((r / 2) % 8) of row r
+    const char* src[RP_NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int q = (4 * w + j) * 64 + lane;
-        const bool is_h = q >= 512;
-        const int pos = q & 511;
-        const int r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
+    for (int j = 0; j < RP_NJ; ++j) {
+        const int q = (RP_NJ * w + j) * 64 + lane;
+        const bool is_h = q >= RP_TN * 8;
+        const int pos = is_h ? q - RP_TN * 8 : q;
+        const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
         const int64_t grow = is_h ? min(m0 + r, p.M - 1) : min(n0 + r, p.D - 1);
         src[j] = reinterpret_cast<const char*>(is_h ? hl : Wl) + (grow * p.dm + 8 * c) * 2;
     }
-    const int dst_off = (4 * w) % 8 * 1024 + (w >= 2 ? RP_HALF : 0);  // + j * 1024
+    const int dst_off = RP_NJ * w * 1024;  // + j * 1024
 
     const int nk = p.dm / RP_KS;
     auto issue = [&](int ks, uint8_t* buf) {
         const int64_t kb = (int64_t)ks * RP_KS * 2;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rp_dma16(src[j] + kb, buf + dst_off + j * 1024);
+        for (int j = 0; j < RP_NJ; ++j) rp_dma16(src[j] + kb, buf + dst_off + j * 1024);
     };
 
-    // ---- operand reads: lane (c16, g) reads row 16a + c16 of its wave's band,
-    // channels 8g..8g+7 of the k-step, at chunk g ^ (c16 / 4)
+    // ---- operand reads: lane (c16, g) reads rows 16a + c16 of its wave's W
+    // band and h band, channel chunk 4 kh + g of half k-step kh
     const int c16 = lane & 15, g = lane >> 4;
-    const int wn = w & 1, wm = w >> 1;
-    const int rd_w = (wn * 64 + c16) * 64 + ((g ^ (c16 >> 2)) << 4);
-    const int rd_h = RP_HALF + (wm * 64 + c16) * 64 + ((g ^ (c16 >> 2)) << 4);
+    const int wn = w & 3, wm = w >> 2;
+    const int rw = (wn * 64 + c16) * 128, rh = RP_H_OFF + (wm * 64 + c16) * 128;
+    const int ch0 = (g ^ (c16 >> 1)) << 4, ch1 = ((4 + g) ^ (c16 >> 1)) << 4;
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -117,46 +160,37 @@ __global__ __launch_bounds__(256, 2) void swa_replay_kernel(ReplayParams p) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8 wa[4], hb[4];
-    auto read_ops = [&](const uint8_t* buf) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) wa[a] = *reinterpret_cast<const bf16x8*>(buf + rd_w + a * 1024);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) hb[b] = *reinterpret_cast<const bf16x8*>(buf + rd_h + b * 1024);
-    };
-    auto multiply = [&]() {
+    bf16x8 wa0[4], hb0[4], wa1[4], hb1[4];
+    auto multiply = [&](const bf16x8 (&wa)[4], const bf16x8 (&hb)[4]) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[a], hb[b], acc[a][b], 0, 0, 0);
     };
 
-    // ---- prologue: k-steps 0..2 in flight.  Exactly three k-steps are always
-    // in flight (past the end the last one is copied again into a slot that is
-    // never read), so every wait below is the same unconditional vmcnt(8)
+    // ---- prologue: two k-steps in flight.  Exactly two are always in flight
+    // (past the end the last one is copied again into a slot that is never
+    // read), so every wait below is the same unconditional one
     issue(0, st0);
     issue(min(1, nk - 1), st1);
-    issue(min(2, nk - 1), st2);
-    // ---- four k-steps per trip so that every ring slot is a distinct LDS
-    // object at each use; the first trip is peeled so that the copies in
-    // flight at the loop head are in the same order on every path (the
-    // compiler then sees that a slot's operands do not wait on later refills)
     auto trip = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < RP_NST; ++u) {
             const int ks = k0 + u;
             if (ks < nk) {
-                rp_wait_vm<8>();  // this wave's copies of ks landed (ks+1, ks+2 may fly)
-                rp_barrier();     // every wave's copies of ks landed; slot of ks-1 free
-                // operands first: the refill issued next cannot alias them
-                read_ops(u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3);
-                issue(min(ks + 3, nk - 1), u == 0 ? st3 : u == 1 ? st0 : u == 2 ? st1 : st2);
-                multiply();
+                uint8_t* cur = u == 0 ? st0 : u == 1 ? st1 : st2;
+                rp_wait_vm<RP_NJ>();  // this wave's copies of ks landed (ks + 1 may fly)
+                rp_barrier();         // every wave's copies of ks landed; slot of ks - 1 free
+                issue(min(ks + 2, nk - 1), u == 0 ? st2 : u == 1 ? st0 : st1);
+                const uint32_t base = lds_addr(cur);
+                read_operands(base + rw + ch0, base + rh + ch0, wa0, hb0);
+                multiply(wa0, hb0);
+                read_operands(base + rw + ch1, base + rh + ch1, wa1, hb1);
+                multiply(wa1, hb1);
             }
         }
     };
-    trip(0);
-    for (int k0 = RP_NST; k0 < nk; k0 += RP_NST) trip(k0);
+    for (int k0 = 0; k0 < nk; k0 += RP_NST) trip(k0);
     rp_wait_vm<0>();  // no copy may land in LDS after the workgroup ends
 
     // ---- epilogue: acc[a][b][i] = C^T[n0 + 64wn + 16a + 4g + i][m0 + 64wm + 16b + c16]
@@ -192,7 +226,7 @@ extern "C" csa2_status csa2_swa_replay(const csa2_replay_args* a, hipStream_t st
     CSA2_ARG(a != nullptr, "swa_replay: null args");
     CSA2_ARG(a->B >= 0 && a->n >= 0, "swa_replay: B=%d n=%d must be >= 0", a->B, a->n);
     CSA2_ARG(a->T > 0 && a->n <= a->T, "swa_replay: n=%d must be in [0, T=%d]", a->n, a->T);
-    CSA2_ARG(a->d_model > 0 && a->d_model % 32 == 0, "swa_replay: d_model=%d must be a positive multiple of 32",
+    CSA2_ARG(a->d_model > 0 && a->d_model % 64 == 0, "swa_replay: d_model=%d must be a positive multiple of 64",
              a->d_model);
     CSA2_ARG(a->D > 0 && a->D % 16 == 0, "swa_replay: D=%d must be a positive multiple of 16", a->D);
     CSA2_ARG(a->n_layers >= 0 && a->n_layers <= RP_MAX_LAYERS, "swa_replay: n_layers=%d out of [0, %d]", a->n_layers,
@@ -216,11 +250,11 @@ extern "C" csa2_status csa2_swa_replay(const csa2_replay_args* a, hipStream_t st
     p.D = a->D;
     p.T = a->T;
     p.t_end = a->t_end;
-    p.n_tiles = (a->D + RP_TILE - 1) / RP_TILE;
-    p.m_tiles = (int32_t)((M + RP_TILE - 1) / RP_TILE);
+    p.n_tiles = (a->D + RP_TN - 1) / RP_TN;
+    p.m_tiles = (int32_t)((M + RP_TM - 1) / RP_TM);
     p.n_layers = a->n_layers;
     const int64_t G = (int64_t)p.n_tiles * p.m_tiles * p.n_layers;
     CSA2_ARG(G <= INT32_MAX, "swa_replay: %lld tiles", (long long)G);
-    swa_replay_kernel<<<(unsigned)G, 256, 0, stream>>>(p);
+    swa_replay_kernel<<<(unsigned)G, 64 * RP_WAVES, 0, stream>>>(p);
     return launch_status("swa_replay");
 }

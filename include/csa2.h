@@ -154,7 +154,7 @@ csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t stream);
  *   W      [n_layers] host array of device [D][d_model] bf16 (output-major)
  *   swa_kv [n_layers] host array of device [B][T][D] bf16 rings (written)
  *   t_end  [B] device int32
- * 0 <= n <= T; d_model % 32 == 0; D % 16 == 0; 0 <= n_layers <= 48; h and W
+ * 0 <= n <= T; d_model % 64 == 0; D % 16 == 0; 0 <= n_layers <= 48; h and W
  * 16-byte aligned, swa_kv 8-byte aligned.  B*n == 0 or n_layers == 0: no-op. */
 typedef struct csa2_replay_args {
     int32_t B;

@@ -131,7 +131,7 @@ def test_replay_and_append_argument_errors(lib):
     arr = (_lib.P * 1)(FAKE.value)
     a = _lib.ReplayArgs(2, 8, 100, 512, 128, FAKE.value, 1, arr, arr, arr)  # d_model not a multiple of 32
     assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_EINVAL
-    assert "multiple of 32" in _err(lib)
+    assert "multiple of 64" in _err(lib)
     a = _lib.ReplayArgs(2, 200, 128, 512, 128, FAKE.value, 1, arr, arr, arr)  # n > T
     assert lib.csa2_swa_replay(ctypes.byref(a), None) == _lib.CSA2_EINVAL
     a = _lib.ReplayArgs(2, 8, 128, 500, 128, FAKE.value, 1, arr, arr, arr)  # D not a multiple of 16

@@ -72,7 +72,7 @@ def _run(h, W, t_end, T, D):
 @pytest.mark.parametrize("L,B,n,dm,D,T,t_end", [
     (3, 2, 37, 256, 192, 128, [36, 500]),       # ragged tokens and columns; start at 0 and wrapped
     (2, 3, 128, 128, 512, 128, [127, 1000, 4095]),  # a full window, every ring row rewritten
-    (1, 5, 1, 96, 16, 4, [0, 1, 2, 3, 9]),      # one token (a decode step's projection), tiny ring
+    (1, 5, 1, 128, 16, 4, [0, 1, 2, 3, 9]),      # one token (a decode step's projection), tiny ring
     (2, 1, 10, 64, 32, 16, [5]),                 # tokens before position 0 are skipped
 ])
 def test_replay_matches_oracle(L, B, n, dm, D, T, t_end):
