@@ -119,6 +119,15 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     const int b = r / p.Q;
     const int64_t nv = min((int64_t)p.n_vis[r], p.kmap.capacity);
 
+    // the first block's row lookups and loads go out before the query sum:
+    // neither depends on it, so their round trips overlap
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+    int64_t blk = (int64_t)blockIdx.x * WAVES + w;
+    const int64_t nbv = REINDEX ? p.blocks_per_row : (min(nv, p.n_pos) + EPB - 1) / EPB;
+    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
+    uint4 v[CH];
+    if (blk < nbv) load_block<DI, REINDEX, CONTIG>(p, r, b, nv, blk, lane, row_next, v);
+
     // qbar_c = sum over heads, ascending, fp32
     if (t < DI) {
         const uint16_t* qr = p.q_idx + (int64_t)r * p.H_i * DI + t;
@@ -132,17 +141,11 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
         for (int i = t; i < NBINS1; i += WAVES * 64) (&hist_s[0][0])[i] = 0u;
     __syncthreads();
 
-    const int64_t stride = (int64_t)gridDim.x * WAVES;
-    int64_t blk = (int64_t)blockIdx.x * WAVES + w;
     const int64_t nblocks8 = (p.n_pos + 7) / 8;
     uint4* my = tile[w];
     uint32_t n_valid = 0, n_valid_b = 0;  // lane counts for the histograms
 
-    // Full mode: only blocks holding a visible entry are read
-    const int64_t nbv = REINDEX ? p.blocks_per_row : (min(nv, p.n_pos) + EPB - 1) / EPB;
-    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
-    uint4 v[CH];
-    if (blk < nbv) load_block<DI, REINDEX, CONTIG>(p, r, b, nv, blk, lane, row_next, v);
+    // (Full mode: only blocks holding a visible entry are read)
     for (; blk < nbv; blk += stride) {
         const int64_t pos = blk * EPB + lane;
         const bool valid = CONTIG ? (pos < nv && pos < p.n_pos) : (row_next != NOROW);
@@ -268,6 +271,20 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
     const int q0 = (blockIdx.y % gps) * RB;
     const int nr = min(RB, p.Q - q0);
     const int r0 = b * p.Q + q0;
+    int64_t nvr[RB];
+    int64_t nvmax = 0;
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+        nvr[rr] = rr < nr ? min((int64_t)p.n_vis[r0 + rr], p.kmap.capacity) : 0;
+        nvmax = max(nvmax, nvr[rr]);
+    }
+    // the first block's loads go out before the query sums
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+    int64_t blk = (int64_t)blockIdx.x * WAVES + w;
+    const int64_t nbv = (min(nvmax, p.n_pos) + EPB - 1) / EPB;
+    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<false>(p, r0, b, nvmax, blk * EPB + lane);
+    uint4 v[CH];
+    if (blk < nbv) load_block<DI, false, CONTIG>(p, r0, b, nvmax, blk, lane, row_next, v);
 
     for (int i = t; i < RB * DI; i += WAVES * 64) {
         const int rr = i / DI, c = i % DI;
@@ -278,23 +295,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
         }
         reinterpret_cast<float*>(qbar_s[rr])[c] = acc;
     }
-    int64_t nvr[RB];
-    int64_t nvmax = 0;
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-        nvr[rr] = rr < nr ? min((int64_t)p.n_vis[r0 + rr], p.kmap.capacity) : 0;
-        nvmax = max(nvmax, nvr[rr]);
-    }
     __syncthreads();
 
-    const int64_t stride = (int64_t)gridDim.x * WAVES;
-    int64_t blk = (int64_t)blockIdx.x * WAVES + w;
     const int64_t nblocks8 = (p.n_pos + 7) / 8;
-    const int64_t nbv = (min(nvmax, p.n_pos) + EPB - 1) / EPB;
     uint4* my = tile[w];
-    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<false>(p, r0, b, nvmax, blk * EPB + lane);
-    uint4 v[CH];
-    if (blk < nbv) load_block<DI, false, CONTIG>(p, r0, b, nvmax, blk, lane, row_next, v);
     for (; blk < nbv; blk += stride) {
         const int64_t pos = blk * EPB + lane;
         int z;

@@ -246,17 +246,18 @@ __device__ void emit_sorted(const int* sel, int total, int n, int k, SelectLds& 
 // Small path.
 //
 // A lower bound T on the k-th largest key first limits the selection to few
-// candidates: every thread's largest key m_t is one of its elements, so if at
-// least ceil(k/16) threads of each of the 16 waves have m_t >= T, at least k
+// keys: every thread's largest key m_t is one of its elements, so if at least
+// ceil(k/16) threads of each of the 16 waves have m_t >= T, at least k
 // elements are >= T.  T = the smallest over the waves of the wave's
-// ceil(k/16)-th largest m_t (found bit by bit with ballots).  Elements with
-// key >= T are appended to LDS (one atomic per wave) and the radix select runs
-// over them alone, which avoids the contended 16-per-thread histogram of the
-// whole row; the result is identical because every selected element is >= T.
-// If T cannot be formed (k > 1024) or the candidates overflow, the select runs
-// over all elements.
-constexpr int SCAP = 4096;                  // candidates held in LDS
-constexpr int E_SC = SCAP / WG;             // candidates per thread in the select (4)
+// ceil(k/16)-th largest m_t (found bit by bit with ballots).  The keys in
+// [T, kmax] then go into one 2048-bin histogram of (key - T) >> shift (shift
+// chosen so that the range fits); the bin holding the k-th largest is found
+// by a prefix sum, and the few keys in that bin are ranked among themselves by
+// their composite (key, ~position) to give the exact threshold composite.
+// Every selected element is >= T, so the result is that of a full radix
+// select.  If T cannot be formed (k > 1024) or the threshold bin holds more
+// than 64 keys (long runs of equal scores), a radix select over all keys runs.
+constexpr int TIE_CAP = 64;                 // keys of the threshold bin ranked directly
 
 __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict__ scores, int n, int k,
                                                         const int32_t* __restrict__ pool,
@@ -264,9 +265,10 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
                                                         int lim_div) {
     __shared__ SelectLds sh;
     __shared__ int32_t pool_s[TOPK_SMALL_N / 8];  // the row's pool blocks (position -> entry map)
-    __shared__ uint32_t c_key[SCAP], c_pos[SCAP];
-    __shared__ uint32_t wave_t[NW];
-    __shared__ uint32_t counts;
+    __shared__ uint32_t tie_key[TIE_CAP], tie_pos[TIE_CAP];
+    __shared__ uint32_t wave_t[NW], wave_m[NW];
+    __shared__ uint32_t counts, tie_n;
+    __shared__ uint64_t cstar_s;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * (int64_t)n;
@@ -276,7 +278,10 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     if (pool)
         for (int i = t; i < nblk; i += WG) pool_s[i] = pool[row * nblk + i];
     for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
-    if (t == 0) counts = 0u;
+    if (t == 0) {
+        counts = 0u;
+        tie_n = 0u;
+    }
     uint32_t key[E_SMALL];
     // thread t owns positions 16t..16t+15 (ordered output); read them as four
     // 16-byte loads when the row is 16-byte aligned (strided scalar loads
@@ -298,86 +303,111 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
             key[e] = i < nl ? key32(s[i]) : 0u;
         }
     }
-    // ---- the bound T
+    // ---- the bound T, the largest key and the number of valid keys
     const int c = (k + NW - 1) / NW;
-    uint32_t T = 0u;
-    if (c <= 64) {
-        uint32_t m = 0u;
+    uint32_t mt = 0u, nv = 0u;
 #pragma unroll
-        for (int e = 0; e < E_SMALL; ++e) m = max(m, key[e]);
-        uint32_t v = 0u;  // largest V with #{lanes: m >= V} >= c
+    for (int e = 0; e < E_SMALL; ++e) {
+        mt = max(mt, key[e]);
+        nv += key[e] != 0u;
+    }
+    if (c <= 64) {
+        uint32_t v = 0u;  // largest V with #{lanes: mt >= V} >= c
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = v | (1u << bit);
-            if (__popcll(__ballot(m >= cand)) >= (uint32_t)c) v = cand;
+            if (__popcll(__ballot(mt >= cand)) >= (uint32_t)c) v = cand;
         }
         if (lane == 0) wave_t[wid] = v;
     }
-    __syncthreads();  // also publishes pool_s, the zeroed hist and counts
+    uint32_t wm = mt;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        wm = max(wm, (uint32_t)__shfl_xor((int)wm, off));
+        nv += (uint32_t)__shfl_xor((int)nv, off);
+    }
+    if (lane == 0) {
+        wave_m[wid] = wm;
+        atomicAdd(&counts, nv);
+    }
+    __syncthreads();  // also publishes pool_s and the zeroed histogram
+    const uint32_t valid = counts;
+    const bool all = valid <= (uint32_t)k;
+    uint32_t T = 0u, kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) kmax = max(kmax, wave_m[w]);
     if (c <= 64) {
         T = wave_t[0];
 #pragma unroll
         for (int w = 1; w < NW; ++w) T = min(T, wave_t[w]);
     }
-    // ---- count valid keys and append the candidates (key >= T) to LDS:
-    // valid count in the low half, candidates in the high half (each <= 16384)
-    uint32_t fc = 0;
-    uint32_t nv = 0;
+    // (a wave without valid keys gives T = 0; then every valid key, at least
+    // k + 1 of them, is >= 1)
+    bool fast = !all && c <= 64;
+    if (T == 0u) T = 1u;
+    uint32_t sft = 0, d = 0, need = 0, mb = 0;
+    uint64_t cstar = 0;
+    if (fast) {
+        // ---- one histogram of the keys >= T over their range
+        const uint32_t span = kmax - T;
+        const int bits = span ? 32 - __clz((int)span) : 0;
+        sft = bits > 11 ? (uint32_t)(bits - 11) : 0u;
 #pragma unroll
-    for (int e = 0; e < E_SMALL; ++e) {
-        nv += key[e] != 0u;
-        fc |= (uint32_t)(key[e] != 0u && key[e] >= T) << e;
-    }
-    const uint32_t mine = nv | ((uint32_t)__popc(fc) << 16);
-    uint32_t incl = mine;
+        for (int e = 0; e < E_SMALL; ++e)
+            if (key[e] >= T) atomicAdd(&sh.hist[0][(key[e] - T) >> sft], 1u);
+        __syncthreads();
+        find_bin(sh.hist[0], sh, NBINS1, (uint32_t)k);
+        d = sh.bin;
+        need = (uint32_t)k - sh.above;
+        mb = sh.hist[0][d];
+        if (mb != need) {
+            if (mb <= (uint32_t)TIE_CAP) {
+                // rank the threshold bin's keys by composite: the need-th largest
+                // is the threshold
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    uint32_t wbase = 0u;
-    if (lane == 63) wbase = atomicAdd(&counts, incl);
-    wbase = __shfl(wbase, 63);
-    uint32_t at = (wbase >> 16) + ((incl - mine) >> 16);
-#pragma unroll
-    for (int e = 0; e < E_SMALL; ++e) {
-        if ((fc >> e) & 1u) {
-            if (at < (uint32_t)SCAP) {
-                c_key[at] = key[e];
-                c_pos[at] = (uint32_t)(t * E_SMALL + e);
+                for (int e = 0; e < E_SMALL; ++e)
+                    if (key[e] >= T && ((key[e] - T) >> sft) == d) {
+                        const uint32_t at = atomicAdd(&tie_n, 1u);
+                        tie_key[at] = key[e];
+                        tie_pos[at] = (uint32_t)(t * E_SMALL + e);
+                    }
+                __syncthreads();
+                if (t < (int)mb) {
+                    const uint64_t me = composite(tie_key[t], tie_pos[t]);
+                    uint32_t rank = 0;
+                    for (uint32_t j = 0; j < mb; ++j) rank += composite(tie_key[j], tie_pos[j]) > me;
+                    if (rank == need - 1u) cstar_s = me;
+                }
+                __syncthreads();
+                cstar = cstar_s;
+            } else {
+                fast = false;  // (block-uniform: mb comes from LDS)
             }
-            ++at;
         }
     }
-    __syncthreads();
-    const uint32_t valid = counts & 0xFFFFu, ncand = counts >> 16;
-    const bool all = valid <= (uint32_t)k;
-    const bool use_cand = !all && ncand <= (uint32_t)SCAP;
     uint64_t prefix = 0, mask = 0;
-    if (!all) {
-        if (use_cand) {
-            uint32_t ck[E_SC], cp[E_SC];
+    if (!all && !fast) {
+        __syncthreads();  // the histogram is reused by the radix select
+        for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
+        __syncthreads();
+        uint32_t pos[E_SMALL];
 #pragma unroll
-            for (int e = 0; e < E_SC; ++e) {
-                const int i = e * WG + t;
-                ck[e] = i < (int)ncand ? c_key[i] : 0u;
-                cp[e] = i < (int)ncand ? c_pos[i] : 0u;
-            }
-            select_regs<E_SC>(ck, cp, (uint32_t)k, 0, prefix, mask, sh);
-        } else {
-            uint32_t pos[E_SMALL];
-#pragma unroll
-            for (int e = 0; e < E_SMALL; ++e) pos[e] = (uint32_t)(t * E_SMALL + e);
-            select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
-        }
+        for (int e = 0; e < E_SMALL; ++e) pos[e] = (uint32_t)(t * E_SMALL + e);
+        select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
     }
-    // ---- selected: valid, (a candidate when the select ran over candidates),
-    // and above the radix boundary; written in position order
-    const uint32_t Tsel = use_cand ? T : 0u;
+    // ---- selected positions, written in position order
     uint32_t fs = 0;
 #pragma unroll
     for (int e = 0; e < E_SMALL; ++e) {
-        const bool ok = key[e] != 0u && key[e] >= Tsel &&
-                        (all || (composite(key[e], (uint32_t)(t * E_SMALL + e)) & mask) >= prefix);
+        bool ok;
+        if (all) {
+            ok = key[e] != 0u;
+        } else if (fast) {
+            const uint32_t b = (key[e] - T) >> sft;
+            ok = key[e] >= T &&
+                 (b > d || (b == d && (mb == need || composite(key[e], (uint32_t)(t * E_SMALL + e)) >= cstar)));
+        } else {
+            ok = key[e] != 0u && (composite(key[e], (uint32_t)(t * E_SMALL + e)) & mask) >= prefix;
+        }
         fs |= (uint32_t)ok << e;
     }
     uint32_t total;

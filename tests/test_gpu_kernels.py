@@ -205,6 +205,8 @@ def _topk_case(rows, n, k, kind, tag):
         s = inputs.normal((rows, n), tag).numpy() * 30
     elif kind == "ties":
         s = inputs.small_ints((rows, n), tag, -40, 40, dtype=torch.float32).numpy()
+    elif kind == "coarse":  # a few equal keys per value: short runs of ties at the threshold
+        s = np.round(inputs.normal((rows, n), tag).numpy() * 120) / 4
     else:  # "flat": one value everywhere -> the threshold bin overflows any candidate buffer
         s = np.full((rows, n), 1.5, np.float32)
         s[:, ::5] = 2.5
@@ -217,7 +219,11 @@ def _topk_case(rows, n, k, kind, tag):
 @pytest.mark.parametrize("rows,n,k,kind", [
     (3, 1, 512, "normal"), (4, 700, 512, "ties"), (2, 16384, 512, "normal"), (5, 16384, 2048, "ties"),
     (3, 16385, 512, "normal"), (4, 100000, 512, "ties"), (4, 100000, 1, "normal"), (2, 300000, 2048, "normal"),
-    (2, 70000, 512, "flat"), (1, 1 << 20, 512, "normal")])
+    (2, 70000, 512, "flat"), (1, 1 << 20, 512, "normal"),
+    # one-workgroup path: threshold bin resolved by ranking, by the radix fallback
+    # (long ties, k > 1024), k at the bound's limit, single key, short rows
+    (3, 16384, 512, "coarse"), (2, 16384, 512, "ties"), (2, 16384, 512, "flat"), (4, 16384, 1024, "normal"),
+    (4, 16384, 1025, "coarse"), (2, 16384, 1, "normal"), (3, 5000, 512, "coarse"), (2, 600, 512, "normal")])
 def test_topk_bit_exact(rows, n, k, kind):
     s = _topk_case(rows, n, k, kind, f"tk{rows}_{n}_{k}_{kind}")
     out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
