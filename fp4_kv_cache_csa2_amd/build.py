@@ -21,6 +21,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with AGPR accumulators the compiler
+    # copied attention's 128 output accumulators out and back on every
+    # key-chunk iteration (the rare rescale needs them in VALU registers)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
 ]
