@@ -246,7 +246,18 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     const int slot = p.Wp ? p.q_slot[row] : 0;
     const int wlo = max(0, slot - p.window + 1);
 
-    // ---- query loads first: they fly while the key rows are resolved
+    // ---- the index loads go first: they head the longest chain (index ->
+    // physical row -> copy -> dequantisation); the query loads follow and fly
+    // while the rows are resolved and the first copies are issued
+    const int nk = max(0, c_hi - c_lo) * CHUNK_KEYS;
+    constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + NT - 1) / NT;  // key rows per thread at most
+    int32_t kent[KR_IT];
+#pragma unroll
+    for (int j = 0; j < KR_IT; ++j) {
+        const int i = tid + j * NT;
+        const int kpos = c_lo * CHUNK_KEYS + i;
+        kent[j] = (i < nk && kpos < p.K) ? p.idx[row * p.K + kpos] : -1;
+    }
     float qf[QF32 ? NBLK : 1][8];
     uint4 qraw[QF32 ? 1 : NBLK];
     if (QF32) {
@@ -265,25 +276,23 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     }
 
     // ---- physical rows of every key of this split (-1: none)
-    const int nk = max(0, c_hi - c_lo) * CHUNK_KEYS;
-    for (int i = tid; i < nk; i += NT) {
+#pragma unroll
+    for (int j = 0; j < KR_IT; ++j) {
+        const int i = tid + j * NT;
+        if (i >= nk) break;
         const int kpos = c_lo * CHUNK_KEYS + i;
         int64_t r = -1;
         if (kpos < p.Kp) {
-            if (kpos < p.K) {
-                const int32_t e = p.idx[row * p.K + kpos];
-                if (e >= 0) r = phys_row(p.kvmap, b, e);
-            }
+            if (kent[j] >= 0) r = phys_row(p.kvmap, b, kent[j]);
         } else {
             const int t = wlo + (kpos - p.Kp);
             if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
         }
         krow[i] = r;
     }
-    // the query and index loads are complete before the copies start (keeps the
-    // copy count the only thing on this wave's vmcnt)
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    __syncthreads();
+    // LDS barrier only: the query loads stay in flight (each chunk's wait
+    // below is for all of this wave's loads, so they are complete before S)
+    lds_barrier();
 
     // ---- raw bytes of the first RING chunks start flowing into the LDS ring
     const int c_pre = min(c_hi, c_lo + RING);
