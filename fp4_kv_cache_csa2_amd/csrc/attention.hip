@@ -93,6 +93,9 @@ constexpr int VT_DT = 16 * 32 + 2 * 16;  // bytes per 16 rows
 
 constexpr int MAX_CPS = 64;  // chunks per split (keys per workgroup <= 1024)
 constexpr int RING = 4;      // chunks whose raw bytes are in flight / staged in LDS at once
+// (many rows, no key split: a 2-chunk ring lets two workgroups share a CU,
+// so one's dequantisation and barriers overlap the other's MFMAs)
+constexpr int RING_WIDE = 2;
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
@@ -218,8 +221,8 @@ __device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, 
     }
 }
 
-template <int D, bool QF32, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
+template <int D, bool QF32, int NW, int RG = RING>
+__global__ __launch_bounds__(64 * NW, RG == RING ? 1 : 2) void attn_kernel(AttnParams p) {
     constexpr int NBLK = D / 32;  // 32-channel blocks of the S MFMA
     constexpr int NDT = D / 16;   // 16-channel tiles of the O MFMA
     constexpr int CPR = D / 8;    // 16-byte chunks per fp16 key row
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     using S = Stage<D>;
     __shared__ uint4 ktile[CHUNK_KEYS * (CPR + 1)];
     __shared__ __attribute__((aligned(16))) uint8_t vtile[D * 32 + (D / 8) * 16];
-    __shared__ __attribute__((aligned(16))) uint8_t ring[RING * S::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[RG * S::SLOT];
     __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
 
     const int tid = threadIdx.x;
@@ -294,10 +297,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     // below is for all of this wave's loads, so they are complete before S)
     lds_barrier();
 
-    // ---- raw bytes of the first RING chunks start flowing into the LDS ring
-    const int c_pre = min(c_hi, c_lo + RING);
+    // ---- raw bytes of the first RG chunks start flowing into the LDS ring
+    const int c_pre = min(c_hi, c_lo + RG);
     for (int ch = c_lo; ch < c_pre; ++ch)
-        stage_chunk<D, NW>(p, ch < n_sp_chunks, krow + (ch - c_lo) * CHUNK_KEYS, ring + ((ch - c_lo) % RING) * S::SLOT,
+        stage_chunk<D, NW>(p, ch < n_sp_chunks, krow + (ch - c_lo) * CHUNK_KEYS, ring + ((ch - c_lo) % RG) * S::SLOT,
                            w, lane);
 
     // ---- Q operand (B of S^T = K Q^T): Q[head][32*blk + 8g .. +8] in fp16,
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     for (int ch = c_lo; ch < c_hi; ++ch) {
         const bool sparse = ch < n_sp_chunks;
         const int64_t* kr = krow + (ch - c_lo) * CHUNK_KEYS;
-        const uint8_t* st = ring + ((ch - c_lo) % RING) * S::SLOT;
+        const uint8_t* st = ring + ((ch - c_lo) % RG) * S::SLOT;
         // ---- the chunk's copies have landed (all of this wave's copies: the
         // compiler cannot tell ring slots apart and would wait for them anyway)
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -376,10 +379,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
             }
         }
         lds_barrier();
-        // ---- the ring slot is free again: refill it with chunk ch + RING
+        // ---- the ring slot is free again: refill it with chunk ch + RG
         if (c_issued < c_hi) {
             stage_chunk<D, NW>(p, c_issued < n_sp_chunks, krow + (c_issued - c_lo) * CHUNK_KEYS,
-                               ring + ((c_issued - c_lo) % RING) * S::SLOT, w, lane);
+                               ring + ((c_issued - c_lo) % RG) * S::SLOT, w, lane);
             ++c_issued;
         }
         // ---- S^T[key][head] = sum_d K[key][d] Q[head][d]
@@ -659,8 +662,15 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     const dim3 block((unsigned)(4 * H));
     const bool f32 = qt == CSA2_F32;
     const int nw = H / 16;
+    const bool wide = p.nsplit == 1 && rows >= 512 && D == 512 && nw == 4;
+    if (wide) {
+        if (f32)
+            attn_kernel<512, true, 4, RING_WIDE><<<grid, block, 0, stream>>>(p);
+        else
+            attn_kernel<512, false, 4, RING_WIDE><<<grid, block, 0, stream>>>(p);
+    }
 #define CSA2_ATTN_NW(DD, F, NWV) \
-    if (nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
+    if (!wide && nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
 #define CSA2_ATTN(DD)                                                                                   \
     if (D == DD) {                                                                                      \
         if (f32) {                                                                                      \
