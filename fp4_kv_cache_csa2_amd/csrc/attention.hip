@@ -22,7 +22,9 @@
 // a lazy maximum: the running maximum moves (and O is rescaled) only when a
 // chunk exceeds it by more than 2^8, so P <= 256 stays well inside fp16.  Few
 // rows (decode) split the keys over several workgroups whose normalised
-// partials (o, lse) are merged by a second kernel.
+// partials (o, lse) are merged by a second kernel; many rows without a split
+// (prefill) at D = 512, H = 64 take a producer/consumer variant
+// (attn_pc_kernel) in which four waves dequantise while four multiply.
 #include "internal.h"
 
 namespace csa2 {
@@ -84,18 +86,29 @@ __device__ __forceinline__ void fp4x8_to_f16(uint32_t w, uint32_t sc2, uint32_t 
     }
 }
 
-// byte offset of V^T[d][key 4kq] inside the padded transposed tile (rows of
-// 16 keys x fp16 = 32 B, plus 16 B after every 8 rows against bank conflicts)
-__device__ __forceinline__ int vt_off(int d, int kq) { return d * 32 + (d >> 3) * 16 + kq * 8; }
+// LDS layouts of the two fp16 tiles, chosen against bank conflicts (measured
+// on gfx950: 64 banks of 4 bytes; a 64-bit access serves lanes 0-31 and 32-63
+// in one pass each, a 128-bit access lanes {0-7, 24-31}, {8-15, 16-23},
+// {32-39, 56-63}, {40-47, 48-55}).
+// K tile: row k of D fp16 at k (D/8 + 2) 16 bytes (32 bytes of padding per
+// row), read by lane (cz, gz) at row cz, 16-byte chunk 4j + gz, written by
+// lane co at chunk co of one row: conflict-free both ways.
+constexpr int KROW_PAD = 2;
+// V^T tile: byte offset of V^T[d][keys 4kq..4kq+3] (8 bytes): rows of 16 keys
+// x fp16 = 32 B, 16 B of padding after every 16 rows, and the four key groups
+// of a row swapped in pairs (kq ^ 3) when bit 3 of d is set.  Read by lane
+// (cz, gz) at row 16dt + cz, group gz (MFMA operand), written by lane co at
+// row 8co + e, one group (dequantisation): both conflict-free.
+__host__ __device__ constexpr int vt_off(int d, int kq) {
+    return d * 32 + (d >> 4) * 16 + ((kq ^ (3 * ((d >> 3) & 1))) * 8);
+}
 // the same for d = 16 dt + c16 (c16 < 16), split so that dt becomes an immediate offset
-__device__ __forceinline__ int vt_base(int c16, int kq) { return c16 * 32 + (c16 >> 3) * 16 + kq * 8; }
-constexpr int VT_DT = 16 * 32 + 2 * 16;  // bytes per 16 rows
+__device__ __forceinline__ int vt_base(int c16, int kq) { return vt_off(c16, kq); }
+constexpr int VT_DT = 16 * 32 + 16;  // bytes per 16 rows
+constexpr int VT_BYTES(int D) { return D * 32 + (D / 16) * 16; }
 
 constexpr int MAX_CPS = 64;  // chunks per split (keys per workgroup <= 1024)
 constexpr int RING = 4;      // chunks whose raw bytes are in flight / staged in LDS at once
-// (many rows, no key split: a 2-chunk ring lets two workgroups share a CU,
-// so one's dequantisation and barriers overlap the other's MFMAs)
-constexpr int RING_WIDE = 2;
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
@@ -136,77 +149,116 @@ struct Stage {
     static constexpr int N_WIN = D / 32;
 };
 
-// A key without a row copies row 0 instead: its values are finite and its
-// softmax weight is exactly 0, so it adds nothing.
+// Copies of one chunk in two steps: the rows each lane copies are read from
+// the workgroup's row list first (chunk_rows), the copies are issued later
+// (chunk_issue), so that no copy waits for its own LDS read.  A key without a
+// row copies row 0 instead: its values are finite and its softmax weight is
+// exactly 0, so it adds nothing.
 template <int D, int NW>
-__device__ __forceinline__ void stage_chunk(const AttnParams& p, bool sparse, const int64_t* kr, uint8_t* slot, int w,
-                                            int lane) {
+struct ChunkRows {
     using S = Stage<D>;
+    static constexpr int NC = (S::N_CODE + NW - 1) / NW;  // code copies per wave
+    static constexpr int NWN = (S::N_WIN + NW - 1) / NW;  // window copies per wave
+    static constexpr int N = NC + S::N_SCALE > NWN ? NC + S::N_SCALE : NWN;
+    int64_t r[N];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void chunk_rows(bool sparse, const int64_t* kr, int w, int lane, ChunkRows<D, NW>& cr) {
+    using S = Stage<D>;
+    using C = ChunkRows<D, NW>;
     if (sparse) {
         constexpr int PPK = D / 32;  // 16-byte pieces per code row
 #pragma unroll
-        for (int jj = 0; jj < (S::N_CODE + NW - 1) / NW; ++jj) {
+        for (int jj = 0; jj < C::NC; ++jj) {
             const int j = jj * NW + w;
             if (j >= S::N_CODE) break;
-            const int piece = j * 64 + lane;
-            const int64_t r = max(kr[piece / PPK], (int64_t)0);
-            dma16_to_lds(p.codes + r * (D / 2) + (piece % PPK) * 16, slot + j * 1024);
+            cr.r[jj] = kr[(j * 64 + lane) / PPK];
         }
         constexpr int DPK = D / 64;  // 4-byte pieces per scale row
 #pragma unroll
         for (int k = 0; k < S::N_SCALE; ++k) {
             if ((S::N_CODE + k) % NW != w) continue;
             const int piece = k * 64 + lane;  // lanes past the 16 rows land in the slot's unused tail
-            const int64_t r = piece < CHUNK_KEYS * DPK ? max(kr[piece / DPK], (int64_t)0) : 0;
-            dma4_to_lds(p.scales + r * (D / 16) + (piece % DPK) * 4, slot + S::SCALE_OFF + k * 256);
+            cr.r[C::NC + k] = piece < CHUNK_KEYS * DPK ? kr[piece / DPK] : 0;
         }
     } else {
         constexpr int PPK = D / 8;  // 16-byte pieces per bf16 row
 #pragma unroll
-        for (int jj = 0; jj < (S::N_WIN + NW - 1) / NW; ++jj) {
+        for (int jj = 0; jj < C::NWN; ++jj) {
             const int j = jj * NW + w;
             if (j >= S::N_WIN) break;
-            const int piece = j * 64 + lane;
-            const int64_t r = max(kr[piece / PPK], (int64_t)0);
-            dma16_to_lds(reinterpret_cast<const uint8_t*>(p.swa) + r * (2 * D) + (piece % PPK) * 16,
-                           slot + j * 1024);
+            cr.r[jj] = kr[(j * 64 + lane) / PPK];
         }
     }
 }
 
-// Dequantise one item (4 keys x 8 channels) from a staged chunk into the K tile
-// (fp16, rows of D + 8 halves: the pad spreads the 16 rows of an MFMA operand
-// read over all banks) and the V^T tile (fp16, transposed, padded).  Keys
-// without a row hold row 0's finite values; their softmax weight is exactly 0.
-// Window rows are bf16; their fp16 conversion is exact for 2^-14 <= |v| < 65504.
-template <int D, bool SPARSE>
-__device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, uint4* ktile, uint8_t* vtile) {
-    constexpr int KROW = D / 8 + 1;  // uint4 per K-tile row
-    uint32_t kh[4][4];               // fp16 pairs: [key][channel pair]
-    if (SPARSE) {
-        uint32_t cw[4], sb[4];
+template <int D, int NW>
+__device__ __forceinline__ void chunk_issue(const AttnParams& p, bool sparse, const ChunkRows<D, NW>& cr,
+                                            uint8_t* slot, int w, int lane) {
+    using S = Stage<D>;
+    using C = ChunkRows<D, NW>;
+    // An opaque zero, fresh every call: the per-lane byte offsets are
+    // recomputed here instead of being kept (hoisted out of the chunk loop) as
+    // 64-bit addresses, which spill; a spill reload waits for every copy in
+    // flight, the ring's prefetch included.
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    const int lz = lane + z;
+    if (sparse) {
+        constexpr int PPK = D / 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = 4 * kq + i;
-            cw[i] = *reinterpret_cast<const uint32_t*>(slot + key * (D / 2) + co * 4);
-            sb[i] = slot[Stage<D>::SCALE_OFF + key * (D / 16) + (co >> 1)];
+        for (int jj = 0; jj < C::NC; ++jj) {
+            const int j = jj * NW + w;
+            if (j >= S::N_CODE) break;
+            const int64_t r = max(cr.r[jj], (int64_t)0);
+            dma16_to_lds(p.codes + r * (D / 2) + ((j * 64 + lz) % PPK) * 16, slot + j * 1024);
         }
+        constexpr int DPK = D / 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fp4x8_to_f16(cw[i], e4m3_f16x2_over256(sb[i]), kh[i]);
+        for (int k = 0; k < S::N_SCALE; ++k) {
+            if ((S::N_CODE + k) % NW != w) continue;
+            const int64_t r = max(cr.r[C::NC + k], (int64_t)0);
+            dma4_to_lds(p.scales + r * (D / 16) + ((k * 64 + lz) % DPK) * 4, slot + S::SCALE_OFF + k * 256);
+        }
     } else {
-        uint4 u[4];
+        constexpr int PPK = D / 8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const uint4*>(slot + (4 * kq + i) * (2 * D) + co * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t wv[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f16x2 v = f16x2{(_Float16)bf16_lo(wv[e]), (_Float16)bf16_hi(wv[e])};
-                kh[i][e] = *reinterpret_cast<const uint32_t*>(&v);
-            }
+        for (int jj = 0; jj < C::NWN; ++jj) {
+            const int j = jj * NW + w;
+            if (j >= S::N_WIN) break;
+            const int64_t r = max(cr.r[jj], (int64_t)0);
+            dma16_to_lds(reinterpret_cast<const uint8_t*>(p.swa) + r * (2 * D) + ((j * 64 + lz) % PPK) * 16,
+                         slot + j * 1024);
         }
     }
+}
+
+// One dequantisation item: 4 keys x 8 channels as fp16 pairs kh[key][pair].
+// FP4: E2M1 values times the E4M3 scale (exact in fp16).  Window rows are
+// bf16; their fp16 conversion is exact for 2^-14 <= |v| < 65504.
+__device__ __forceinline__ void item_from_fp4(const uint32_t (&cw)[4], const uint32_t (&sb)[4], uint32_t (&kh)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fp4x8_to_f16(cw[i], e4m3_f16x2_over256(sb[i]), kh[i]);
+}
+__device__ __forceinline__ void item_from_bf16(const uint4 (&u)[4], uint32_t (&kh)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wv[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f16x2 v = f16x2{(_Float16)bf16_lo(wv[e]), (_Float16)bf16_hi(wv[e])};
+            kh[i][e] = *reinterpret_cast<const uint32_t*>(&v);
+        }
+    }
+}
+
+// Write one item (keys 4kq..4kq+3, channels 8co..8co+7) into the K tile (fp16,
+// rows of D + 8 halves: the pad spreads the 16 rows of an MFMA operand read
+// over all banks) and the V^T tile (fp16, transposed, padded).
+template <int D>
+__device__ __forceinline__ void put_item(const uint32_t (&kh)[4][4], int kq, int co, uint4* ktile, uint8_t* vtile) {
+    constexpr int KROW = D / 8 + KROW_PAD;  // uint4 per K-tile row
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         ktile[(4 * kq + i) * KROW + co] = make_uint4(kh[i][0], kh[i][1], kh[i][2], kh[i][3]);
@@ -221,16 +273,274 @@ __device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, 
     }
 }
 
-template <int D, bool QF32, int NW, int RG = RING>
-__global__ __launch_bounds__(64 * NW, RG == RING ? 1 : 2) void attn_kernel(AttnParams p) {
+// Dequantise one item from a staged chunk into the tiles.  Keys without a row
+// hold row 0's finite values; their softmax weight is exactly 0.
+template <int D, bool SPARSE>
+__device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, uint4* ktile, uint8_t* vtile) {
+    uint32_t kh[4][4];  // fp16 pairs: [key][channel pair]
+    if (SPARSE) {
+        uint32_t cw[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = 4 * kq + i;
+            cw[i] = *reinterpret_cast<const uint32_t*>(slot + key * (D / 2) + co * 4);
+            sb[i] = slot[Stage<D>::SCALE_OFF + key * (D / 16) + (co >> 1)];
+        }
+        item_from_fp4(cw, sb, kh);
+    } else {
+        uint4 u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const uint4*>(slot + (4 * kq + i) * (2 * D) + co * 16);
+        item_from_bf16(u, kh);
+    }
+    put_item<D>(kh, kq, co, ktile, vtile);
+}
+
+// max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// by two row swaps on the VALU, without an LDS round trip.  Every lane ends
+// with the same bits: each pairwise step is commutative.
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ uint32_t rows_umax(uint32_t x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)a[0], (uint32_t)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// Q operand (B of S^T = K Q^T) of one lane: Q[head][32 blk + 8g .. +8] in
+// fp16, pre-scaled by 2^-qs so that the head's largest element lies in
+// [2^14, 2^15); an fp32 query is split into hi + lo fp16 parts.  Returns the
+// logit scale sm_scale log2(e) 2^qs.
+template <int D, bool QF32>
+__device__ __forceinline__ float q_operand(const float (&qf)[QF32 ? D / 32 : 1][8], const uint4 (&qraw)[QF32 ? 1 : D / 32],
+                                          float scale_log2, f16x8 (&qhi)[D / 32], f16x8 (&qlo)[QF32 ? D / 32 : 1]) {
+    constexpr int NBLK = D / 32;
+    uint32_t qmax = 0;  // largest |q| as an fp32 bit pattern (monotone in |q|)
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+        if (QF32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qmax = max(qmax, __float_as_uint(qf[QF32 ? blk : 0][e]) & 0x7FFFFFFFu);
+        } else {
+            const uint4 u = qraw[QF32 ? 0 : blk];
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qmax = max(qmax, max((wv[e] << 16) & 0x7FFF0000u, wv[e] & 0x7FFF0000u));
+        }
+    }
+    qmax = rows_umax(qmax);
+    // 2^-qs maps the largest element into [2^14, 2^15)
+    const int qs = qmax == 0 ? 0 : min(113, max(-100, (int)(qmax >> 23) - 127 - 14));
+    const float qscale = __uint_as_float((uint32_t)(127 - qs) << 23);
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+        float x[8];
+        if (QF32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = qf[QF32 ? blk : 0][e] * qscale;
+        } else {
+            const uint4 u = qraw[QF32 ? 0 : blk];
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_lo(wv[e]) * qscale;
+                x[2 * e + 1] = bf16_hi(wv[e]) * qscale;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const _Float16 h = (_Float16)x[e];
+            qhi[blk][e] = h;
+            if (QF32) qlo[QF32 ? blk : 0][e] = (_Float16)(x[e] - (float)h);
+        }
+    }
+    return scale_log2 * __uint_as_float((uint32_t)(127 + qs) << 23);
+}
+
+// One 16-key chunk from the LDS tiles for the lane's head, in three steps:
+// S^T = K Q^T (attn_scores), online softmax in the log2 domain with a lazy
+// maximum (attn_weights), O^T += V^T P^T (attn_pv).  kr: the chunk's key rows
+// (-1: none); cz, gz: lane % 16 and lane / 16, recomputed by the caller every
+// chunk (so that no address lives across the chunk loop).
+template <int D, bool QF32>
+__device__ __forceinline__ f32x4 attn_scores(const uint4* ktile, int cz, int gz, const f16x8 (&qhi)[D / 32],
+                                             const f16x8 (&qlo)[QF32 ? D / 32 : 1]) {
+    constexpr int NBLK = D / 32, CPR = D / 8;
+    // S^T[key][head] = sum_d K[key][d] Q[head][d]: four accumulator chains (a
+    // dependent MFMA waits for three others); the operands of the next four
+    // blocks are read while these multiply
+    f32x4 sacc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 kop[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kop[0][j] = ktile[cz * (CPR + KROW_PAD) + 4 * j + gz];
+#pragma unroll
+    for (int grp = 0; grp < NBLK / 4; ++grp) {
+        if (grp + 1 < NBLK / 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                kop[(grp + 1) & 1][j] = ktile[cz * (CPR + KROW_PAD) + 4 * (4 * (grp + 1) + j) + gz];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f16x8 a = *reinterpret_cast<const f16x8*>(&kop[grp & 1][j]);
+            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[4 * grp + j], sacc[j], 0, 0, 0);
+            if (QF32) sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? 4 * grp + j : 0], sacc[j], 0, 0, 0);
+        }
+    }
+    return (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+}
+
+// Softmax weights of keys 4gz..4gz+3 (scores s), with the running maximum and
+// sum; rescales O when the maximum moves.  Returns P as the fp16 B operand.
+template <int NDT>
+__device__ __forceinline__ f16x4 attn_weights(const f32x4& s, const int64_t* kr, int gz, float zscale,
+                                              f32x4 (&oacc)[NDT], float& m_run, float& l_run) {
+    float z[4];
+    float mloc = -INFINITY;
+    int64_t kv4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kv4[i] = kr[4 * gz + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        z[i] = (kv4[i] >= 0) ? s[i] * zscale : -INFINITY;
+        mloc = fmaxf(mloc, z[i]);
+    }
+    mloc = rows_max(mloc);
+    // lazy maximum: move it only when this chunk exceeds it by more than 2^8
+    // (nothing to rescale while nothing has been accumulated)
+    float alpha = 1.0f;
+    if (mloc > m_run + 8.0f) {
+        if (l_run > 0.0f) alpha = exp2f(m_run - mloc);
+        m_run = mloc;
+    }
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+    float psum = 0.0f;
+    f16x4 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // z - m_run <= 8: the hardware exp2 needs no range reduction
+        const _Float16 h = (_Float16)((z[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_run));
+        psum += (float)h;  // normalise by the weights the MFMA actually applies
+        pb[i] = h;
+    }
+    l_run = l_run * alpha + rows_sum(psum);
+    return pb;
+}
+
+// O^T[d][head] += sum_key V^T[d][key] P^T[key][head]
+template <int D>
+__device__ __forceinline__ void attn_pv(const uint8_t* vtile, int cz, int gz, const f16x4& pb, f32x4 (&oacc)[D / 16]) {
+    constexpr int NDT = D / 16;
+    // operands read eight tiles ahead of the MFMAs that use them.  Four base
+    // addresses, one per tile index mod 4 (opaque to the compiler): reads from
+    // one base lie 4 tiles apart, beyond the reach of a paired 64-bit read, so
+    // each stays a single 64-bit read -- conflict-free in this layout, where a
+    // paired read of two neighbouring tiles would conflict two ways.
+    constexpr int PG = NDT < 8 ? NDT : 8;
+    const uint8_t* vbr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int zr;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zr));
+        vbr[r] = vtile + vt_base(cz, gz) + VT_DT * r + zr;
+    }
+    auto vread = [&](int t) { return *reinterpret_cast<const uint2*>(vbr[t & 3] + VT_DT * (t & ~3)); };
+    uint2 vop[2][PG];
+#pragma unroll
+    for (int j = 0; j < PG; ++j) vop[0][j] = vread(j);
+#pragma unroll
+    for (int grp = 0; grp < NDT / PG; ++grp) {
+        if (grp + 1 < NDT / PG) {
+#pragma unroll
+            for (int j = 0; j < PG; ++j) vop[(grp + 1) & 1][j] = vread(PG * (grp + 1) + j);
+        }
+#pragma unroll
+        for (int j = 0; j < PG; ++j) {
+            const f16x4 a = *reinterpret_cast<const f16x4*>(&vop[grp & 1][j]);
+            oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, oacc[PG * grp + j], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, bool QF32>
+__device__ __forceinline__ void attn_chunk(const uint4* ktile, const uint8_t* vtile, const int64_t* kr, int cz, int gz,
+                                           const f16x8 (&qhi)[D / 32], const f16x8 (&qlo)[QF32 ? D / 32 : 1],
+                                           float zscale, f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
+    const f32x4 s = attn_scores<D, QF32>(ktile, cz, gz, qhi, qlo);
+    const f16x4 pb = attn_weights<D / 16>(s, kr, gz, zscale, oacc, m_run, l_run);
+    attn_pv<D>(vtile, cz, gz, pb, oacc);
+}
+
+// Normalised output (o, lse) of one head's key set, merged with the (o, lse)
+// already in the output when p.merge is set.
+template <int D>
+__device__ __forceinline__ void attn_store(const AttnParams& p, int64_t row, int head, int g,
+                                           const f32x4 (&oacc)[D / 16], float m_run, float l_run) {
+    constexpr int NDT = D / 16;
+    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    const float lse_cur = (l_run > 0.0f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    float* orow = p.o + (row * p.H + head) * D;
+    float w_cur = 1.0f, w_old = 0.0f, lse_out = lse_cur;
+    if (p.merge) {
+        const float lse_old = p.lse[row * p.H + head];
+        const float L = fmaxf(lse_old, lse_cur);
+        if (L == -INFINITY) {
+            w_cur = 0.0f;
+            w_old = 0.0f;
+            lse_out = -INFINITY;
+        } else {
+            w_old = expf(lse_old - L);
+            w_cur = expf(lse_cur - L);
+            const float tot = w_old + w_cur;
+            w_old /= tot;
+            w_cur /= tot;
+            lse_out = L + logf(tot);
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        float4* dst = reinterpret_cast<float4*>(orow + 16 * dt + 4 * g);
+        float4 r = make_float4(oacc[dt][0] * inv * w_cur, oacc[dt][1] * inv * w_cur, oacc[dt][2] * inv * w_cur,
+                               oacc[dt][3] * inv * w_cur);
+        if (p.merge && w_old != 0.0f) {
+            const float4 old = *dst;
+            r.x += w_old * old.x;
+            r.y += w_old * old.y;
+            r.z += w_old * old.z;
+            r.w += w_old * old.w;
+        }
+        *dst = r;
+    }
+    if (g == 0) p.lse[row * p.H + head] = lse_out;
+}
+
+template <int D, bool QF32, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
+    constexpr int RG = RING;
     constexpr int NBLK = D / 32;  // 32-channel blocks of the S MFMA
     constexpr int NDT = D / 16;   // 16-channel tiles of the O MFMA
     constexpr int CPR = D / 8;    // 16-byte chunks per fp16 key row
     constexpr int NT = 64 * NW;
     constexpr int ITEMS = 4 * CPR;  // dequantisation items per chunk
     using S = Stage<D>;
-    __shared__ uint4 ktile[CHUNK_KEYS * (CPR + 1)];
-    __shared__ __attribute__((aligned(16))) uint8_t vtile[D * 32 + (D / 8) * 16];
+    __shared__ uint4 ktile[CHUNK_KEYS * (CPR + KROW_PAD)];
+    __shared__ __attribute__((aligned(16))) uint8_t vtile[VT_BYTES(D)];
     __shared__ __attribute__((aligned(16))) uint8_t ring[RG * S::SLOT];
     __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
 
@@ -299,55 +609,16 @@ __global__ __launch_bounds__(64 * NW, RG == RING ? 1 : 2) void attn_kernel(AttnP
 
     // ---- raw bytes of the first RG chunks start flowing into the LDS ring
     const int c_pre = min(c_hi, c_lo + RG);
-    for (int ch = c_lo; ch < c_pre; ++ch)
-        stage_chunk<D, NW>(p, ch < n_sp_chunks, krow + (ch - c_lo) * CHUNK_KEYS, ring + ((ch - c_lo) % RG) * S::SLOT,
-                           w, lane);
-
-    // ---- Q operand (B of S^T = K Q^T): Q[head][32*blk + 8g .. +8] in fp16,
-    // pre-scaled by 2^-qs; an fp32 query is split into hi + lo fp16 parts
-    uint32_t qmax = 0;  // largest |q| as an fp32 bit pattern (monotone in |q|)
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-        if (QF32) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qmax = max(qmax, __float_as_uint(qf[QF32 ? blk : 0][e]) & 0x7FFFFFFFu);
-        } else {
-            const uint4 u = qraw[QF32 ? 0 : blk];
-            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) qmax = max(qmax, max((wv[e] << 16) & 0x7FFF0000u, wv[e] & 0x7FFF0000u));
-        }
+    for (int ch = c_lo; ch < c_pre; ++ch) {
+        ChunkRows<D, NW> cr;
+        chunk_rows<D, NW>(ch < n_sp_chunks, krow + (ch - c_lo) * CHUNK_KEYS, w, lane, cr);
+        chunk_issue<D, NW>(p, ch < n_sp_chunks, cr, ring + ((ch - c_lo) % RG) * S::SLOT, w, lane);
     }
-    qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 16));
-    qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32));
-    // 2^-qs maps the largest element into [2^14, 2^15)
-    const int qs = qmax == 0 ? 0 : min(113, max(-100, (int)(qmax >> 23) - 127 - 14));
-    const float qscale = __uint_as_float((uint32_t)(127 - qs) << 23);
-    const float zscale = p.scale_log2 * __uint_as_float((uint32_t)(127 + qs) << 23);
+
+    // ---- Q operand in fp16 (pre-scaled by a power of two)
     f16x8 qhi[NBLK];
     f16x8 qlo[QF32 ? NBLK : 1];
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-        float x[8];
-        if (QF32) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = qf[QF32 ? blk : 0][e] * qscale;
-        } else {
-            const uint4 u = qraw[QF32 ? 0 : blk];
-            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[2 * e] = bf16_lo(wv[e]) * qscale;
-                x[2 * e + 1] = bf16_hi(wv[e]) * qscale;
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const _Float16 h = (_Float16)x[e];
-            qhi[blk][e] = h;
-            if (QF32) qlo[QF32 ? blk : 0][e] = (_Float16)(x[e] - (float)h);
-        }
-    }
+    const float zscale = q_operand<D, QF32>(qf, qraw, p.scale_log2, qhi, qlo);
 
     f32x4 oacc[NDT];
 #pragma unroll
@@ -355,11 +626,25 @@ __global__ __launch_bounds__(64 * NW, RG == RING ? 1 : 2) void attn_kernel(AttnP
     float m_run = -INFINITY, l_run = 0.0f;
 
     int c_issued = c_pre;  // chunks [c_lo, c_issued) have been issued
-    const int vb = vt_base(c16, g);
     for (int ch = c_lo; ch < c_hi; ++ch) {
+        // An opaque zero, fresh every chunk: the per-thread LDS addresses below
+        // are recomputed from it (a few ALU ops) instead of living across the
+        // loop in ~20 registers, which would spill next to the 128 output
+        // accumulators and 64 query registers (and every spill reload waits
+        // for all copies in flight, the ring's prefetch included).
+        int zz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+        const int tz = tid + zz;
+        const int lz = tz & 63, gz = lz >> 4, cz = lz & 15;
         const bool sparse = ch < n_sp_chunks;
         const int64_t* kr = krow + (ch - c_lo) * CHUNK_KEYS;
         const uint8_t* st = ring + ((ch - c_lo) % RG) * S::SLOT;
+        // ---- rows of the chunk the refill below copies, read now: they have
+        // arrived by the barriers, so the refill issues its copies at once
+        const bool refill = c_issued < c_hi;
+        const bool nsparse = c_issued < n_sp_chunks;
+        ChunkRows<D, NW> nr;
+        if (refill) chunk_rows<D, NW>(nsparse, krow + (c_issued - c_lo) * CHUNK_KEYS, w, lz, nr);
         // ---- the chunk's copies have landed (all of this wave's copies: the
         // compiler cannot tell ring slots apart and would wait for them anyway)
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -368,101 +653,23 @@ __global__ __launch_bounds__(64 * NW, RG == RING ? 1 : 2) void attn_kernel(AttnP
         if (sparse) {
 #pragma unroll
             for (int it = 0; it < (ITEMS + NT - 1) / NT; ++it) {
-                const int item = it * NT + tid;
+                const int item = it * NT + tz;
                 if (item < ITEMS) store_item<D, true>(st, item / CPR, item % CPR, ktile, vtile);
             }
         } else {
 #pragma unroll
             for (int it = 0; it < (ITEMS + NT - 1) / NT; ++it) {
-                const int item = it * NT + tid;
+                const int item = it * NT + tz;
                 if (item < ITEMS) store_item<D, false>(st, item / CPR, item % CPR, ktile, vtile);
             }
         }
         lds_barrier();
         // ---- the ring slot is free again: refill it with chunk ch + RG
-        if (c_issued < c_hi) {
-            stage_chunk<D, NW>(p, c_issued < n_sp_chunks, krow + (c_issued - c_lo) * CHUNK_KEYS,
-                               ring + ((c_issued - c_lo) % RG) * S::SLOT, w, lane);
+        if (refill) {
+            chunk_issue<D, NW>(p, nsparse, nr, ring + ((c_issued - c_lo) % RG) * S::SLOT, w, lz);
             ++c_issued;
         }
-        // ---- S^T[key][head] = sum_d K[key][d] Q[head][d]
-        // four accumulator chains (a dependent MFMA waits for three others);
-        // the operands of the next four blocks are read while these multiply
-        f32x4 sacc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        uint4 kop[2][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kop[0][j] = ktile[c16 * (CPR + 1) + 4 * j + g];
-#pragma unroll
-        for (int grp = 0; grp < NBLK / 4; ++grp) {
-            if (grp + 1 < NBLK / 4) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kop[(grp + 1) & 1][j] = ktile[c16 * (CPR + 1) + 4 * (4 * (grp + 1) + j) + g];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f16x8 a = *reinterpret_cast<const f16x8*>(&kop[grp & 1][j]);
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[4 * grp + j], sacc[j], 0, 0, 0);
-                if (QF32) sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlo[QF32 ? 4 * grp + j : 0], sacc[j], 0, 0, 0);
-            }
-        }
-        const f32x4 s = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
-        // ---- online softmax for head `head` over keys 4g..4g+3 of this chunk
-        float z[4];
-        float mloc = -INFINITY;
-        int64_t kv4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kv4[i] = kr[4 * g + i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = (kv4[i] >= 0) ? s[i] * zscale : -INFINITY;
-            mloc = fmaxf(mloc, z[i]);
-        }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        // lazy maximum: move it only when this chunk exceeds it by more than 2^8
-        // (nothing to rescale while nothing has been accumulated)
-        float alpha = 1.0f;
-        if (mloc > m_run + 8.0f) {
-            if (l_run > 0.0f) alpha = exp2f(m_run - mloc);
-            m_run = mloc;
-        }
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-        }
-        float psum = 0.0f;
-        f16x4 pb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // z - m_run <= 8: the hardware exp2 needs no range reduction
-            const _Float16 h = (_Float16)((z[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_run));
-            psum += (float)h;  // normalise by the weights the MFMA actually applies
-            pb[i] = h;
-        }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        // ---- O^T[d][head] += sum_key V^T[d][key] P^T[key][head]
-        // operands read eight tiles ahead of the MFMAs that use them
-        constexpr int PG = NDT < 8 ? NDT : 8;
-        uint2 vop[2][PG];
-#pragma unroll
-        for (int j = 0; j < PG; ++j) vop[0][j] = *reinterpret_cast<const uint2*>(vtile + vb + VT_DT * j);
-#pragma unroll
-        for (int grp = 0; grp < NDT / PG; ++grp) {
-            if (grp + 1 < NDT / PG) {
-#pragma unroll
-                for (int j = 0; j < PG; ++j)
-                    vop[(grp + 1) & 1][j] = *reinterpret_cast<const uint2*>(vtile + vb + VT_DT * (PG * (grp + 1) + j));
-            }
-#pragma unroll
-            for (int j = 0; j < PG; ++j) {
-                const f16x4 a = *reinterpret_cast<const f16x4*>(&vop[grp & 1][j]);
-                oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, oacc[PG * grp + j], 0, 0, 0);
-            }
-        }
+        attn_chunk<D, QF32>(ktile, vtile, kr, cz, gz, qhi, qlo, zscale, oacc, m_run, l_run);
     }
 
     if (p.nsplit > 1) {
@@ -476,42 +683,276 @@ __global__ __launch_bounds__(64 * NW, RG == RING ? 1 : 2) void attn_kernel(AttnP
         if (p.merge && split == 0 && g == 0) p.lse_prev[row * p.H + head] = p.lse[row * p.H + head];
         return;
     }
-    // ---- normalised output (o, lse) of this key set
-    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-    const float lse_cur = (l_run > 0.0f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-    float* orow = p.o + (row * p.H + head) * D;
-    float w_cur = 1.0f, w_old = 0.0f, lse_out = lse_cur;
-    if (p.merge) {
-        const float lse_old = p.lse[row * p.H + head];
-        const float L = fmaxf(lse_old, lse_cur);
-        if (L == -INFINITY) {
-            w_cur = 0.0f;
-            w_old = 0.0f;
-            lse_out = -INFINITY;
-        } else {
-            w_old = expf(lse_old - L);
-            w_cur = expf(lse_cur - L);
-            const float tot = w_old + w_cur;
-            w_old /= tot;
-            w_cur /= tot;
-            lse_out = L + logf(tot);
-        }
+    attn_store<D>(p, row, head, g, oacc, m_run, l_run);
+}
+
+// ---- Many query rows at D = 512, H = 64 with bf16 queries and no key split
+// (prefill).  One workgroup of eight waves per CU.  Waves 0-3 consume as in
+// attn_kernel (wave w: heads 16w..16w+15); waves 4-7 produce: producer p
+// copies keys 4p..4p+3 of each chunk global -> LDS, PC_RING chunks ahead, and
+// dequantises exactly those keys into one of three tile buffers.  A producer
+// only reads the copies it issued itself, so it waits on its own
+// vector-memory counter and never on another wave; one workgroup barrier per
+// chunk hands a filled buffer to the consumers.  The consumers are pipelined
+// one chunk deep: while chunk k's PV products run on the matrix cores, they
+// issue chunk k+1's score products and compute its softmax weights, and the
+// producers dequantise chunk k+2 -- VALU, LDS and MFMA work of different
+// chunks overlap on every SIMD.
+constexpr int PC_RING = 3;
+constexpr int PC_TILES = 3;
+constexpr int PC_D = 512;
+constexpr int PC_NT = 512;
+
+// copies one producer issues per chunk (codes + scales, or 4 window rows)
+__device__ __forceinline__ int pc_copies(bool sparse) { return sparse ? 2 : 4; }
+
+// wait until at most n (0..15) of this wave's vector-memory operations are in flight
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+#define CSA2_VMW(N) \
+    case N: __builtin_amdgcn_s_waitcnt((N) | (7 << 4) | (15 << 8)); break;
+    switch (n) {
+        CSA2_VMW(0) CSA2_VMW(1) CSA2_VMW(2) CSA2_VMW(3) CSA2_VMW(4) CSA2_VMW(5) CSA2_VMW(6) CSA2_VMW(7)
+        CSA2_VMW(8) CSA2_VMW(9) CSA2_VMW(10) CSA2_VMW(11) CSA2_VMW(12) CSA2_VMW(13) CSA2_VMW(14)
+        default: __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (15 << 8)); break;
     }
+#undef CSA2_VMW
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)ptr;
+}
+
+// Producer pw's copies of one chunk (kr: the chunk's 16 key rows) into a ring
+// slot laid out as in Stage: codes [16][D/2] from 0, scales in one 256-byte
+// group per producer at SCALE_OFF (key 4pw+i at +256 pw + 32 i; the group's
+// upper half takes duplicate copies), window rows [16][2D].
+__device__ __forceinline__ void pc_issue(const AttnParams& p, bool sparse, const int64_t* kr, uint8_t* slot, int pw,
+                                         int lane) {
+    constexpr int D = PC_D;
+    // an opaque zero, fresh every call: per-lane offsets are recomputed here
+    // instead of being kept across the chunk loop as 64-bit addresses
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    const int lz = lane + z;
+    const int64_t* k4 = kr + 4 * pw;
+    if (sparse) {
+        const int64_t rc = max(k4[lz >> 4], (int64_t)0);
+        const int64_t rs = max(k4[(lz >> 3) & 3], (int64_t)0);
+        dma16_to_lds(p.codes + rc * (D / 2) + (lz & 15) * 16, slot + pw * 1024);
+        dma4_to_lds(p.scales + rs * (D / 16) + (lz & 7) * 4, slot + Stage<D>::SCALE_OFF + pw * 256);
+    } else {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        float4* dst = reinterpret_cast<float4*>(orow + 16 * dt + 4 * g);
-        float4 r = make_float4(oacc[dt][0] * inv * w_cur, oacc[dt][1] * inv * w_cur, oacc[dt][2] * inv * w_cur,
-                               oacc[dt][3] * inv * w_cur);
-        if (p.merge && w_old != 0.0f) {
-            const float4 old = *dst;
-            r.x += w_old * old.x;
-            r.y += w_old * old.y;
-            r.z += w_old * old.z;
-            r.w += w_old * old.w;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = max(k4[i], (int64_t)0);
+            dma16_to_lds(reinterpret_cast<const uint8_t*>(p.swa) + r * (2 * D) + lz * 16, slot + (4 * pw + i) * 1024);
         }
-        *dst = r;
     }
-    if (g == 0) p.lse[row * p.H + head] = lse_out;
+}
+
+// Producer pw dequantises its keys 4pw..4pw+3 (channels 8co..8co+7) from a
+// ring slot into a tile buffer.  The slot is read in one asm block with its
+// own wait: the compiler cannot tell ring slots apart and would make these
+// reads wait for every copy in flight.
+template <bool SPARSE>
+__device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, uint4* ktile, uint8_t* vtile) {
+    constexpr int D = PC_D;
+    uint32_t kh[4][4];
+    if (SPARSE) {
+        uint32_t cw[4], sb[4];
+        const uint32_t ac = lds_addr(slot + 4 * pw * (D / 2) + co * 4);
+        const uint32_t as = lds_addr(slot + Stage<D>::SCALE_OFF + pw * 256 + (co >> 1));
+        asm volatile(
+            "ds_read_b32 %0, %8\n"
+            "ds_read_b32 %1, %8 offset:256\n"
+            "ds_read_b32 %2, %8 offset:512\n"
+            "ds_read_b32 %3, %8 offset:768\n"
+            "ds_read_u8 %4, %9\n"
+            "ds_read_u8 %5, %9 offset:32\n"
+            "ds_read_u8 %6, %9 offset:64\n"
+            "ds_read_u8 %7, %9 offset:96\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]),
+              "=&v"(sb[3])
+            : "v"(ac), "v"(as)
+            : "memory");
+        item_from_fp4(cw, sb, kh);
+    } else {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        u32x4_t r0, r1, r2, r3;
+        const uint32_t a = lds_addr(slot + 4 * pw * (2 * D) + co * 16);
+        asm volatile(
+            "ds_read_b128 %0, %4\n"
+            "ds_read_b128 %1, %4 offset:1024\n"
+            "ds_read_b128 %2, %4 offset:2048\n"
+            "ds_read_b128 %3, %4 offset:3072\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+            : "v"(a)
+            : "memory");
+        const uint4 u[4] = {make_uint4(r0.x, r0.y, r0.z, r0.w), make_uint4(r1.x, r1.y, r1.z, r1.w),
+                            make_uint4(r2.x, r2.y, r2.z, r2.w), make_uint4(r3.x, r3.y, r3.z, r3.w)};
+        item_from_bf16(u, kh);
+    }
+    // the tile writes of put_item, in one asm block for the same reason: the
+    // compiler would make them wait for the copies in flight.  K tile: key
+    // 4pw+i at (4pw+i)(D/8+2)16 + 16co; V^T tile: channel 8co+e at
+    // vt_off(8co+e, pw) = vt_off(8co, pw) + 32e.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    constexpr int KROWB = (D / 8 + KROW_PAD) * 16;
+    static_assert(3 * KROWB < 65536 && vt_off(8 * 63 + 7, 3) < 65536, "ds offsets are 16-bit");
+    static_assert(vt_off(8 * 5 + 7, 2) == vt_off(8 * 5, 2) + 32 * 7 && vt_off(8 * 6 + 3, 1) == vt_off(8 * 6, 1) + 96,
+                  "row 8co+e of a lane is 32e bytes past row 8co");
+    const uint32_t ak = lds_addr(ktile) + (uint32_t)(4 * pw * KROWB + co * 16);
+    const uint32_t av = lds_addr(vtile) + (uint32_t)vt_off(8 * co, pw);
+    u32x2_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        v[e] = u32x2_t{__builtin_amdgcn_perm(kh[1][e >> 1], kh[0][e >> 1], sel),
+                       __builtin_amdgcn_perm(kh[3][e >> 1], kh[2][e >> 1], sel)};
+    }
+    const u32x4_t k0{kh[0][0], kh[0][1], kh[0][2], kh[0][3]}, k1{kh[1][0], kh[1][1], kh[1][2], kh[1][3]};
+    const u32x4_t k2{kh[2][0], kh[2][1], kh[2][2], kh[2][3]}, k3{kh[3][0], kh[3][1], kh[3][2], kh[3][3]};
+    asm volatile(
+        "ds_write_b128 %0, %2\n"
+        "ds_write_b128 %0, %3 offset:%c14\n"
+        "ds_write_b128 %0, %4 offset:%c15\n"
+        "ds_write_b128 %0, %5 offset:%c16\n"
+        "ds_write_b64 %1, %6\n"
+        "ds_write_b64 %1, %7 offset:32\n"
+        "ds_write_b64 %1, %8 offset:64\n"
+        "ds_write_b64 %1, %9 offset:96\n"
+        "ds_write_b64 %1, %10 offset:128\n"
+        "ds_write_b64 %1, %11 offset:160\n"
+        "ds_write_b64 %1, %12 offset:192\n"
+        "ds_write_b64 %1, %13 offset:224"
+        :
+        : "v"(ak), "v"(av), "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]),
+          "v"(v[5]), "v"(v[6]), "v"(v[7]), "i"(KROWB), "i"(2 * KROWB), "i"(3 * KROWB)
+        : "memory");
+}
+
+__global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
+    constexpr int D = PC_D, NW = 4;
+    constexpr int NBLK = D / 32, NDT = D / 16, CPR = D / 8;
+    using S = Stage<D>;
+    __shared__ uint4 ktile[PC_TILES][CHUNK_KEYS * (CPR + KROW_PAD)];
+    __shared__ __attribute__((aligned(16))) uint8_t vtile[PC_TILES][VT_BYTES(D)];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[PC_RING * S::SLOT];
+    __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool consumer = wv < NW;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t row = blockIdx.y;
+    const int b = (int)(row / p.Q);
+    const int head = 16 * wv + c16;  // (consumers)
+    const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
+    const int n_sp = p.Kp / CHUNK_KEYS;
+    const int slot = p.Wp ? p.q_slot[row] : 0;
+    const int wlo = max(0, slot - p.window + 1);
+    const int nk = nchunks * CHUNK_KEYS;
+
+    // ---- index loads first, then the consumers' query loads
+    constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + PC_NT - 1) / PC_NT;
+    int32_t kent[KR_IT];
+#pragma unroll
+    for (int j = 0; j < KR_IT; ++j) {
+        const int i = tid + j * PC_NT;
+        kent[j] = (i < nk && i < p.K) ? p.idx[row * p.K + i] : -1;
+    }
+    uint4 qraw[NBLK];
+    if (consumer) {
+        const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.H + head) * D;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) qraw[blk] = *reinterpret_cast<const uint4*>(qr + 32 * blk + 8 * g);
+    }
+    // ---- physical rows of every key (-1: none)
+#pragma unroll
+    for (int j = 0; j < KR_IT; ++j) {
+        const int i = tid + j * PC_NT;
+        if (i >= nk) break;
+        int64_t r = -1;
+        if (i < p.Kp) {
+            if (kent[j] >= 0) r = phys_row(p.kvmap, b, kent[j]);
+        } else {
+            const int t = wlo + (i - p.Kp);
+            if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
+        }
+        krow[i] = r;
+    }
+    lds_barrier();
+
+    f16x8 qhi[NBLK];
+    f16x8 qlo[1];
+    float zscale = 0.0f;
+    f32x4 oacc[NDT];
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int pw = wv - NW;
+    int issued = 0;  // (producers) chunks whose copies this wave has issued
+    // producer step for chunk c: wait for this wave's copies of it, dequantise
+    // them into tile buffer c % PC_TILES, refill the freed ring slot
+    auto produce = [&](int c) {
+        int later = 0;
+        for (int ch = c + 1; ch < issued; ++ch) later += pc_copies(ch < n_sp);
+        wait_vm_at_most(later);
+        int zz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+        const int co = lane + zz;
+        const uint8_t* st = ring + (c % PC_RING) * S::SLOT;
+        const int tb = c % PC_TILES;
+        if (c < n_sp)
+            pc_store<true>(st, pw, co, ktile[tb], vtile[tb]);
+        else
+            pc_store<false>(st, pw, co, ktile[tb], vtile[tb]);
+        if (issued < nchunks) {
+            pc_issue(p, issued < n_sp, krow + issued * CHUNK_KEYS, ring + (issued % PC_RING) * S::SLOT, pw, lane);
+            ++issued;
+        }
+    };
+    if (consumer) {
+        const float qf[1][8] = {};
+        zscale = q_operand<D, false>(qf, qraw, p.scale_log2, qhi, qlo);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        issued = min(nchunks, PC_RING);
+        for (int ch = 0; ch < issued; ++ch)
+            pc_issue(p, ch < n_sp, krow + ch * CHUNK_KEYS, ring + ch * S::SLOT, pw, lane);
+        if (nchunks > 0) produce(0);
+        if (nchunks > 1) produce(1);
+    }
+    lds_barrier();
+
+    // consumers: chunk 0's scores and weights ahead of the loop
+    f16x4 pb = {};
+    if (consumer && nchunks > 0) {
+        int zz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+        const int lz = lane + zz;
+        const f32x4 s0 = attn_scores<D, false>(ktile[0], lz & 15, lz >> 4, qhi, qlo);
+        pb = attn_weights<NDT>(s0, krow, lz >> 4, zscale, oacc, m_run, l_run);
+    }
+    // iteration k: consumers read tiles k and k+1, producers fill tile k+2
+    // (last read in iteration k-1)
+    for (int k = 0; k < nchunks; ++k) {
+        if (consumer) {
+            int zz;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+            const int lz = lane + zz;
+            const bool next = k + 1 < nchunks;
+            f32x4 s1 = {};
+            if (next) s1 = attn_scores<D, false>(ktile[(k + 1) % PC_TILES], lz & 15, lz >> 4, qhi, qlo);
+            attn_pv<D>(vtile[k % PC_TILES], lz & 15, lz >> 4, pb, oacc);
+            if (next) pb = attn_weights<NDT>(s1, krow + (k + 1) * CHUNK_KEYS, lz >> 4, zscale, oacc, m_run, l_run);
+        } else if (k + 2 < nchunks) {
+            produce(k + 2);
+        }
+        lds_barrier();
+    }
+    if (consumer) attn_store<D>(p, row, head, g, oacc, m_run, l_run);
 }
 
 // Merge the split partials: exact log-sum-exp combination, optionally together
@@ -662,13 +1103,10 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     const dim3 block((unsigned)(4 * H));
     const bool f32 = qt == CSA2_F32;
     const int nw = H / 16;
-    const bool wide = p.nsplit == 1 && rows >= 512 && D == 512 && nw == 4;
-    if (wide) {
-        if (f32)
-            attn_kernel<512, true, 4, RING_WIDE><<<grid, block, 0, stream>>>(p);
-        else
-            attn_kernel<512, false, 4, RING_WIDE><<<grid, block, 0, stream>>>(p);
-    }
+    // many rows without a key split at D = 512, H = 64, bf16 queries: the
+    // producer/consumer kernel (the fp32 query's extra 64 registers do not fit)
+    const bool wide = p.nsplit == 1 && rows >= 512 && D == 512 && nw == 4 && !f32;
+    if (wide) attn_pc_kernel<<<grid, dim3(PC_NT), 0, stream>>>(p);
 #define CSA2_ATTN_NW(DD, F, NWV) \
     if (!wide && nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
 #define CSA2_ATTN(DD)                                                                                   \

@@ -288,7 +288,8 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
 @pytest.mark.parametrize("B,Q,H,D,K,qdtype", [
     (2, 1, 64, 512, 512, torch.bfloat16), (1, 1, 16, 128, 512, torch.float32), (3, 2, 32, 256, 100, torch.bfloat16),
     (600, 1, 16, 128, 48, torch.bfloat16),
-    # many rows at D = 512, H = 64: the two-workgroups-per-CU variant (rows sampled)
+    # many rows at D = 512, H = 64 (rows sampled): bf16 queries take the
+    # two-workgroups-per-CU variant, fp32 queries the one-workgroup kernel
     (520, 1, 64, 512, 512, torch.bfloat16), (300, 2, 64, 512, 200, torch.float32)])
 def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype):
     n, T, window = (3000 if B < 100 else 520), 200, 128
