@@ -86,26 +86,16 @@ __device__ __forceinline__ void fp4x8_to_f16(uint32_t w, uint32_t sc2, uint32_t 
     }
 }
 
-// LDS layouts of the two fp16 tiles, chosen against bank conflicts (measured
-// on gfx950: 64 banks of 4 bytes; a 64-bit access serves lanes 0-31 and 32-63
-// in one pass each, a 128-bit access lanes {0-7, 24-31}, {8-15, 16-23},
-// {32-39, 56-63}, {40-47, 48-55}).
-// K tile: row k of D fp16 at k (D/8 + 2) 16 bytes (32 bytes of padding per
-// row), read by lane (cz, gz) at row cz, 16-byte chunk 4j + gz, written by
-// lane co at chunk co of one row: conflict-free both ways.
+// LDS layout of the fp16 K tile, chosen against bank conflicts (measured on
+// gfx950: 64 banks of 4 bytes; a 64-bit access serves lanes 0-31 and 32-63 in
+// one pass each, a 128-bit access lanes {0-7, 24-31}, {8-15, 16-23},
+// {32-39, 56-63}, {40-47, 48-55}).  Row k (D fp16) at k (D/8 + 2) 16 bytes, 32
+// bytes of padding per row.  The tile serves both products: S reads lane
+// (cz, gz) at row cz, 16-byte chunk 4j + gz; PV reads V^T by the transposing
+// 64-bit LDS read (see attn_pv) at rows 4gz + cz/4, byte 32dt + 8(cz % 4);
+// the dequantisation writes lane co at chunk co of one row.  All three are
+// conflict-free.
 constexpr int KROW_PAD = 2;
-// V^T tile: byte offset of V^T[d][keys 4kq..4kq+3] (8 bytes): rows of 16 keys
-// x fp16 = 32 B, 16 B of padding after every 16 rows, and the four key groups
-// of a row swapped in pairs (kq ^ 3) when bit 3 of d is set.  Read by lane
-// (cz, gz) at row 16dt + cz, group gz (MFMA operand), written by lane co at
-// row 8co + e, one group (dequantisation): both conflict-free.
-__host__ __device__ constexpr int vt_off(int d, int kq) {
-    return d * 32 + (d >> 4) * 16 + ((kq ^ (3 * ((d >> 3) & 1))) * 8);
-}
-// the same for d = 16 dt + c16 (c16 < 16), split so that dt becomes an immediate offset
-__device__ __forceinline__ int vt_base(int c16, int kq) { return vt_off(c16, kq); }
-constexpr int VT_DT = 16 * 32 + 16;  // bytes per 16 rows
-constexpr int VT_BYTES(int D) { return D * 32 + (D / 16) * 16; }
 
 constexpr int MAX_CPS = 64;  // chunks per split (keys per workgroup <= 1024)
 constexpr int RING = 4;      // chunks whose raw bytes are in flight / staged in LDS at once
@@ -253,30 +243,19 @@ __device__ __forceinline__ void item_from_bf16(const uint4 (&u)[4], uint32_t (&k
     }
 }
 
-// Write one item (keys 4kq..4kq+3, channels 8co..8co+7) into the K tile (fp16,
-// rows of D + 8 halves: the pad spreads the 16 rows of an MFMA operand read
-// over all banks) and the V^T tile (fp16, transposed, padded).
+// Write one item (keys 4kq..4kq+3, channels 8co..8co+7) into the K tile.
 template <int D>
-__device__ __forceinline__ void put_item(const uint32_t (&kh)[4][4], int kq, int co, uint4* ktile, uint8_t* vtile) {
+__device__ __forceinline__ void put_item(const uint32_t (&kh)[4][4], int kq, int co, uint4* ktile) {
     constexpr int KROW = D / 8 + KROW_PAD;  // uint4 per K-tile row
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         ktile[(4 * kq + i) * KROW + co] = make_uint4(kh[i][0], kh[i][1], kh[i][2], kh[i][3]);
-    // V^T row d = 8co + e holds channel e of the 4 keys
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int d = 8 * co + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t x01 = __builtin_amdgcn_perm(kh[1][e >> 1], kh[0][e >> 1], sel);
-        const uint32_t x23 = __builtin_amdgcn_perm(kh[3][e >> 1], kh[2][e >> 1], sel);
-        *reinterpret_cast<uint2*>(vtile + vt_off(d, kq)) = make_uint2(x01, x23);
-    }
 }
 
-// Dequantise one item from a staged chunk into the tiles.  Keys without a row
+// Dequantise one item from a staged chunk into the K tile.  Keys without a row
 // hold row 0's finite values; their softmax weight is exactly 0.
 template <int D, bool SPARSE>
-__device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, uint4* ktile, uint8_t* vtile) {
+__device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, uint4* ktile) {
     uint32_t kh[4][4];  // fp16 pairs: [key][channel pair]
     if (SPARSE) {
         uint32_t cw[4], sb[4];
@@ -293,7 +272,7 @@ __device__ __forceinline__ void store_item(const uint8_t* slot, int kq, int co, 
         for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const uint4*>(slot + (4 * kq + i) * (2 * D) + co * 16);
         item_from_bf16(u, kh);
     }
-    put_item<D>(kh, kq, co, ktile, vtile);
+    put_item<D>(kh, kq, co, ktile);
 }
 
 // max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
@@ -322,9 +301,10 @@ __device__ __forceinline__ uint32_t rows_umax(uint32_t x) {
 // fp16, pre-scaled by 2^-qs so that the head's largest element lies in
 // [2^14, 2^15); an fp32 query is split into hi + lo fp16 parts.  Returns the
 // logit scale sm_scale log2(e) 2^qs.
-template <int D, bool QF32>
+// Only blocks BLK0..BLK0+NB-1 are converted; the scale comes from all D channels.
+template <int D, bool QF32, int NB = D / 32, int BLK0 = 0>
 __device__ __forceinline__ float q_operand(const float (&qf)[QF32 ? D / 32 : 1][8], const uint4 (&qraw)[QF32 ? 1 : D / 32],
-                                          float scale_log2, f16x8 (&qhi)[D / 32], f16x8 (&qlo)[QF32 ? D / 32 : 1]) {
+                                          float scale_log2, f16x8 (&qhi)[NB], f16x8 (&qlo)[QF32 ? NB : 1]) {
     constexpr int NBLK = D / 32;
     uint32_t qmax = 0;  // largest |q| as an fp32 bit pattern (monotone in |q|)
 #pragma unroll
@@ -344,7 +324,8 @@ __device__ __forceinline__ float q_operand(const float (&qf)[QF32 ? D / 32 : 1][
     const int qs = qmax == 0 ? 0 : min(113, max(-100, (int)(qmax >> 23) - 127 - 14));
     const float qscale = __uint_as_float((uint32_t)(127 - qs) << 23);
 #pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
+    for (int bi = 0; bi < NB; ++bi) {
+        const int blk = BLK0 + bi;
         float x[8];
         if (QF32) {
 #pragma unroll
@@ -361,8 +342,8 @@ __device__ __forceinline__ float q_operand(const float (&qf)[QF32 ? D / 32 : 1][
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const _Float16 h = (_Float16)x[e];
-            qhi[blk][e] = h;
-            if (QF32) qlo[QF32 ? blk : 0][e] = (_Float16)(x[e] - (float)h);
+            qhi[bi][e] = h;
+            if (QF32) qlo[QF32 ? bi : 0][e] = (_Float16)(x[e] - (float)h);
         }
     }
     return scale_log2 * __uint_as_float((uint32_t)(127 + qs) << 23);
@@ -373,10 +354,12 @@ __device__ __forceinline__ float q_operand(const float (&qf)[QF32 ? D / 32 : 1][
 // maximum (attn_weights), O^T += V^T P^T (attn_pv).  kr: the chunk's key rows
 // (-1: none); cz, gz: lane % 16 and lane / 16, recomputed by the caller every
 // chunk (so that no address lives across the chunk loop).
-template <int D, bool QF32>
-__device__ __forceinline__ f32x4 attn_scores(const uint4* ktile, int cz, int gz, const f16x8 (&qhi)[D / 32],
-                                             const f16x8 (&qlo)[QF32 ? D / 32 : 1]) {
-    constexpr int NBLK = D / 32, CPR = D / 8;
+// (over the NB 32-channel blocks from blk0 only: a partial score)
+template <int D, bool QF32, int NB = D / 32>
+__device__ __forceinline__ f32x4 attn_scores(const uint4* ktile, int cz, int gz, const f16x8 (&qhi)[NB],
+                                             const f16x8 (&qlo)[QF32 ? NB : 1], int blk0 = 0) {
+    constexpr int NBLK = NB, CPR = D / 8;
+    ktile += 4 * blk0;
     // S^T[key][head] = sum_d K[key][d] Q[head][d]: four accumulator chains (a
     // dependent MFMA waits for three others); the operands of the next four
     // blocks are read while these multiply
@@ -443,25 +426,25 @@ __device__ __forceinline__ f16x4 attn_weights(const f32x4& s, const int64_t* kr,
     return pb;
 }
 
-// O^T[d][head] += sum_key V^T[d][key] P^T[key][head]
-template <int D>
-__device__ __forceinline__ void attn_pv(const uint8_t* vtile, int cz, int gz, const f16x4& pb, f32x4 (&oacc)[D / 16]) {
-    constexpr int NDT = D / 16;
-    // operands read eight tiles ahead of the MFMAs that use them.  Four base
-    // addresses, one per tile index mod 4 (opaque to the compiler): reads from
-    // one base lie 4 tiles apart, beyond the reach of a paired 64-bit read, so
-    // each stays a single 64-bit read -- conflict-free in this layout, where a
-    // paired read of two neighbouring tiles would conflict two ways.
+// O^T[d][head] += sum_key V^T[d][key] P^T[key][head].  The A operand of lane
+// (cz, gz), V^T[16dt + cz][keys 4gz..4gz+3], comes from the K tile through the
+// transposing LDS read: within each 16-lane group, lane j receives element
+// j % 4 of the four fp16 that lane 4e + j / 4 addresses, for e = 0..3.  So
+// lane (cz, gz) addresses row 4gz + cz / 4 at columns 16dt + 4(cz % 4) .. +3.
+// (over the NDTP 16-channel tiles from dt0 only)
+template <int D, int NDTP = D / 16>
+__device__ __forceinline__ void attn_pv(const uint4* ktile, int cz, int gz, const f16x4& pb, f32x4 (&oacc)[NDTP],
+                                        int dt0 = 0) {
+    constexpr int NDT = NDTP, ROWB = (D / 8 + KROW_PAD) * 16;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(ktile) + (4 * gz + (cz >> 2)) * ROWB + 8 * (cz & 3) + 32 * dt0;
+    auto vread = [&](int dt) {
+        return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base + 32 * dt)));
+    };
+    // operands read eight tiles ahead of the MFMAs that use them
     constexpr int PG = NDT < 8 ? NDT : 8;
-    const uint8_t* vbr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        int zr;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(zr));
-        vbr[r] = vtile + vt_base(cz, gz) + VT_DT * r + zr;
-    }
-    auto vread = [&](int t) { return *reinterpret_cast<const uint2*>(vbr[t & 3] + VT_DT * (t & ~3)); };
-    uint2 vop[2][PG];
+    f16x4 vop[2][PG];
 #pragma unroll
     for (int j = 0; j < PG; ++j) vop[0][j] = vread(j);
 #pragma unroll
@@ -471,28 +454,101 @@ __device__ __forceinline__ void attn_pv(const uint8_t* vtile, int cz, int gz, co
             for (int j = 0; j < PG; ++j) vop[(grp + 1) & 1][j] = vread(PG * (grp + 1) + j);
         }
 #pragma unroll
-        for (int j = 0; j < PG; ++j) {
-            const f16x4 a = *reinterpret_cast<const f16x4*>(&vop[grp & 1][j]);
-            oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, oacc[PG * grp + j], 0, 0, 0);
+        for (int j = 0; j < PG; ++j)
+            oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop[grp & 1][j], pb, oacc[PG * grp + j], 0, 0, 0);
+    }
+}
+
+// Two chunks A, B at once (many rows): softmax weights of keys 4gz..4gz+3 of
+// both, and one O^T += V^T P^T over their 32 keys with the K = 32 MFMA (the
+// K = 16 form runs at half its rate).  K index 8gz + e of the product is key
+// 4gz + e of chunk A for e < 4 and key 4gz + e - 4 of chunk B otherwise, in
+// both operands: P is (pA, pB), V^T is the transposing read of tile A
+// followed by that of tile B.
+template <int NDT>
+__device__ __forceinline__ f16x8 attn_weights2(const f32x4& sa, const f32x4& sb, const int64_t* kra,
+                                               const int64_t* krb, int gz, float zscale, f32x4 (&oacc)[NDT],
+                                               float& m_run, float& l_run) {
+    float z[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        z[i] = (kra[4 * gz + i] >= 0) ? sa[i] * zscale : -INFINITY;
+        z[4 + i] = (krb[4 * gz + i] >= 0) ? sb[i] * zscale : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mloc = fmaxf(mloc, z[i]);
+    mloc = rows_max(mloc);
+    // lazy maximum: move it only when these keys exceed it by more than 2^8
+    float alpha = 1.0f;
+    if (mloc > m_run + 8.0f) {
+        if (l_run > 0.0f) alpha = exp2f(m_run - mloc);
+        m_run = mloc;
+    }
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+    float psum = 0.0f;
+    f16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const _Float16 h = (_Float16)((z[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - m_run));
+        psum += (float)h;
+        pb[i] = h;
+    }
+    l_run = l_run * alpha + rows_sum(psum);
+    return pb;
+}
+
+template <int D>
+__device__ __forceinline__ void attn_pv2(const uint4* ka, const uint4* kb, int cz, int gz, const f16x8& pb,
+                                         f32x4 (&oacc)[D / 16]) {
+    constexpr int NDT = D / 16, ROWB = (D / 8 + KROW_PAD) * 16;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+    const int off = (4 * gz + (cz >> 2)) * ROWB + 8 * (cz & 3);
+    const uint8_t* ba = reinterpret_cast<const uint8_t*>(ka) + off;
+    const uint8_t* bb = reinterpret_cast<const uint8_t*>(kb) + off;
+    auto vread = [&](int dt) {
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(ba + 32 * dt));
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(bb + 32 * dt));
+        return __builtin_bit_cast(f16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // operands read eight tiles ahead of the MFMAs that use them
+    constexpr int PG = 8;
+    f16x8 vop[2][PG];
+#pragma unroll
+    for (int j = 0; j < PG; ++j) vop[0][j] = vread(j);
+#pragma unroll
+    for (int grp = 0; grp < NDT / PG; ++grp) {
+        if (grp + 1 < NDT / PG) {
+#pragma unroll
+            for (int j = 0; j < PG; ++j) vop[(grp + 1) & 1][j] = vread(PG * (grp + 1) + j);
         }
+#pragma unroll
+        for (int j = 0; j < PG; ++j)
+            oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[grp & 1][j], pb, oacc[PG * grp + j], 0, 0, 0);
     }
 }
 
 template <int D, bool QF32>
-__device__ __forceinline__ void attn_chunk(const uint4* ktile, const uint8_t* vtile, const int64_t* kr, int cz, int gz,
+__device__ __forceinline__ void attn_chunk(const uint4* ktile, const int64_t* kr, int cz, int gz,
                                            const f16x8 (&qhi)[D / 32], const f16x8 (&qlo)[QF32 ? D / 32 : 1],
                                            float zscale, f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
     const f32x4 s = attn_scores<D, QF32>(ktile, cz, gz, qhi, qlo);
     const f16x4 pb = attn_weights<D / 16>(s, kr, gz, zscale, oacc, m_run, l_run);
-    attn_pv<D>(vtile, cz, gz, pb, oacc);
+    attn_pv<D>(ktile, cz, gz, pb, oacc);
 }
 
 // Normalised output (o, lse) of one head's key set, merged with the (o, lse)
 // already in the output when p.merge is set.
-template <int D>
+// (columns of the NDTP tiles from tile dt0; the lse only when write_lse)
+template <int D, int NDTP = D / 16>
 __device__ __forceinline__ void attn_store(const AttnParams& p, int64_t row, int head, int g,
-                                           const f32x4 (&oacc)[D / 16], float m_run, float l_run) {
-    constexpr int NDT = D / 16;
+                                           const f32x4 (&oacc)[NDTP], float m_run, float l_run, int dt0 = 0,
+                                           bool write_lse = true) {
+    constexpr int NDT = NDTP;
     const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
     const float lse_cur = (l_run > 0.0f) ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
     float* orow = p.o + (row * p.H + head) * D;
@@ -515,7 +571,7 @@ __device__ __forceinline__ void attn_store(const AttnParams& p, int64_t row, int
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-        float4* dst = reinterpret_cast<float4*>(orow + 16 * dt + 4 * g);
+        float4* dst = reinterpret_cast<float4*>(orow + 16 * (dt0 + dt) + 4 * g);
         float4 r = make_float4(oacc[dt][0] * inv * w_cur, oacc[dt][1] * inv * w_cur, oacc[dt][2] * inv * w_cur,
                                oacc[dt][3] * inv * w_cur);
         if (p.merge && w_old != 0.0f) {
@@ -527,7 +583,7 @@ __device__ __forceinline__ void attn_store(const AttnParams& p, int64_t row, int
         }
         *dst = r;
     }
-    if (g == 0) p.lse[row * p.H + head] = lse_out;
+    if (write_lse && g == 0) p.lse[row * p.H + head] = lse_out;
 }
 
 template <int D, bool QF32, int NW>
@@ -540,7 +596,6 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
     constexpr int ITEMS = 4 * CPR;  // dequantisation items per chunk
     using S = Stage<D>;
     __shared__ uint4 ktile[CHUNK_KEYS * (CPR + KROW_PAD)];
-    __shared__ __attribute__((aligned(16))) uint8_t vtile[VT_BYTES(D)];
     __shared__ __attribute__((aligned(16))) uint8_t ring[RG * S::SLOT];
     __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
 
@@ -654,13 +709,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
 #pragma unroll
             for (int it = 0; it < (ITEMS + NT - 1) / NT; ++it) {
                 const int item = it * NT + tz;
-                if (item < ITEMS) store_item<D, true>(st, item / CPR, item % CPR, ktile, vtile);
+                if (item < ITEMS) store_item<D, true>(st, item / CPR, item % CPR, ktile);
             }
         } else {
 #pragma unroll
             for (int it = 0; it < (ITEMS + NT - 1) / NT; ++it) {
                 const int item = it * NT + tz;
-                if (item < ITEMS) store_item<D, false>(st, item / CPR, item % CPR, ktile, vtile);
+                if (item < ITEMS) store_item<D, false>(st, item / CPR, item % CPR, ktile);
             }
         }
         lds_barrier();
@@ -669,7 +724,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
             chunk_issue<D, NW>(p, nsparse, nr, ring + ((c_issued - c_lo) % RG) * S::SLOT, w, lz);
             ++c_issued;
         }
-        attn_chunk<D, QF32>(ktile, vtile, kr, cz, gz, qhi, qlo, zscale, oacc, m_run, l_run);
+        attn_chunk<D, QF32>(ktile, kr, cz, gz, qhi, qlo, zscale, oacc, m_run, l_run);
     }
 
     if (p.nsplit > 1) {
@@ -698,10 +753,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
 // issue chunk k+1's score products and compute its softmax weights, and the
 // producers dequantise chunk k+2 -- VALU, LDS and MFMA work of different
 // chunks overlap on every SIMD.
-constexpr int PC_RING = 3;
-constexpr int PC_TILES = 3;
+constexpr int PC_RING = 4;
+constexpr int PC_TILES = 4;  // two pairs of chunk tiles
+constexpr int PC_CONS = 4;   // consumer waves (16 heads each)
 constexpr int PC_D = 512;
-constexpr int PC_NT = 512;
+constexpr int PC_NT = 512;  // 4 consumer + 4 producer waves
 
 // copies one producer issues per chunk (codes + scales, or 4 window rows)
 __device__ __forceinline__ int pc_copies(bool sparse) { return sparse ? 2 : 4; }
@@ -754,7 +810,7 @@ __device__ __forceinline__ void pc_issue(const AttnParams& p, bool sparse, const
 // own wait: the compiler cannot tell ring slots apart and would make these
 // reads wait for every copy in flight.
 template <bool SPARSE>
-__device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, uint4* ktile, uint8_t* vtile) {
+__device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, uint4* ktile) {
     constexpr int D = PC_D;
     uint32_t kh[4][4];
     if (SPARSE) {
@@ -794,53 +850,31 @@ __device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, ui
         item_from_bf16(u, kh);
     }
     // the tile writes of put_item, in one asm block for the same reason: the
-    // compiler would make them wait for the copies in flight.  K tile: key
-    // 4pw+i at (4pw+i)(D/8+2)16 + 16co; V^T tile: channel 8co+e at
-    // vt_off(8co+e, pw) = vt_off(8co, pw) + 32e.
+    // compiler would make them wait for the copies in flight.  Key 4pw+i at
+    // (4pw+i)(D/8+2)16 + 16co.
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     constexpr int KROWB = (D / 8 + KROW_PAD) * 16;
-    static_assert(3 * KROWB < 65536 && vt_off(8 * 63 + 7, 3) < 65536, "ds offsets are 16-bit");
-    static_assert(vt_off(8 * 5 + 7, 2) == vt_off(8 * 5, 2) + 32 * 7 && vt_off(8 * 6 + 3, 1) == vt_off(8 * 6, 1) + 96,
-                  "row 8co+e of a lane is 32e bytes past row 8co");
+    static_assert(3 * KROWB < 65536, "ds offsets are 16-bit");
     const uint32_t ak = lds_addr(ktile) + (uint32_t)(4 * pw * KROWB + co * 16);
-    const uint32_t av = lds_addr(vtile) + (uint32_t)vt_off(8 * co, pw);
-    u32x2_t v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        v[e] = u32x2_t{__builtin_amdgcn_perm(kh[1][e >> 1], kh[0][e >> 1], sel),
-                       __builtin_amdgcn_perm(kh[3][e >> 1], kh[2][e >> 1], sel)};
-    }
     const u32x4_t k0{kh[0][0], kh[0][1], kh[0][2], kh[0][3]}, k1{kh[1][0], kh[1][1], kh[1][2], kh[1][3]};
     const u32x4_t k2{kh[2][0], kh[2][1], kh[2][2], kh[2][3]}, k3{kh[3][0], kh[3][1], kh[3][2], kh[3][3]};
     asm volatile(
-        "ds_write_b128 %0, %2\n"
-        "ds_write_b128 %0, %3 offset:%c14\n"
-        "ds_write_b128 %0, %4 offset:%c15\n"
-        "ds_write_b128 %0, %5 offset:%c16\n"
-        "ds_write_b64 %1, %6\n"
-        "ds_write_b64 %1, %7 offset:32\n"
-        "ds_write_b64 %1, %8 offset:64\n"
-        "ds_write_b64 %1, %9 offset:96\n"
-        "ds_write_b64 %1, %10 offset:128\n"
-        "ds_write_b64 %1, %11 offset:160\n"
-        "ds_write_b64 %1, %12 offset:192\n"
-        "ds_write_b64 %1, %13 offset:224"
+        "ds_write_b128 %0, %1\n"
+        "ds_write_b128 %0, %2 offset:%c5\n"
+        "ds_write_b128 %0, %3 offset:%c6\n"
+        "ds_write_b128 %0, %4 offset:%c7"
         :
-        : "v"(ak), "v"(av), "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]),
-          "v"(v[5]), "v"(v[6]), "v"(v[7]), "i"(KROWB), "i"(2 * KROWB), "i"(3 * KROWB)
+        : "v"(ak), "v"(k0), "v"(k1), "v"(k2), "v"(k3), "i"(KROWB), "i"(2 * KROWB), "i"(3 * KROWB)
         : "memory");
 }
 
 __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
-    constexpr int D = PC_D, NW = 4;
+    constexpr int D = PC_D, NW = PC_CONS;
     constexpr int NBLK = D / 32, NDT = D / 16, CPR = D / 8;
     using S = Stage<D>;
     __shared__ uint4 ktile[PC_TILES][CHUNK_KEYS * (CPR + KROW_PAD)];
-    __shared__ __attribute__((aligned(16))) uint8_t vtile[PC_TILES][VT_BYTES(D)];
     __shared__ __attribute__((aligned(16))) uint8_t ring[PC_RING * S::SLOT];
-    __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS];
+    __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS + CHUNK_KEYS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -850,13 +884,18 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     const int b = (int)(row / p.Q);
     const int head = 16 * wv + c16;  // (consumers)
     const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
+    // chunks are consumed in pairs; an odd count gets one padding chunk
+    // whose keys have no row (finite copies of row 0, weight exactly 0)
+    const int npad = nchunks + (nchunks & 1);
     const int n_sp = p.Kp / CHUNK_KEYS;
     const int slot = p.Wp ? p.q_slot[row] : 0;
     const int wlo = max(0, slot - p.window + 1);
     const int nk = nchunks * CHUNK_KEYS;
+    // the padding chunk is copied as the last real chunk's kind (its view is valid)
+    auto sparse_chunk = [&](int c) { return c < n_sp || (c >= nchunks && p.Wp == 0); };
 
     // ---- index loads first, then the consumers' query loads
-    constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + PC_NT - 1) / PC_NT;
+    constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + CHUNK_KEYS + PC_NT - 1) / PC_NT;
     int32_t kent[KR_IT];
 #pragma unroll
     for (int j = 0; j < KR_IT; ++j) {
@@ -869,13 +908,14 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk) qraw[blk] = *reinterpret_cast<const uint4*>(qr + 32 * blk + 8 * g);
     }
-    // ---- physical rows of every key (-1: none)
+    // ---- physical rows of every key (-1: none), the padding chunk included
 #pragma unroll
     for (int j = 0; j < KR_IT; ++j) {
         const int i = tid + j * PC_NT;
-        if (i >= nk) break;
+        if (i >= npad * CHUNK_KEYS) break;
         int64_t r = -1;
-        if (i < p.Kp) {
+        if (i >= nk) {
+        } else if (i < p.Kp) {
             if (kent[j] >= 0) r = phys_row(p.kvmap, b, kent[j]);
         } else {
             const int t = wlo + (i - p.Kp);
@@ -896,19 +936,20 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     // them into tile buffer c % PC_TILES, refill the freed ring slot
     auto produce = [&](int c) {
         int later = 0;
-        for (int ch = c + 1; ch < issued; ++ch) later += pc_copies(ch < n_sp);
+        for (int ch = c + 1; ch < issued; ++ch) later += pc_copies(sparse_chunk(ch));
         wait_vm_at_most(later);
         int zz;
         asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
         const int co = lane + zz;
         const uint8_t* st = ring + (c % PC_RING) * S::SLOT;
         const int tb = c % PC_TILES;
-        if (c < n_sp)
-            pc_store<true>(st, pw, co, ktile[tb], vtile[tb]);
+        if (sparse_chunk(c))
+            pc_store<true>(st, pw, co, ktile[tb]);
         else
-            pc_store<false>(st, pw, co, ktile[tb], vtile[tb]);
-        if (issued < nchunks) {
-            pc_issue(p, issued < n_sp, krow + issued * CHUNK_KEYS, ring + (issued % PC_RING) * S::SLOT, pw, lane);
+            pc_store<false>(st, pw, co, ktile[tb]);
+        if (issued < npad) {
+            pc_issue(p, sparse_chunk(issued), krow + issued * CHUNK_KEYS, ring + (issued % PC_RING) * S::SLOT, pw,
+                     lane);
             ++issued;
         }
     };
@@ -918,37 +959,33 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
-        issued = min(nchunks, PC_RING);
+        issued = min(npad, PC_RING);
         for (int ch = 0; ch < issued; ++ch)
-            pc_issue(p, ch < n_sp, krow + ch * CHUNK_KEYS, ring + ch * S::SLOT, pw, lane);
-        if (nchunks > 0) produce(0);
-        if (nchunks > 1) produce(1);
+            pc_issue(p, sparse_chunk(ch), krow + ch * CHUNK_KEYS, ring + ch * S::SLOT, pw, lane);
+        if (npad > 0) {
+            produce(0);
+            produce(1);
+        }
     }
     lds_barrier();
 
-    // consumers: chunk 0's scores and weights ahead of the loop
-    f16x4 pb = {};
-    if (consumer && nchunks > 0) {
-        int zz;
-        asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
-        const int lz = lane + zz;
-        const f32x4 s0 = attn_scores<D, false>(ktile[0], lz & 15, lz >> 4, qhi, qlo);
-        pb = attn_weights<NDT>(s0, krow, lz >> 4, zscale, oacc, m_run, l_run);
-    }
-    // iteration k: consumers read tiles k and k+1, producers fill tile k+2
-    // (last read in iteration k-1)
-    for (int k = 0; k < nchunks; ++k) {
+    // iteration j: consumers take chunks 2j, 2j+1 (tile buffers of one pair),
+    // producers fill the other pair's buffers with chunks 2j+2, 2j+3
+    for (int c = 0; c < npad; c += 2) {
         if (consumer) {
             int zz;
             asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
-            const int lz = lane + zz;
-            const bool next = k + 1 < nchunks;
-            f32x4 s1 = {};
-            if (next) s1 = attn_scores<D, false>(ktile[(k + 1) % PC_TILES], lz & 15, lz >> 4, qhi, qlo);
-            attn_pv<D>(vtile[k % PC_TILES], lz & 15, lz >> 4, pb, oacc);
-            if (next) pb = attn_weights<NDT>(s1, krow + (k + 1) * CHUNK_KEYS, lz >> 4, zscale, oacc, m_run, l_run);
-        } else if (k + 2 < nchunks) {
-            produce(k + 2);
+            const int lz = lane + zz, cz = lz & 15, gz = lz >> 4;
+            const uint4* ka = ktile[c % PC_TILES];
+            const uint4* kb = ktile[(c + 1) % PC_TILES];
+            const f32x4 sa = attn_scores<D, false>(ka, cz, gz, qhi, qlo);
+            const f32x4 sb = attn_scores<D, false>(kb, cz, gz, qhi, qlo);
+            const f16x8 pb = attn_weights2<NDT>(sa, sb, krow + c * CHUNK_KEYS, krow + (c + 1) * CHUNK_KEYS, gz,
+                                                zscale, oacc, m_run, l_run);
+            attn_pv2<D>(ka, kb, cz, gz, pb, oacc);
+        } else if (c + 2 < npad) {
+            produce(c + 2);
+            produce(c + 3);
         }
         lds_barrier();
     }

@@ -285,14 +285,17 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
     return cache, q, idx, swa, slot, rc.reshape(B, n, -1), rs.reshape(B, n, -1)
 
 
-@pytest.mark.parametrize("B,Q,H,D,K,qdtype", [
-    (2, 1, 64, 512, 512, torch.bfloat16), (1, 1, 16, 128, 512, torch.float32), (3, 2, 32, 256, 100, torch.bfloat16),
-    (600, 1, 16, 128, 48, torch.bfloat16),
+@pytest.mark.parametrize("B,Q,H,D,K,qdtype,window", [
+    (2, 1, 64, 512, 512, torch.bfloat16, 128), (1, 1, 16, 128, 512, torch.float32, 128),
+    (3, 2, 32, 256, 100, torch.bfloat16, 128), (600, 1, 16, 128, 48, torch.bfloat16, 128),
     # many rows at D = 512, H = 64 (rows sampled): bf16 queries take the
-    # two-workgroups-per-CU variant, fp32 queries the one-workgroup kernel
-    (520, 1, 64, 512, 512, torch.bfloat16), (300, 2, 64, 512, 200, torch.float32)])
-def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype):
-    n, T, window = (3000 if B < 100 else 520), 200, 128
+    # producer/consumer kernel (chunks in pairs; 13 sparse chunks and a
+    # one-chunk window exercise its padding chunk), fp32 queries the
+    # one-workgroup kernel
+    (520, 1, 64, 512, 512, torch.bfloat16, 128), (520, 1, 64, 512, 200, torch.bfloat16, 8),
+    (300, 2, 64, 512, 200, torch.float32, 128)])
+def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype, window):
+    n, T = (3000 if B < 100 else 520), 200
     cache, q, idx, swa, slot, rc, rs = _attn_inputs(B, Q, H, D, n, K, T, qdtype, f"at{B}{H}{D}{K}")
     sc = 1 / math.sqrt(D)
     o = torch.empty(B, Q, H, D, device=DEV)
@@ -302,7 +305,7 @@ def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype):
     api.csa2_sparse_attn_fp4(q.to(DEV), cache, idx.to(DEV), sc, o, lse, ws=ws)
     torch.cuda.synchronize()
     o1, l1 = to_np(o), to_np(lse)
-    case("swa_attn merge")
+    case(f"swa_attn merge window={window}")
     api.csa2_swa_attn(q.to(DEV), swa.to(DEV), slot.to(DEV), window, sc, 1, o, lse, ws=ws)
     torch.cuda.synchronize()
     o2, l2 = to_np(o), to_np(lse)
