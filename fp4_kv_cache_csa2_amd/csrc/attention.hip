@@ -58,10 +58,6 @@ struct AttnParams {
     float* lse_prev;           // [rows][H]: the output's lse before a merge
 };
 
-// E2M1 magnitude x 2^8 -> high byte of its fp16 value (the low byte is 0):
-// magnitudes 0, 0.5, 1, 1.5 | 2, 3, 4, 6, times 256
-constexpr uint32_t F16HI_LO = 0x5E5C5800u, F16HI_HI = 0x66646260u;
-
 // E4M3FN scale byte -> fp16 bits of scale x 2^-8, twice (exact: E4M3 and fp16
 // share the mantissa alignment, so the byte shifted into the fp16 exponent /
 // mantissa fields is the scale with its exponent bias off by 8; subnormal
@@ -69,21 +65,17 @@ constexpr uint32_t F16HI_LO = 0x5E5C5800u, F16HI_HI = 0x66646260u;
 __device__ __forceinline__ uint32_t e4m3_f16x2_over256(uint32_t code) { return (code << 7) | (code << 23); }
 
 // 8 FP4 codes (one 32-bit word, channel 2i in the low nibble of byte i) times
-// the scale -> four fp16 pairs (channels 2i, 2i+1).  (E2M1 x 2^8) x (E4M3 x
-// 2^-8) is exact: <= 6 significant bits in [2^-10, 2688].
+// the scale -> four fp16 pairs (channels 2i, 2i+1).  gfx950's FP4 conversion
+// turns byte i into (E2M1 x 2^8) of both its nibbles, low nibble first (its
+// fp32 scale is applied as a power of two; checked exhaustively on all 256
+// byte values); (E2M1 x 2^8) x (E4M3 x 2^-8) is exact in fp16: <= 6
+// significant bits in [2^-10, 2688].
 __device__ __forceinline__ void fp4x8_to_f16(uint32_t w, uint32_t sc2, uint32_t (&out)[4]) {
-    const uint32_t ev = w & 0x07070707u;         // magnitudes of channels 0, 2, 4, 6
-    const uint32_t od = (w >> 4) & 0x07070707u;  // magnitudes of channels 1, 3, 5, 7
-    const uint32_t hbe = __builtin_amdgcn_perm(F16HI_HI, F16HI_LO, ev) | ((w << 4) & 0x80808080u);
-    const uint32_t hbo = __builtin_amdgcn_perm(F16HI_HI, F16HI_LO, od) | (w & 0x80808080u);
-    const uint32_t sel[4] = {0x040C000Cu, 0x050C010Cu, 0x060C020Cu, 0x070C030Cu};
-    const f16x2 sc = *reinterpret_cast<const f16x2*>(&sc2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t pr = __builtin_amdgcn_perm(hbo, hbe, sel[i]);
-        const f16x2 v = *reinterpret_cast<const f16x2*>(&pr) * sc;
-        out[i] = *reinterpret_cast<const uint32_t*>(&v);
-    }
+    const f16x2 sc = __builtin_bit_cast(f16x2, sc2);
+#define CSA2_FP4B(I)                                                                                            \
+    out[I] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, I)) * sc);
+    CSA2_FP4B(0) CSA2_FP4B(1) CSA2_FP4B(2) CSA2_FP4B(3)
+#undef CSA2_FP4B
 }
 
 // LDS layout of the fp16 K tile, chosen against bank conflicts (measured on
