@@ -457,6 +457,21 @@ __device__ __forceinline__ void attn_pv(const uint4* ktile, int cz, int gz, cons
 // 4gz + e of chunk A for e < 4 and key 4gz + e - 4 of chunk B otherwise, in
 // both operands: P is (pA, pB), V^T is the transposing read of tile A
 // followed by that of tile B.
+// Scheduling hint for a run of N MFMAs fed by LDS reads (R per MFMA): the
+// reads of the first A MFMAs first, then each MFMA followed by the reads of
+// the one A places later, so that A MFMAs' operands are in flight while the
+// matrix core works (the default schedule waits for each operand just before
+// its MFMA).
+template <int N, int R, int A>
+__device__ __forceinline__ void mfma_pipeline_hint() {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i + A < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+}
+
 template <int NDT>
 __device__ __forceinline__ f16x8 attn_weights2(const f32x4& sa, const f32x4& sb, const int64_t* kra,
                                                const int64_t* krb, int gz, float zscale, f32x4 (&oacc)[NDT],
@@ -522,6 +537,7 @@ __device__ __forceinline__ void attn_pv2(const uint4* ka, const uint4* kb, int c
         for (int j = 0; j < PG; ++j)
             oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[grp & 1][j], pb, oacc[PG * grp + j], 0, 0, 0);
     }
+    mfma_pipeline_hint<NDT, 2, 8>();
 }
 
 template <int D, bool QF32>
@@ -972,6 +988,7 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
             const uint4* kb = ktile[(c + 1) % PC_TILES];
             const f32x4 sa = attn_scores<D, false>(ka, cz, gz, qhi, qlo);
             const f32x4 sb = attn_scores<D, false>(kb, cz, gz, qhi, qlo);
+            mfma_pipeline_hint<2 * NBLK, 1, 8>();
             const f16x8 pb = attn_weights2<NDT>(sa, sb, krow + c * CHUNK_KEYS, krow + (c + 1) * CHUNK_KEYS, gz,
                                                 zscale, oacc, m_run, l_run);
             attn_pv2<D>(ka, kb, cz, gz, pb, oacc);
