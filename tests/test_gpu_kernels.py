@@ -207,6 +207,8 @@ def _topk_case(rows, n, k, kind, tag):
         s = inputs.small_ints((rows, n), tag, -40, 40, dtype=torch.float32).numpy()
     elif kind == "coarse":  # a few equal keys per value: short runs of ties at the threshold
         s = np.round(inputs.normal((rows, n), tag).numpy() * 120) / 4
+    elif kind == "empty":  # no valid entry in any row: every output is -1
+        return np.full((rows, n), -np.inf, np.float32)
     else:  # "flat": one value everywhere -> the threshold bin overflows any candidate buffer
         s = np.full((rows, n), 1.5, np.float32)
         s[:, ::5] = 2.5
@@ -223,7 +225,9 @@ def _topk_case(rows, n, k, kind, tag):
     # one-workgroup path: threshold bin resolved by ranking, by the radix fallback
     # (long ties, k > 1024), k at the bound's limit, single key, short rows
     (3, 16384, 512, "coarse"), (2, 16384, 512, "ties"), (2, 16384, 512, "flat"), (4, 16384, 1024, "normal"),
-    (4, 16384, 1025, "coarse"), (2, 16384, 1, "normal"), (3, 5000, 512, "coarse"), (2, 600, 512, "normal")])
+    (4, 16384, 1025, "coarse"), (2, 16384, 1, "normal"), (3, 5000, 512, "coarse"), (2, 600, 512, "normal"),
+    # rows without a single valid entry, on both paths
+    (3, 16384, 512, "empty"), (2, 100000, 512, "empty")])
 def test_topk_bit_exact(rows, n, k, kind):
     s = _topk_case(rows, n, k, kind, f"tk{rows}_{n}_{k}_{kind}")
     out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
