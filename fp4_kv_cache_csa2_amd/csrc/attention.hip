@@ -1002,20 +1002,21 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
 }
 
 // Merge the split partials: exact log-sum-exp combination, optionally together
-// with the (o, lse) already in the output.  One workgroup = one row x one
-// 16-head group x 4 of its 16-column tiles; thread = one lane-order float4
+// with the (o, lse) already in the output.  One workgroup (one wave: many
+// small workgroups spread the loads over all CUs) = one row x one 16-head
+// group x one of its 16-column tiles; thread = one lane-order float4
 // (head 16 hg + lane % 16, columns 16 dt + 4 (lane / 16) .. +3).  Splits are
 // taken NB at a time (all loads of a batch issued before any arithmetic) with
 // a running maximum across batches.
 template <int NB>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          const float* __restrict__ lse_prev, int nsplit, int H, int D,
                                                          int merge, float* __restrict__ o, float* __restrict__ lse) {
     const int64_t row = blockIdx.x;
     const int hg = blockIdx.y;
     const int t = threadIdx.x, lane = t & 63;
-    const int dt = blockIdx.z * 4 + (t >> 6);
+    const int dt = blockIdx.z;
     const int h = 16 * hg + (lane & 15);
     const int c = 16 * dt + 4 * (lane >> 4);
     float* op = o + (row * H + h) * D + c;
@@ -1171,7 +1172,7 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
 #undef CSA2_ATTN
 #undef CSA2_ATTN_NW
     if (p.nsplit > 1) {
-        const dim3 mg((unsigned)rows, (unsigned)(H / 16), (unsigned)(D / 64)), mb(256);
+        const dim3 mg((unsigned)rows, (unsigned)(H / 16), (unsigned)(D / 16)), mb(64);
         if (p.nsplit <= 4)
             attn_merge_kernel<4><<<mg, mb, 0, stream>>>(p.part_o, p.part_ml, p.lse_prev, p.nsplit, H, D, p.merge, o,
                                                          lse);
