@@ -30,7 +30,7 @@ LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
     w.pool_scores = off;
     off = align256(off + (size_t)(rows * 8 * (int64_t)P) * 4);
     // two selections (entries, pool blocks) may run side by side
-    const size_t tk = (n_max > TOPK_SMALL_N || 8 * (int64_t)P > TOPK_SMALL_N) ? 2 * topk_large_ws_bytes(rows) : 0;
+    const size_t tk = (n_max > TOPK_ONEWG_N || 8 * (int64_t)P > TOPK_ONEWG_N) ? 2 * topk_large_ws_bytes(rows) : 0;
     w.topk = off;
     w.topk_bytes = tk;
     off = align256(off + tk);
@@ -97,8 +97,8 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
         // Top-K entries and pool blocks: large selections share the zero /
         // split / finish launches; their first-digit histograms come out of the scan
         const int32_t n = a->n_max, nb = (int32_t)((a->n_max + 7) / 8);
-        const bool e_large = n > TOPK_SMALL_N;
-        const bool b_large = a->build_pool && nb > TOPK_SMALL_N;  // implies e_large
+        const bool e_large = n > TOPK_ONEWG_N;
+        const bool b_large = a->build_pool && nb > TOPK_ONEWG_N;  // implies e_large
         TopkSegs segs{};
         segs.rows = rows32;
         TopkSeg* se = nullptr;

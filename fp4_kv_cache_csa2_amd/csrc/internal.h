@@ -9,7 +9,8 @@
 namespace csa2 {
 
 constexpr int TOPK_KMAX = 2048;       // largest k
-constexpr int TOPK_SMALL_N = 16384;   // rows up to this length are selected by one workgroup
+constexpr int TOPK_SMALL_N = 16384;   // one workgroup per row, 16 keys per thread
+constexpr int TOPK_ONEWG_N = 32768;   // rows up to this length are selected by one workgroup (32 keys per thread)
 constexpr int TOPK_CAP = 8192;        // candidates kept per row from the threshold bin
 constexpr int NBINS1 = 2048;          // first digit: top 11 bits of the order-preserving key
 
@@ -57,7 +58,7 @@ void topk_launch_zero(const TopkSegs& segs, hipStream_t stream);
 void topk_launch_hist(const TopkSegs& segs, hipStream_t stream);
 // threshold split + candidate select + sorted output
 void topk_launch_select(const TopkSegs& segs, hipStream_t stream);
-// one workgroup per row (n <= TOPK_SMALL_N); lim as in TopkSeg
+// one workgroup per row (n <= TOPK_ONEWG_N); lim as in TopkSeg
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
                        hipStream_t stream, const int32_t* lim = nullptr, int lim_div = 1);
 

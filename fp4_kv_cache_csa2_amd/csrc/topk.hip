@@ -12,8 +12,9 @@
 // number of elements still needed.
 //
 // Two paths:
-//  * n <= 16384 (Reindex pools, short contexts): one 1024-thread workgroup per
-//    row holds 16 consecutive keys per thread in registers, narrows the
+//  * n <= 32768 (Reindex pools, short contexts, prefill rows): one 1024-thread
+//    workgroup per row holds 16 (n <= 16384) or 32 consecutive keys per thread
+//    in registers, narrows the
 //    selection to the keys above a sampled lower bound, runs the passes with
 //    an LDS histogram over those, and writes the selection in position order
 //    with one block-wide prefix sum (no sort).
@@ -33,7 +34,6 @@ namespace {
 
 constexpr int WG = 1024;        // single-row workgroup
 constexpr int NW = WG / 64;     // its wavefronts
-constexpr int E_SMALL = TOPK_SMALL_N / WG;  // keys per thread in the small path (16)
 constexpr int PWG = 256;        // threads of the grid-wide passes
 constexpr int CHUNK = 4096;     // positions per workgroup in the histogram pass (16 per thread)
 constexpr int CCHUNK = 16384;   // positions per workgroup in the split pass (64 per thread): few workgroups
@@ -259,12 +259,15 @@ __device__ void emit_sorted(const int* sel, int total, int n, int k, SelectLds& 
 // than 64 keys (long runs of equal scores), a radix select over all keys runs.
 constexpr int TIE_CAP = 64;                 // keys of the threshold bin ranked directly
 
+// E_SMALL keys per thread: 16 (n <= 16384) or 32 (n <= 32768).
+template <int E_SMALL>
 __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict__ scores, int n, int k,
                                                         const int32_t* __restrict__ pool,
                                                         int32_t* __restrict__ out, const int32_t* __restrict__ lim,
                                                         int lim_div) {
+    static_assert(E_SMALL <= 32, "selection flags are one 32-bit word per thread");
     __shared__ SelectLds sh;
-    __shared__ int32_t pool_s[TOPK_SMALL_N / 8];  // the row's pool blocks (position -> entry map)
+    __shared__ int32_t pool_s[E_SMALL * WG / 8];  // the row's pool blocks (position -> entry map)
     __shared__ uint32_t tie_key[TIE_CAP], tie_pos[TIE_CAP];
     __shared__ uint32_t wave_t[NW], wave_m[NW];
     __shared__ uint32_t counts, tie_n;
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
         tie_n = 0u;
     }
     uint32_t key[E_SMALL];
-    // thread t owns positions 16t..16t+15 (ordered output); read them as four
+    // thread t owns positions E t .. E t + E - 1 (ordered output); read them as
     // 16-byte loads when the row is 16-byte aligned (strided scalar loads
     // thrash the vector cache and cost several microseconds here)
     if ((n & 3) == 0 && (((uintptr_t)s) & 15) == 0 && (t + 1) * E_SMALL <= nl) {
@@ -707,7 +710,10 @@ void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
 
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
                        hipStream_t stream, const int32_t* lim, int lim_div) {
-    topk_small_kernel<<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
+    if (n <= TOPK_SMALL_N)
+        topk_small_kernel<TOPK_SMALL_N / WG><<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
+    else
+        topk_small_kernel<TOPK_ONEWG_N / WG><<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
 }
 
 __global__ void zero_ranges_kernel(ZeroRanges z) {
@@ -729,7 +735,7 @@ using namespace csa2;
 
 extern "C" size_t csa2_topk_workspace_size(int32_t rows, int32_t n, int32_t k) {
     (void)k;
-    if (rows <= 0 || n <= TOPK_SMALL_N) return 0;
+    if (rows <= 0 || n <= TOPK_ONEWG_N) return 0;
     return topk_large_ws_bytes(rows);
 }
 
@@ -744,7 +750,7 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, i
     if (rows == 0) return CSA2_OK;
     CSA2_ARG(out_idx != nullptr, "topk: null out_idx");
     CSA2_ARG(n == 0 || scores != nullptr, "topk: null scores");
-    if (n <= TOPK_SMALL_N) {
+    if (n <= TOPK_ONEWG_N) {
         topk_launch_small(scores, rows, n, k, pool_blocks, out_idx, stream);
         return launch_status("topk");
     }

@@ -62,7 +62,9 @@ def test_topk_argument_errors(lib):
     assert need > 0
     assert lib.csa2_topk(FAKE, 4, 1 << 20, 512, None, FAKE, None, 0, None) == _lib.CSA2_EWORKSPACE
     assert lib.csa2_topk(FAKE, 4, 1 << 20, 512, None, FAKE, FAKE, need - 1, None) == _lib.CSA2_EWORKSPACE
-    assert lib.csa2_topk_workspace_size(64, 16384, 512) == 0  # LDS-resident path
+    assert lib.csa2_topk_workspace_size(64, 16384, 512) == 0  # one-workgroup path
+    assert lib.csa2_topk_workspace_size(64, 32768, 512) == 0
+    assert lib.csa2_topk_workspace_size(64, 32769, 512) > 0
 
 
 def test_indexer_argument_errors(lib):

@@ -227,7 +227,11 @@ def _topk_case(rows, n, k, kind, tag):
     (3, 16384, 512, "coarse"), (2, 16384, 512, "ties"), (2, 16384, 512, "flat"), (4, 16384, 1024, "normal"),
     (4, 16384, 1025, "coarse"), (2, 16384, 1, "normal"), (3, 5000, 512, "coarse"), (2, 600, 512, "normal"),
     # rows without a single valid entry, on both paths
-    (3, 16384, 512, "empty"), (2, 100000, 512, "empty")])
+    (3, 16384, 512, "empty"), (2, 100000, 512, "empty"),
+    # one workgroup with 32 keys per thread (16384 < n <= 32768), and the first
+    # length past it
+    (3, 32768, 512, "normal"), (2, 20000, 512, "ties"), (2, 32768, 2048, "coarse"), (2, 32768, 512, "flat"),
+    (2, 16392, 1, "normal"), (4, 30001, 1024, "coarse"), (2, 32768, 512, "empty"), (2, 32769, 512, "normal")])
 def test_topk_bit_exact(rows, n, k, kind):
     s = _topk_case(rows, n, k, kind, f"tk{rows}_{n}_{k}_{kind}")
     out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
@@ -241,18 +245,19 @@ def test_topk_bit_exact(rows, n, k, kind):
         np.testing.assert_array_equal(got[r], oracle.topk(s[r], k), err_msg=f"row {r}")
 
 
-def test_topk_with_pool_map():
-    rows, P, k = 3, 2048, 512
+@pytest.mark.parametrize("P", [2048, 4096])
+def test_topk_with_pool_map(P):
+    rows, k = 3, 512
     n = 8 * P
     s = inputs.normal((rows, n), "tkpool").numpy()
     pool = np.full((rows, P), -1, np.int32)
     rng = np.random.default_rng(1)
     for r in range(rows):
-        nb = [2048, 1500, 10][r]
+        nb = [P, 1500, 10][r]
         pool[r, :nb] = np.sort(rng.choice(200000, nb, replace=False))
         s[r, 8 * nb:] = -np.inf
     out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
-    case("topk pool map")
+    case(f"topk pool map P={P}")
     api.csa2_topk(torch.from_numpy(s).to(DEV), k, out, pool_blocks=torch.from_numpy(pool).to(DEV))
     torch.cuda.synchronize()
     for r in range(rows):
