@@ -72,11 +72,26 @@ __device__ __forceinline__ uint32_t entry_row(const IndexParams& p, int r, int b
 
 // Issue the loads of one wave block into registers.  Load i of lane l covers
 // 16-byte chunk c of entry e with i*64 + l = e*CH + c.
-template <int DI, bool REINDEX, bool CONTIG>
+// FAST: a fully visible block of a contiguous plane takes the short path below
+// (the multi-row kernel, where the per-load index arithmetic is a fifth of the
+// VALU work; the single-row scan keeps the one addressing it was tuned with).
+template <int DI, bool REINDEX, bool CONTIG, bool FAST = false>
 __device__ __forceinline__ void load_block(const IndexParams& p, int r, int b, int64_t nv, int64_t blk, int lane,
                                            uint32_t myrow, uint4 (&v)[DI / 8]) {
     constexpr int CH = DI / 8;
     const int64_t p0 = blk * EPB;
+    if (FAST && CONTIG && p0 + EPB <= min(nv, p.n_pos)) {
+        // the whole block is visible and contiguous: its 64 entries are one run
+        // of 64 DI bf16, read at a wave-uniform base + 16 lane + 1024 i (no
+        // per-load index arithmetic or masking)
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.kmap.seq_stride + p0) * DI);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * lane + 1024 * i));
+            v[i] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int L = i * 64 + lane;
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
     __shared__ float4 qbar_s[RB][DI / 4];
 
     const int t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6;
+    const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int gps = (p.Q + RB - 1) / RB;  // row groups per sequence
     const int b = blockIdx.y / gps;
     const int q0 = (blockIdx.y % gps) * RB;
@@ -284,7 +299,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
     const int64_t nbv = (min(nvmax, p.n_pos) + EPB - 1) / EPB;
     uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<false>(p, r0, b, nvmax, blk * EPB + lane);
     uint4 v[CH];
-    if (blk < nbv) load_block<DI, false, CONTIG>(p, r0, b, nvmax, blk, lane, row_next, v);
+    if (blk < nbv) load_block<DI, false, CONTIG, true>(p, r0, b, nvmax, blk, lane, row_next, v);
 
     for (int i = t; i < RB * DI; i += WAVES * 64) {
         const int rr = i / DI, c = i % DI;
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
         const int64_t nxt = blk + stride;
         if (nxt < nbv) {
             if (!CONTIG) row_next = entry_row<false>(p, r0, b, nvmax, nxt * EPB + lane);
-            load_block<DI, false, CONTIG>(p, r0, b, nvmax, nxt, lane, row_next, v);
+            load_block<DI, false, CONTIG, true>(p, r0, b, nvmax, nxt, lane, row_next, v);
         }
         const uint4* mine = my + lz * CH;
         const int sw = lz & (CH - 1);
