@@ -10,11 +10,12 @@
 // One workgroup = one query row x a range of 16-key chunks; wave w owns query
 // heads 16w..16w+15 (heads are the MFMA N dimension, keys the M dimension).
 // Per chunk the workgroup gathers 16 keys once and dequantises them in
-// registers into two fp16 LDS tiles: K row-major for S^T = K Q^T
-// (v_mfma_f32_16x16x32_f16) and V^T for O^T = V^T P^T
-// (v_mfma_f32_16x16x16_f16).  An E2M1 x E4M3 product has <= 6 significant
-// bits and lies in [2^-10, 2688], so it is exact in fp16; the E2M1 values come
-// from a byte-permute table.  The query is pre-scaled per head by a power of
+// registers into one fp16 LDS tile, K row-major: S^T = K Q^T reads it directly
+// (v_mfma_f32_16x16x32_f16), O^T = V^T P^T (v_mfma_f32_16x16x16_f16) reads V^T
+// out of the same tile with the transposing LDS read.  An E2M1 x E4M3 product
+// has <= 6 significant bits and lies in [2^-10, 2688], so it is exact in fp16;
+// the E2M1 values come from the hardware FP4 conversion.  The query is
+// pre-scaled per head by a power of
 // two so that its largest element sits in [2^14, 2^15) (exact), and the scale
 // is folded into the logit scale.  The S^T accumulator layout (lane holds keys
 // 4g..4g+3 of head lane%16) is exactly the P^T operand layout of the second
