@@ -94,8 +94,8 @@ def read_traffic(kernel=SCAN_KERNEL):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="hier_decode_b4_n1m")
     ap.add_argument("--scan-reps", type=int, default=21, help="timed launches of the indexer scan")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
