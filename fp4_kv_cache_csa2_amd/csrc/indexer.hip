@@ -72,19 +72,28 @@ __device__ __forceinline__ uint32_t entry_row(const IndexParams& p, int r, int b
 
 // Issue the loads of one wave block into registers.  Load i of lane l covers
 // 16-byte chunk c of entry e with i*64 + l = e*CH + c.
-// FAST: a fully visible block of a contiguous plane takes the short path below
-// (the multi-row kernel, where the per-load index arithmetic is a fifth of the
-// VALU work; the single-row scan keeps the one addressing it was tuned with).
+// A block whose 64 entries are all visible and lie in one run of the K plane:
+// a contiguous plane, or pages of at least 64 entries (blocks are 64-aligned,
+// so they never straddle such a page).
+template <bool CONTIG>
+__device__ __forceinline__ bool run_block(const IndexParams& p, int64_t nv, int64_t blk) {
+    return (CONTIG || p.kmap.page_shift >= 6) && blk * EPB + EPB <= min(nv, p.n_pos);
+}
+
+// FAST: a run block (Full mode) takes the short path below; used by the
+// multi-row kernel, where the per-load index arithmetic is a fifth of the VALU
+// work, and by the paged single-row scan (the contiguous single-row scan keeps
+// the one addressing it was tuned with).
 template <int DI, bool REINDEX, bool CONTIG, bool FAST = false>
 __device__ __forceinline__ void load_block(const IndexParams& p, int r, int b, int64_t nv, int64_t blk, int lane,
                                            uint32_t myrow, uint4 (&v)[DI / 8]) {
     constexpr int CH = DI / 8;
     const int64_t p0 = blk * EPB;
-    if (FAST && CONTIG && p0 + EPB <= min(nv, p.n_pos)) {
-        // the whole block is visible and contiguous: its 64 entries are one run
-        // of 64 DI bf16, read at a wave-uniform base + 16 lane + 1024 i (no
-        // per-load index arithmetic or masking)
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(p.k + ((int64_t)b * p.kmap.seq_stride + p0) * DI);
+    if (FAST && !REINDEX && run_block<CONTIG>(p, nv, blk)) {
+        // 64 entries in one run of 64 DI bf16, read at a wave-uniform base +
+        // 16 lane + 1024 i (no per-load index arithmetic, shuffles or masking)
+        const int64_t row0 = CONTIG ? (int64_t)b * p.kmap.seq_stride + p0 : phys_row(p.kmap, b, p0);
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(p.k + row0 * DI);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * lane + 1024 * i));
@@ -139,9 +148,12 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     const int64_t stride = (int64_t)gridDim.x * WAVES;
     int64_t blk = (int64_t)blockIdx.x * WAVES + w;
     const int64_t nbv = REINDEX ? p.blocks_per_row : (min(nv, p.n_pos) + EPB - 1) / EPB;
-    uint32_t row_next = (CONTIG || blk >= nbv) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
+    // paged Full scan: run blocks skip the per-lane row lookups
+    constexpr bool PFAST = !CONTIG && !REINDEX;
+    bool full = PFAST && blk < nbv && run_block<CONTIG>(p, nv, blk);
+    uint32_t row_next = (CONTIG || blk >= nbv || full) ? 0u : entry_row<REINDEX>(p, r, b, nv, blk * EPB + lane);
     uint4 v[CH];
-    if (blk < nbv) load_block<DI, REINDEX, CONTIG>(p, r, b, nv, blk, lane, row_next, v);
+    if (blk < nbv) load_block<DI, REINDEX, CONTIG, PFAST>(p, r, b, nv, blk, lane, row_next, v);
 
     // qbar_c = sum over heads, ascending, fp32
     if (t < DI) {
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     // (Full mode: only blocks holding a visible entry are read)
     for (; blk < nbv; blk += stride) {
         const int64_t pos = blk * EPB + lane;
-        const bool valid = CONTIG ? (pos < nv && pos < p.n_pos) : (row_next != NOROW);
+        const bool valid = CONTIG ? (pos < nv && pos < p.n_pos) : (full || row_next != NOROW);
         // An opaque zero, fresh every block: LDS addresses are recomputed each
         // block (two ALU ops each) instead of being hoisted into ~48 registers.
         int z;
@@ -180,8 +192,9 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
         // next block's loads fly while this one is scored
         const int64_t nxt = blk + stride;
         if (nxt < nbv) {
-            if (!CONTIG) row_next = entry_row<REINDEX>(p, r, b, nv, nxt * EPB + lane);
-            load_block<DI, REINDEX, CONTIG>(p, r, b, nv, nxt, lane, row_next, v);
+            full = PFAST && run_block<CONTIG>(p, nv, nxt);
+            if (!CONTIG && !full) row_next = entry_row<REINDEX>(p, r, b, nv, nxt * EPB + lane);
+            load_block<DI, REINDEX, CONTIG, PFAST>(p, r, b, nv, nxt, lane, row_next, v);
         }
         // one entry per lane: sequential FMA chain over channels.  qbar is
         // re-read from LDS (a broadcast) each block rather than held in 128

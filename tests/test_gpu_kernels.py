@@ -118,11 +118,10 @@ def test_append_token(paged, n_layers, with_k, xdtype):
 
 
 # --------------------------------------------------------------------------- indexer
-def _k_view(B, n_max, D_i, tag, paged):
+def _k_view(B, n_max, D_i, tag, paged, ps=64):
     K = inputs.normal((B, n_max, D_i), tag, dtype=torch.bfloat16)
     if not paged:
         return K, api.IndexerK(K.reshape(B * n_max, D_i).to(DEV), D_i, n_max)
-    ps = 64
     table, n_pages = inputs.random_page_table(np.full(B, n_max), ps, tag + "/pt")
     phys = torch.zeros(n_pages * ps, D_i, dtype=torch.bfloat16)
     for b in range(B):
@@ -132,16 +131,19 @@ def _k_view(B, n_max, D_i, tag, paged):
     return K, api.IndexerK(phys.to(DEV), D_i, 0, torch.from_numpy(table).to(DEV), ps)
 
 
-@pytest.mark.parametrize("D_i,H_i,paged", [(128, 8, False), (64, 4, False), (128, 8, True)])
-def test_index_full_bit_exact(D_i, H_i, paged):
+@pytest.mark.parametrize("D_i,H_i,paged,ps", [(128, 8, False, 0), (64, 4, False, 0), (128, 8, True, 64),
+                                             (128, 8, True, 16), (128, 8, True, 256)])
+def test_index_full_bit_exact(D_i, H_i, paged, ps):
+    """Pages of 64 entries or more hold whole 64-entry blocks (one-run loads);
+    16-entry pages take the per-entry row lookup."""
     B, Q, n_max = 2, 3, 5000
-    K, kview = _k_view(B, n_max, D_i, f"ifK{D_i}{paged}", paged)
+    K, kview = _k_view(B, n_max, D_i, f"ifK{D_i}{paged}", paged, ps or 64)
     q = inputs.normal((B, Q, H_i, D_i), f"ifq{D_i}", dtype=torch.bfloat16)
     n_vis = np.array([[5000, 4999, 0], [1, 257, 3333]], np.int32)
     scores = torch.empty(B * Q, n_max, device=DEV)
     nb = (n_max + 7) // 8
     bmax = torch.empty(B * Q, nb, device=DEV)
-    case(f"index_full D_i={D_i} paged={paged}")
+    case(f"index_full D_i={D_i} paged={paged} ps={ps}")
     api.csa2_index_full(q.to(DEV), kview, torch.from_numpy(n_vis).to(DEV), n_max, scores, bmax)
     torch.cuda.synchronize()
     s, bm = to_np(scores), to_np(bmax)
