@@ -1070,7 +1070,10 @@ int choose_nsplit(int64_t rows, int nchunks) {
     // one resident workgroup per CU (its LDS ring holds one): about 256
     // workgroups run in a single round, more only add rounds and partials
     int64_t want = (256 + rows - 1) / rows;
-    int64_t by_chunks = (nchunks + 1) / 2;   // at least two chunks per split
+    // at least RING chunks per split: a workgroup has RING chunks in flight, so
+    // a shorter split costs the same time and only adds partials to write and
+    // merge (measured at 4 and 8 decode rows)
+    int64_t by_chunks = (nchunks + RING - 1) / RING;
     int64_t s = want < by_chunks ? want : by_chunks;
     if (s > MAX_SPLIT) s = MAX_SPLIT;
     if (s < 1) s = 1;

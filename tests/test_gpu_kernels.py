@@ -299,6 +299,9 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
 @pytest.mark.parametrize("B,Q,H,D,K,qdtype,window", [
     (2, 1, 64, 512, 512, torch.bfloat16, 128), (1, 1, 16, 128, 512, torch.float32, 128),
     (3, 2, 32, 256, 100, torch.bfloat16, 128), (600, 1, 16, 128, 48, torch.bfloat16, 128),
+    # long lists at one or two rows: 16 splits, and 32 splits merged in two
+    # batches of at most 24
+    (2, 1, 32, 256, 1024, torch.float32, 128), (1, 1, 64, 512, 2048, torch.bfloat16, 128),
     # many rows at D = 512, H = 64 (rows sampled): bf16 queries take the
     # producer/consumer kernel (chunks in pairs; 13 sparse chunks and a
     # one-chunk window exercise its padding chunk), fp32 queries the
