@@ -22,10 +22,10 @@
 // MFMA, so P never leaves registers.  Softmax is online in the log2 domain with
 // a lazy maximum: the running maximum moves (and O is rescaled) only when a
 // chunk exceeds it by more than 2^8, so P <= 256 stays well inside fp16.  Few
-// rows (decode) split the keys over several workgroups whose normalised
-// partials (o, lse) are merged by a second kernel; many rows without a split
-// (prefill) at D = 512, H = 64 take a producer/consumer variant
-// (attn_pc_kernel) in which four waves dequantise while four multiply.
+// rows (decode) split the keys over several workgroups whose unnormalised
+// partials are merged by a second kernel.  At D = 512, H = 64 with bf16
+// queries a producer/consumer variant (attn_pc_kernel) runs instead, split or
+// not: four waves dequantise while four multiply.
 #include "internal.h"
 
 namespace csa2 {
@@ -595,6 +595,23 @@ __device__ __forceinline__ void attn_store(const AttnParams& p, int64_t row, int
     if (write_lse && g == 0) p.lse[row * p.H + head] = lse_out;
 }
 
+// Unnormalised partial of one key split (a wave's 16 heads): each lane's
+// 4 x D/16 accumulators stored contiguously (full 1 KB per wave instruction),
+// the running max and sum per head, and for split 0 a snapshot of the lse to
+// merge with (the merge kernel overwrites it).
+template <int D>
+__device__ __forceinline__ void attn_store_partial(const AttnParams& p, int64_t row, int split, int w, int lane,
+                                                   int head, const f32x4 (&oacc)[D / 16], float m_run, float l_run) {
+    constexpr int NDT = D / 16;
+    float* po = p.part_o + ((row * p.nsplit + split) * p.H + 16 * w) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = oacc[dt];
+    if ((lane >> 4) == 0) {
+        p.part_ml[(row * p.nsplit + split) * p.H + head] = make_float2(m_run, l_run);
+        if (p.merge && split == 0) p.lse_prev[row * p.H + head] = p.lse[row * p.H + head];
+    }
+}
+
 template <int D, bool QF32, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
     constexpr int RG = RING;
@@ -736,32 +753,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
         attn_chunk<D, QF32>(ktile, kr, cz, gz, qhi, qlo, zscale, oacc, m_run, l_run);
     }
 
-    if (p.nsplit > 1) {
-        // ---- unnormalised partial of this key range, each lane's 4 x D/16
-        // accumulators stored contiguously (full 1 KB per wave instruction)
-        float* po = p.part_o + ((row * p.nsplit + split) * p.H + 16 * w) * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = oacc[dt];
-        if (g == 0) p.part_ml[(row * p.nsplit + split) * p.H + head] = make_float2(m_run, l_run);
-        // snapshot of the lse to merge with: the merge kernel overwrites it
-        if (p.merge && split == 0 && g == 0) p.lse_prev[row * p.H + head] = p.lse[row * p.H + head];
-        return;
-    }
-    attn_store<D>(p, row, head, g, oacc, m_run, l_run);
+    if (p.nsplit > 1)
+        attn_store_partial<D>(p, row, split, w, lane, head, oacc, m_run, l_run);
+    else
+        attn_store<D>(p, row, head, g, oacc, m_run, l_run);
 }
 
-// ---- Many query rows at D = 512, H = 64 with bf16 queries and no key split
-// (prefill).  One workgroup of eight waves per CU.  Waves 0-3 consume as in
-// attn_kernel (wave w: heads 16w..16w+15); waves 4-7 produce: producer p
-// copies keys 4p..4p+3 of each chunk global -> LDS, PC_RING chunks ahead, and
-// dequantises exactly those keys into one of three tile buffers.  A producer
-// only reads the copies it issued itself, so it waits on its own
-// vector-memory counter and never on another wave; one workgroup barrier per
-// chunk hands a filled buffer to the consumers.  The consumers are pipelined
-// one chunk deep: while chunk k's PV products run on the matrix cores, they
-// issue chunk k+1's score products and compute its softmax weights, and the
-// producers dequantise chunk k+2 -- VALU, LDS and MFMA work of different
-// chunks overlap on every SIMD.
+// ---- D = 512, H = 64 with bf16 queries: prefill (no key split) and decode
+// (keys split over workgroups, partials as in attn_kernel).  One workgroup of
+// eight waves per CU.  Waves 0-3 consume (wave w: heads 16w..16w+15); waves
+// 4-7 produce: producer p copies keys 4p..4p+3 of each chunk global -> LDS,
+// PC_RING chunks ahead, and dequantises exactly those keys into one of
+// PC_TILES tile buffers.  A producer only reads the copies it issued itself,
+// so it waits on its own vector-memory counter and never on another wave.
+// The consumers take the chunks in pairs: S for both chunks, one softmax over
+// their 32 keys and one PV product over them on the K = 32 MFMA, while the
+// producers fill the other pair's buffers; one workgroup barrier per pair
+// hands the buffers over.  An odd chunk count gets a padding chunk whose keys
+// have no row (weight exactly 0).
 constexpr int PC_RING = 4;
 constexpr int PC_TILES = 4;  // two pairs of chunk tiles
 constexpr int PC_CONS = 4;   // consumer waves (16 heads each)
@@ -877,6 +886,9 @@ __device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, ui
         : "memory");
 }
 
+// SPLIT: keys split over workgroups (partials merged afterwards); without it
+// every workgroup takes its row's whole list.
+template <bool SPLIT>
 __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     constexpr int D = PC_D, NW = PC_CONS;
     constexpr int NBLK = D / 32, NDT = D / 16, CPR = D / 8;
@@ -890,18 +902,27 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     const bool consumer = wv < NW;
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t row = blockIdx.y;
+    const int split = blockIdx.x;
     const int b = (int)(row / p.Q);
     const int head = 16 * wv + c16;  // (consumers)
     const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
+    // this workgroup's chunks: c_lo + c for local c in [0, nloc)
+    const int c_lo = SPLIT ? split * p.cps : 0;
+    const int nloc = SPLIT ? max(0, min(nchunks, c_lo + p.cps) - c_lo) : nchunks;
     // chunks are consumed in pairs; an odd count gets one padding chunk
     // whose keys have no row (finite copies of row 0, weight exactly 0)
-    const int npad = nchunks + (nchunks & 1);
+    const int npad = nloc + (nloc & 1);
     const int n_sp = p.Kp / CHUNK_KEYS;
     const int slot = p.Wp ? p.q_slot[row] : 0;
     const int wlo = max(0, slot - p.window + 1);
-    const int nk = nchunks * CHUNK_KEYS;
-    // the padding chunk is copied as the last real chunk's kind (its view is valid)
-    auto sparse_chunk = [&](int c) { return c < n_sp || (c >= nchunks && p.Wp == 0); };
+    const int nk = nloc * CHUNK_KEYS;
+    // a local chunk's kind (sparse or window); the padding chunk is copied as
+    // the kind of the chunk after the range, or past the last chunk as the
+    // last one's (either view is valid)
+    auto sparse_chunk = [&](int c) {
+        const int a = c_lo + c;
+        return a < n_sp || (a >= nchunks && p.Wp == 0);
+    };
 
     // ---- index loads first, then the consumers' query loads
     constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + CHUNK_KEYS + PC_NT - 1) / PC_NT;
@@ -909,7 +930,8 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < KR_IT; ++j) {
         const int i = tid + j * PC_NT;
-        kent[j] = (i < nk && i < p.K) ? p.idx[row * p.K + i] : -1;
+        const int kpos = c_lo * CHUNK_KEYS + i;
+        kent[j] = (i < nk && kpos < p.K) ? p.idx[row * p.K + kpos] : -1;
     }
     uint4 qraw[NBLK];
     if (consumer) {
@@ -922,12 +944,13 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     for (int j = 0; j < KR_IT; ++j) {
         const int i = tid + j * PC_NT;
         if (i >= npad * CHUNK_KEYS) break;
+        const int kpos = c_lo * CHUNK_KEYS + i;
         int64_t r = -1;
         if (i >= nk) {
-        } else if (i < p.Kp) {
+        } else if (kpos < p.Kp) {
             if (kent[j] >= 0) r = phys_row(p.kvmap, b, kent[j]);
         } else {
-            const int t = wlo + (i - p.Kp);
+            const int t = wlo + (kpos - p.Kp);
             if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
         }
         krow[i] = r;
@@ -999,7 +1022,12 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
         }
         lds_barrier();
     }
-    if (consumer) attn_store<D>(p, row, head, g, oacc, m_run, l_run);
+    if (consumer) {
+        if (SPLIT)
+            attn_store_partial<D>(p, row, split, wv, lane, head, oacc, m_run, l_run);
+        else
+            attn_store<D>(p, row, head, g, oacc, m_run, l_run);
+    }
 }
 
 // Merge the split partials: exact log-sum-exp combination, optionally together
@@ -1154,10 +1182,13 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     const dim3 block((unsigned)(4 * H));
     const bool f32 = qt == CSA2_F32;
     const int nw = H / 16;
-    // many rows without a key split at D = 512, H = 64, bf16 queries: the
-    // producer/consumer kernel (the fp32 query's extra 64 registers do not fit)
-    const bool wide = p.nsplit == 1 && rows >= 512 && D == 512 && nw == 4 && !f32;
-    if (wide) attn_pc_kernel<<<grid, dim3(PC_NT), 0, stream>>>(p);
+    // D = 512, H = 64, bf16 queries: the producer/consumer kernel, with or
+    // without a key split (the fp32 query's extra 64 registers do not fit);
+    // the split instance is separate so that the prefill one keeps its
+    // registers for the unsplit loop
+    const bool wide = D == 512 && nw == 4 && !f32;
+    if (wide && p.nsplit > 1) attn_pc_kernel<true><<<grid, dim3(PC_NT), 0, stream>>>(p);
+    if (wide && p.nsplit == 1) attn_pc_kernel<false><<<grid, dim3(PC_NT), 0, stream>>>(p);
 #define CSA2_ATTN_NW(DD, F, NWV) \
     if (!wide && nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
 #define CSA2_ATTN(DD)                                                                                   \

@@ -302,6 +302,10 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
     # long lists at one or two rows: 16 splits, and 32 splits merged in two
     # batches of at most 24
     (2, 1, 32, 256, 1024, torch.float32, 128), (1, 1, 64, 512, 2048, torch.bfloat16, 128),
+    # 5 sparse + 4 window chunks in 3 splits of 3: every split of the
+    # producer/consumer kernel pads its odd range, with a sparse, a window and
+    # a past-the-end chunk's kind
+    (100, 1, 64, 512, 80, torch.bfloat16, 64),
     # many rows at D = 512, H = 64 (rows sampled): bf16 queries take the
     # producer/consumer kernel (chunks in pairs; 13 sparse chunks and a
     # one-chunk window exercise its padding chunk), fp32 queries the
