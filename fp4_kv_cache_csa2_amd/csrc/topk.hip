@@ -54,15 +54,56 @@ struct SelectLds {
     uint32_t bin, above, total, nsel;
 };
 
+// ---- wave-wide scan and reductions on the VALU: DPP row operations and
+// row swaps, no LDS round trips (a shuffle is an LDS-unit permute with its
+// own latency, and a scan chains six of them).  Lanes a DPP operation leaves
+// without a source add the identity 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, true);
+}
+
+// inclusive prefix sum over the 64 lanes: within each 16-lane row by right
+// shifts of 1, 2, 4, 8 lanes, then the row totals carried by the row
+// broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp_src<0x111>(x);
+    x += dpp_src<0x112>(x);
+    x += dpp_src<0x114>(x);
+    x += dpp_src<0x118>(x);
+    x += dpp_src<0x142, 0xA>(x);
+    x += dpp_src<0x143, 0xC>(x);
+    return x;
+}
+
+// within each row: partners lane^1 and lane^2 (quad permutes), then the
+// mirrored half row and the mirrored row; across rows: two row swaps.  Every
+// lane ends with the wave's sum / maximum.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+    x += dpp_src<0xB1>(x);
+    x += dpp_src<0x4E>(x);
+    x += dpp_src<0x141>(x);
+    x += dpp_src<0x140>(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = (uint32_t)a[0] + (uint32_t)a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (uint32_t)b[0] + (uint32_t)b[1];
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+    x = max(x, dpp_src<0xB1>(x));
+    x = max(x, dpp_src<0x4E>(x));
+    x = max(x, dpp_src<0x141>(x));
+    x = max(x, dpp_src<0x140>(x));
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)a[0], (uint32_t)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
 // Exclusive prefix sum over the threads of the block; *total gets the sum.
 __device__ uint32_t block_excl_scan(uint32_t v, SelectLds& sh, uint32_t* total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) sh.wsum[wid] = x;
     __syncthreads();
     uint32_t base = 0, tot = 0;
@@ -87,12 +128,7 @@ __device__ void find_bin(const uint32_t* hist, SelectLds& sh, int nb, uint32_t n
         const int bin = nb - 1 - (t * per + i);
         if (bin >= 0) local += hist[bin];
     }
-    uint32_t x = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(local);
     if (lane == 63) sh.wsum[wid] = x;
     __syncthreads();
     uint32_t above = x - local;
@@ -322,12 +358,8 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
         }
         if (lane == 0) wave_t[wid] = v;
     }
-    uint32_t wm = mt;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        wm = max(wm, (uint32_t)__shfl_xor((int)wm, off));
-        nv += (uint32_t)__shfl_xor((int)nv, off);
-    }
+    const uint32_t wm = wave_umax(mt);
+    nv = wave_sum(nv);
     if (lane == 0) {
         wave_m[wid] = wm;
         atomicAdd(&counts, nv);
@@ -397,7 +429,12 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
         for (int e = 0; e < E_SMALL; ++e) pos[e] = (uint32_t)(t * E_SMALL + e);
         select_regs<E_SMALL>(key, pos, (uint32_t)k, 0, prefix, mask, sh);
     }
-    // ---- selected positions, written in position order
+    // ---- selected positions, written in position order.  Fast path: the
+    // selected composites are exactly those >= one threshold -- the ranked
+    // need-th composite of bin d, or when the whole bin is taken the bin's
+    // lowest key with the smallest position part (bin d's keys start at
+    // T + d 2^sft, which no overflow reaches: d 2^sft <= kmax - T)
+    const uint64_t cthr = (fast && mb == need) ? (uint64_t)(T + (d << sft)) << 32 : cstar;
     uint32_t fs = 0;
 #pragma unroll
     for (int e = 0; e < E_SMALL; ++e) {
@@ -405,9 +442,7 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
         if (all) {
             ok = key[e] != 0u;
         } else if (fast) {
-            const uint32_t b = (key[e] - T) >> sft;
-            ok = key[e] >= T &&
-                 (b > d || (b == d && (mb == need || composite(key[e], (uint32_t)(t * E_SMALL + e)) >= cstar)));
+            ok = composite(key[e], (uint32_t)(t * E_SMALL + e)) >= cthr;
         } else {
             ok = key[e] != 0u && (composite(key[e], (uint32_t)(t * E_SMALL + e)) & mask) >= prefix;
         }
@@ -464,7 +499,7 @@ __global__ __launch_bounds__(PWG) void topk_hist_kernel(TopkSegs segs) {
             ++cnt;
         }
     }
-    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    cnt = wave_sum(cnt);
     if ((t & 63) == 0 && cnt) atomicAdd(&sg.state[row].valid, cnt);
     __syncthreads();
     uint32_t* gh = sg.hist + row * NBINS1;
@@ -489,12 +524,7 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* lh, u
         mine[i] = lh[NBINS1 - 1 - (t * per + i)];
         local += mine[i];
     }
-    uint32_t x = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(local);
     if (lane == 63) scan[wid] = x;
     __syncthreads();
     uint32_t base = 0;
@@ -581,15 +611,11 @@ __global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
             fcand |= (uint32_t)(ok && !all && dig == d) << e;
         }
         const uint32_t mine = (uint32_t)__popc(fsel) | ((uint32_t)__popc(fcand) << 16);
-        uint32_t incl = mine;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(incl, off);
-            if ((t & 63) >= off) incl += y;
-        }
+        // (each half sums to at most 64 x 16: no carry into the other)
+        const uint32_t incl = wave_incl_scan(mine);
         uint32_t wbase = 0;
         if ((t & 63) == 63) wbase = atomicAdd(&sh[2], incl);
-        wbase = __shfl(wbase, 63);
+        wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63);
         uint32_t at_s = (wbase & 0xFFFFu) + ((incl - mine) & 0xFFFFu);
         uint32_t at_c = (wbase >> 16) + ((incl - mine) >> 16);
 #pragma unroll
