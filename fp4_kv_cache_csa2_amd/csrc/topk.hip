@@ -13,8 +13,9 @@
 //
 // Two paths:
 //  * n <= 32768 (Reindex pools, short contexts, prefill rows): one 1024-thread
-//    workgroup per row holds 16 (n <= 16384) or 32 consecutive keys per thread
-//    in registers, narrows the
+//    workgroup per row holds 4, 8, 16 or 32 consecutive keys per thread (the
+//    fewest that cover n, so that every wave holds keys) in registers,
+//    narrows the
 //    selection to the keys above a sampled lower bound, runs the passes with
 //    an LDS histogram over those, and writes the selection in position order
 //    with one block-wide prefix sum (no sort).
@@ -295,7 +296,7 @@ __device__ void emit_sorted(const int* sel, int total, int n, int k, SelectLds& 
 // than 64 keys (long runs of equal scores), a radix select over all keys runs.
 constexpr int TIE_CAP = 64;                 // keys of the threshold bin ranked directly
 
-// E_SMALL keys per thread: 16 (n <= 16384) or 32 (n <= 32768).
+// E_SMALL keys per thread: 4, 8, 16 or 32 (n up to 4096, 8192, 16384, 32768).
 template <int E_SMALL>
 __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict__ scores, int n, int k,
                                                         const int32_t* __restrict__ pool,
@@ -736,7 +737,14 @@ void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
 
 void topk_launch_small(const float* scores, int rows, int n, int k, const int32_t* pool, int32_t* out,
                        hipStream_t stream, const int32_t* lim, int lim_div) {
-    if (n <= TOPK_SMALL_N)
+    // short rows take fewer keys per thread so that every wave holds keys: a
+    // wave without any gives the sampled bound T no strength (T = 1), and the
+    // selection then falls back to the radix passes
+    if (n <= TOPK_SMALL_N / 4)
+        topk_small_kernel<TOPK_SMALL_N / 4 / WG><<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
+    else if (n <= TOPK_SMALL_N / 2)
+        topk_small_kernel<TOPK_SMALL_N / 2 / WG><<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
+    else if (n <= TOPK_SMALL_N)
         topk_small_kernel<TOPK_SMALL_N / WG><<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);
     else
         topk_small_kernel<TOPK_ONEWG_N / WG><<<rows, WG, 0, stream>>>(scores, n, k, pool, out, lim, lim_div);

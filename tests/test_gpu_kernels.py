@@ -228,6 +228,9 @@ def _topk_case(rows, n, k, kind, tag):
     # (long ties, k > 1024), k at the bound's limit, single key, short rows
     (3, 16384, 512, "coarse"), (2, 16384, 512, "ties"), (2, 16384, 512, "flat"), (4, 16384, 1024, "normal"),
     (4, 16384, 1025, "coarse"), (2, 16384, 1, "normal"), (3, 5000, 512, "coarse"), (2, 600, 512, "normal"),
+    # short rows with 4 and 8 keys per thread (up to 4096 and 8192 positions)
+    (3, 4096, 512, "normal"), (3, 4096, 512, "flat"), (2, 4096, 2048, "normal"), (2, 4097, 512, "ties"),
+    (2, 8192, 512, "ties"), (2, 8192, 1024, "coarse"),
     # rows without a single valid entry, on both paths
     (3, 16384, 512, "empty"), (2, 100000, 512, "empty"),
     # one workgroup with 32 keys per thread (16384 < n <= 32768), and the first
