@@ -3,6 +3,7 @@
 // scores), the scan launcher with those histograms, and the attention
 // launcher used by both the standalone entry points and the layer dispatcher.
 #pragma once
+#include <cstddef>
 
 #include "common.h"
 
@@ -22,11 +23,16 @@ __device__ __forceinline__ uint32_t key32(float s) {
 }
 
 struct TopkRowState {
-    uint32_t valid;   // valid (finite) positions of the row
     uint32_t n_sel;   // positions above the threshold bin (definitely selected)
     uint32_t n_cand;  // positions inside the threshold bin
+    uint32_t valid;   // valid (finite) positions of the row
     uint32_t digit;   // the threshold bin
 };
+// n_sel and n_cand form one 8-byte word: a split workgroup reserves room in
+// both lists with a single 64-bit atomic (workspaces are 16-byte aligned)
+static_assert(sizeof(TopkRowState) == 16 && offsetof(TopkRowState, n_sel) == 0 &&
+                  offsetof(TopkRowState, n_cand) == 4,
+              "list counters must share one 8-byte word");
 
 // One selection problem: rows x n scores -> rows x k indices.  The last five
 // pointers are carved from a workspace by topk_carve.

@@ -635,11 +635,19 @@ __global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
     __syncthreads();
     const uint32_t ns = sh[2] & 0xFFFFu, nc = sh[2] >> 16;
     if (t == 0) {
-        sh[4] = ns ? atomicAdd(&sg.state[row].n_sel, ns) : 0u;
         // a local overflow pushes the row's count past the capacity: the finish
         // pass then selects from the whole row instead of the candidate list
         const uint32_t add = nc > (uint32_t)LCAP ? (uint32_t)TOPK_CAP + 1u : nc;
-        sh[5] = add ? atomicAdd(&sg.state[row].n_cand, add) : 0u;
+        // both lists reserved by one 64-bit atomic (n_sel low, n_cand high): the
+        // row's workgroups queue on one counter once, not twice.  Neither half
+        // carries into the other: n_sel stays <= k, n_cand below
+        // (n / CCHUNK + 1) (TOPK_CAP + 1) < 2^32
+        uint64_t both = 0;
+        if (ns | add)
+            both = atomicAdd(reinterpret_cast<unsigned long long*>(&sg.state[row].n_sel),
+                             ((unsigned long long)add << 32) | ns);
+        sh[4] = (uint32_t)both;
+        sh[5] = (uint32_t)(both >> 32);
     }
     __syncthreads();
     int* sel = sg.sel + row * TOPK_KMAX + sh[4];
