@@ -509,14 +509,16 @@ __global__ __launch_bounds__(PWG) void topk_hist_kernel(TopkSegs segs) {
 }
 
 // Threshold bin of a row from its global histogram (NT threads, NBINS1 / NT
-// bins each): the histogram is read with coalesced loads into LDS first.
+// bins each): hv holds bins i NT + t of the histogram, read by the caller with
+// coalesced loads (issued before its own loads, so the search does not wait
+// behind them); they are staged in LDS first.
 template <int NT>
-__device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* lh, uint32_t* scan, uint32_t* d_out,
-                              uint32_t* above_out) {
+__device__ void row_threshold(const uint32_t (&hv)[NBINS1 / NT], uint32_t need, uint32_t* lh, uint32_t* scan,
+                              uint32_t* d_out, uint32_t* above_out) {
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     constexpr int per = NBINS1 / NT;
 #pragma unroll
-    for (int i = 0; i < per; ++i) lh[i * NT + t] = gh[i * NT + t];
+    for (int i = 0; i < per; ++i) lh[i * NT + t] = hv[i];
     __syncthreads();
     uint32_t mine[per];
     uint32_t local = 0;
@@ -545,6 +547,10 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t need, uint32_t* lh, u
 // Threshold split of one chunk.  Positions above the threshold bin go to the
 // row's selection list, positions inside it to the candidate list; both are
 // gathered in LDS first, so each list costs one global atomic per workgroup.
+// VEC: every segment's rows are 16-byte aligned with n a multiple of 4 (the
+// launcher checks), so scores are read as 16-byte groups without a per-thread
+// branch (a branch makes the compiler wait for every load at its join).
+template <bool VEC>
 __global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
     __shared__ uint32_t scan[CWG / 64];
     __shared__ uint32_t sh[6];
@@ -560,7 +566,12 @@ __global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
     const int lo = blockIdx.x * CCHUNK;
     const int hi = min(lim, lo + CCHUNK);
     const float* s = sg.scores + row * (int64_t)sg.n;
-    const bool vec = (sg.n & 3) == 0 && (((uintptr_t)s) & 15) == 0;  // (i + 3 < hi is checked per load)
+    // the row's valid count and histogram first: the threshold search needs
+    // them before any score (loads complete in order)
+    const uint32_t valid = sg.state[row].valid;
+    uint32_t hv[NBINS1 / CWG];
+#pragma unroll
+    for (int i = 0; i < NBINS1 / CWG; ++i) hv[i] = sg.hist[row * NBINS1 + i * CWG + t];
     // every position of this thread is loaded before any is classified: one
     // memory round trip, overlapping the threshold search; round rd covers
     // positions lo + rd*CWG*16 + (e*CWG + t)*4 + j
@@ -569,27 +580,36 @@ __global__ __launch_bounds__(CWG) void topk_compact_kernel(TopkSegs segs) {
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
         const int base = lo + rd * CWG * 16;
+        if (VEC) {
+            // a group starting below n lies inside the row (n and i are
+            // multiples of 4); one starting at or past n reads the row's last
+            // group instead, and every position at or past hi is masked
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = base + (e * CWG + t) * 4;  // 4 consecutive positions
-            if (vec && i + 3 < hi) {
-                const float4 f = *reinterpret_cast<const float4*>(s + i);
-                va[rd][4 * e] = f.x;
-                va[rd][4 * e + 1] = f.y;
-                va[rd][4 * e + 2] = f.z;
-                va[rd][4 * e + 3] = f.w;
-            } else {
+            for (int e = 0; e < 4; ++e) {
+                const int i = base + (e * CWG + t) * 4;
+                const float4 f = *reinterpret_cast<const float4*>(s + min(i, sg.n - 4));
+                va[rd][4 * e] = i < hi ? f.x : -INFINITY;
+                va[rd][4 * e + 1] = i + 1 < hi ? f.y : -INFINITY;
+                va[rd][4 * e + 2] = i + 2 < hi ? f.z : -INFINITY;
+                va[rd][4 * e + 3] = i + 3 < hi ? f.w : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = base + (e * CWG + t) * 4;  // 4 consecutive positions
 #pragma unroll
                 for (int j = 0; j < 4; ++j) va[rd][4 * e + j] = (i + j < hi) ? s[i + j] : -INFINITY;
             }
         }
     }
+    // keep the loads here, ahead of the threshold search (a compiler barrier,
+    // not a wait: the values are awaited where they are first used)
+    asm volatile("" ::: "memory");
     if (t < 2) sh[2 + t] = 0u;
-    const uint32_t valid = sg.state[row].valid;
     const bool all = valid <= (uint32_t)sg.k;
     uint32_t d = 0;
     if (!all) {
-        row_threshold<CWG>(sg.hist + row * NBINS1, (uint32_t)sg.k, lh, scan, &sh[0], &sh[1]);
+        row_threshold<CWG>(hv, (uint32_t)sg.k, lh, scan, &sh[0], &sh[1]);
         d = sh[0];
         if (blockIdx.x == 0 && t == 0) sg.state[row].digit = d;
     }
@@ -739,7 +759,14 @@ void topk_launch_hist(const TopkSegs& segs, hipStream_t stream) {
 void topk_launch_select(const TopkSegs& segs, hipStream_t stream) {
     int chunks = 0;
     for (int i = 0; i < segs.nseg; ++i) chunks = max(chunks, (segs.seg[i].n + CCHUNK - 1) / CCHUNK);
-    topk_compact_kernel<<<dim3((unsigned)chunks, (unsigned)(segs.rows * segs.nseg)), CWG, 0, stream>>>(segs);
+    bool vec = true;
+    for (int i = 0; i < segs.nseg; ++i)
+        vec = vec && segs.seg[i].n >= 4 && (segs.seg[i].n & 3) == 0 && (((uintptr_t)segs.seg[i].scores) & 15) == 0;
+    const dim3 grid((unsigned)chunks, (unsigned)(segs.rows * segs.nseg));
+    if (vec)
+        topk_compact_kernel<true><<<grid, CWG, 0, stream>>>(segs);
+    else
+        topk_compact_kernel<false><<<grid, CWG, 0, stream>>>(segs);
     topk_finish_kernel<<<(unsigned)(segs.rows * segs.nseg), WG, 0, stream>>>(segs);
 }
 
