@@ -692,22 +692,38 @@ __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
     const TopkSeg& sg = segs.seg[sgi];
     const int t = threadIdx.x;
     const TopkRowState st = sg.state[row];
-    for (int i = t; i < TOPK_KMAX; i += WG) sel[i] = (i < (int)st.n_sel) ? sg.sel[row * TOPK_KMAX + i] : 0x7FFFFFFF;
+    const bool all = st.valid <= (uint32_t)sg.k;
+    const bool from_list = !all && st.n_cand <= (uint32_t)TOPK_CAP;
+    // the selected list and the candidates are loaded together, before any
+    // wait: unconditional loads at clamped (in-bounds) indices, masked after,
+    // so that no branch makes the compiler wait for one before issuing the other
+    int selv[TOPK_KMAX / WG];
+#pragma unroll
+    for (int j = 0; j < TOPK_KMAX / WG; ++j) selv[j] = sg.sel[row * TOPK_KMAX + t + j * WG];
+    uint32_t key[E_CAND], pos[E_CAND];
+#pragma unroll
+    for (int e = 0; e < E_CAND; ++e) {
+        key[e] = sg.ckey[row * TOPK_CAP + e * WG + t];
+        pos[e] = sg.cpos[row * TOPK_CAP + e * WG + t];
+    }
+#pragma unroll
+    for (int j = 0; j < TOPK_KMAX / WG; ++j) {
+        const int i = t + j * WG;
+        sel[i] = i < (int)st.n_sel ? selv[j] : 0x7FFFFFFF;
+    }
     for (int i = t; i < NBINS1; i += WG) sh.hist[1][i] = 0u;
     if (t == 0) sh.nsel = st.n_sel;
     __syncthreads();
-    const bool all = st.valid <= (uint32_t)sg.k;
     if (!all) {
         const uint32_t need = (uint32_t)sg.k - st.n_sel;
         uint64_t prefix = (uint64_t)st.digit << 53;
         uint64_t mask = (uint64_t)0x7FF << 53;
-        if (st.n_cand <= (uint32_t)TOPK_CAP) {
-            uint32_t key[E_CAND], pos[E_CAND];
+        if (from_list) {
 #pragma unroll
             for (int e = 0; e < E_CAND; ++e) {
-                const int i = e * WG + t;
-                key[e] = i < (int)st.n_cand ? sg.ckey[row * TOPK_CAP + i] : 0u;
-                pos[e] = i < (int)st.n_cand ? sg.cpos[row * TOPK_CAP + i] : 0u;
+                const bool in = e * WG + t < (int)st.n_cand;
+                key[e] = in ? key[e] : 0u;
+                pos[e] = in ? pos[e] : 0u;
             }
             select_regs<E_CAND>(key, pos, need, 1, prefix, mask, sh);
 #pragma unroll
