@@ -167,12 +167,24 @@ def build_pool(scores: np.ndarray, n_blocks: int) -> np.ndarray:
     return topk(block_max(scores), n_blocks)
 
 
+def visible_entries(t: int, ratio: int) -> int:
+    """Number of compressed entries the token at position t may attend when each
+    entry compresses `ratio` consecutive tokens (entry j covers tokens
+    ratio*j .. ratio*j + ratio - 1).  Reading of the encoder's causal mask
+    (aprilzz.com CSA2 section: compression ratio 2 in the encoder): an entry is
+    visible once every token it covers is at or before t, so the visible
+    entries are j = 0 .. floor((t + 1) / ratio) - 1."""
+    return (int(t) + 1) // int(ratio)
+
+
 # ----------------------------------------------------------------------------- attention
 def attention(q: np.ndarray, codes: np.ndarray | None, scales: np.ndarray | None, idx: np.ndarray | None,
-              swa: np.ndarray | None, slot: int, window: int, sm_scale: float):
+              swa: np.ndarray | None, q_pos: int, window: int, sm_scale: float):
     """q[H][D] (any float dtype, used exactly as fp64); codes/scales the FP4 cache
-    of one sequence in logical entry order; idx[K] (or None); swa[T][D] window
-    rows (or None).  Returns (o[H][D] fp64, lse[H] fp64)."""
+    of one sequence in logical entry order; idx[K] (or None); swa[T][D] the
+    layer's window ring (token t in row t mod T), or None; q_pos the query
+    token's absolute position (window = tokens max(0, q_pos-window+1)..q_pos,
+    window <= T).  Returns (o[H][D] fp64, lse[H] fp64)."""
     q = _c(q, np.float64)
     H, D = q.shape
     if idx is None:
@@ -185,9 +197,11 @@ def attention(q: np.ndarray, codes: np.ndarray | None, scales: np.ndarray | None
         scales = _c(scales, np.uint8)
     swa_a = None if swa is None else _c(swa, np.float64)
     T = 0 if swa_a is None else swa_a.shape[0]
+    if swa_a is not None and window > T:
+        raise ValueError(f"window {window} exceeds the ring's {T} rows")
     o = np.empty((H, D), np.float64)
     lse = np.empty(H, np.float64)
-    _load().oracle_attention(_ptr(q), H, D, _ptr(codes), _ptr(scales), _ptr(idx_a), K, _ptr(swa_a), T, int(slot),
+    _load().oracle_attention(_ptr(q), H, D, _ptr(codes), _ptr(scales), _ptr(idx_a), K, _ptr(swa_a), T, int(q_pos),
                              int(window), float(sm_scale), _ptr(o), _ptr(lse))
     return o, lse
 
@@ -249,7 +263,8 @@ def run_stack(pattern: str, seq: dict, layers: list[dict], K: int = 512, pool_bl
 
     seq:    shared state of the sequence: K_idx[n][D_i] (bf16 bits), codes, scales
             (logical entry order), n_vis.
-    layers: per-layer dict: q[H][D], q_idx[H_i][D_i] (F/R only), swa[T][D], slot.
+    layers: per-layer dict: q[H][D], q_idx[H_i][D_i] (F/R only), swa[T][D] (window
+            ring, token t in row t mod T), q_pos (the query token's position).
 
     Follows the mode table: Full scores every visible entry and selects a new
     Top-K (and, when the pattern holds a Reindex layer, the pool of the best
@@ -266,7 +281,7 @@ def run_stack(pattern: str, seq: dict, layers: list[dict], K: int = 512, pool_bl
     out = []
     for mode, L, idx in zip(pattern, layers, sel):
         q = L["q"] if attn_heads is None else L["q"][attn_heads]
-        o, lse = attention(q, seq["codes"], seq["scales"], idx, L["swa"], L["slot"], window, sm_scale)
+        o, lse = attention(q, seq["codes"], seq["scales"], idx, L["swa"], L["q_pos"], window, sm_scale)
         rec = dict(idx=idx.copy(), o=o, lse=lse)
         if mode == "F" and pool is not None:
             rec["pool"] = pool

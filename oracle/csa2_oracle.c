@@ -284,18 +284,22 @@ void oracle_topk(const float* scores, int64_t n, int32_t k, const int32_t* map, 
 
 /* One query row, H heads of width D (q[H][D], values as fp64).
  * Key set = { decoded FP4 entry idx[i] : i < K, idx[i] >= 0 }
- *         u { SWA token t : max(0, slot-window+1) <= t <= slot } (rows of
- *           swa[T][D]; omitted when swa == NULL).
+ *         u { window token t : max(0, q_pos-window+1) <= t <= q_pos }
+ *           (omitted when swa == NULL).  The window is the 128 most recent
+ *           tokens including the query token itself [P4 "把 prefill 砍掉一半"];
+ *           the layer's window rows are kept in a ring swa[T][D] in which
+ *           token t occupies row t mod T -- the row a rebuilt (replayed)
+ *           window is written to, below -- so window <= T is required (no
+ *           two tokens of one window share a row).
  * K = V = the key vector.  For each head: z = sm_scale * q.key,
  * o = sum softmax(z) * key, lse = log sum exp(z) (natural log).
  * An empty key set gives o = 0, lse = -inf. */
 void oracle_attention(const double* q, int32_t H, int32_t D, const uint8_t* codes, const uint8_t* scales,
-                      const int32_t* idx, int32_t K, const double* swa, int32_t T, int32_t slot, int32_t window,
+                      const int32_t* idx, int32_t K, const double* swa, int32_t T, int32_t q_pos, int32_t window,
                       double sm_scale, double* o, double* lse) {
-    int32_t lo = slot - window + 1;
+    int32_t lo = q_pos - window + 1;
     if (lo < 0) lo = 0;
-    int32_t n_swa = (swa != NULL && window > 0) ? (slot - lo + 1) : 0;
-    if (swa != NULL && slot >= T) n_swa = 0;
+    int32_t n_swa = (swa != NULL && window > 0 && q_pos >= 0) ? (q_pos - lo + 1) : 0;
     int32_t n_keys = 0;
     for (int32_t i = 0; i < K; ++i)
         if (idx != NULL && idx[i] >= 0) ++n_keys;
@@ -310,8 +314,10 @@ void oracle_attention(const double* q, int32_t H, int32_t D, const uint8_t* code
             for (int c = 0; c < D; ++c) keys[(int64_t)r * D + c] = fp4_value(cr, sr, c);
             ++r;
         }
-    for (int32_t t = lo; t < lo + n_swa; ++t, ++r)
-        for (int c = 0; c < D; ++c) keys[(int64_t)r * D + c] = swa[(int64_t)t * D + c];
+    for (int32_t t = lo; t < lo + n_swa; ++t, ++r) {
+        const int64_t row = t % T; /* the ring row of token t */
+        for (int c = 0; c < D; ++c) keys[(int64_t)r * D + c] = swa[row * D + c];
+    }
 
     double* z = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
     for (int32_t h = 0; h < H; ++h) {

@@ -70,19 +70,34 @@ def test_lse_merge_identity(orc):
     np.testing.assert_allclose(l_u, l_m, rtol=1e-13)
 
 
-def test_window_bounds(orc):
-    # slot 5 with window 128 sees rows 0..5 only; rows after the slot never count.
+def _ring_from_history(hist, T):
+    """The window ring after appending the rows of tokens 0..len(hist)-1 in
+    order: each token's row overwrites ring row (token mod T)."""
+    ring = np.zeros((T, hist.shape[1]))
+    for t in range(hist.shape[0]):
+        ring[t % T] = hist[t]
+    return ring
+
+
+@pytest.mark.parametrize("T,W,p", [(128, 128, 5), (128, 128, 127), (128, 128, 300), (256, 128, 300),
+                                   (40, 3, 30), (131, 128, 1000), (2175, 128, 65535)])
+def test_window_bounds(orc, T, W, p):
+    # The window of the query token at position p is tokens max(0, p-W+1)..p
+    # (the query token included); the ring holds what appends left in it.
+    # Expected keys: a plain slice of the token-ordered history.
     D, H = 128, 16
-    swa = inputs.normal((40, D), "wb", dtype=torch.bfloat16).double().numpy()
+    hist = inputs.normal((p + 1, D), f"wb{T}_{p}", dtype=torch.bfloat16).double().numpy()
     q = inputs.normal((H, D), "wq", dtype=torch.bfloat16).double().numpy()
-    o, lse = orc.attention(q, None, None, None, swa, 5, WINDOW, 0.1)
-    o_ref, lse_ref = _sdpa(q, swa[:6], 0.1)
-    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
-    # window 3 at slot 30 -> rows 28..30
-    o, lse = orc.attention(q, None, None, None, swa, 30, 3, 0.1)
-    o_ref, lse_ref = _sdpa(q, swa[28:31], 0.1)
+    ring = _ring_from_history(hist, T)
+    o, lse = orc.attention(q, None, None, None, ring, p, W, 0.1)
+    o_ref, lse_ref = _sdpa(q, hist[max(0, p - W + 1):p + 1], 0.1)
     np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
+
+
+def test_window_larger_than_ring_is_rejected(orc):
+    with pytest.raises(ValueError):
+        orc.attention(np.ones((16, 128)), None, None, None, np.zeros((64, 128)), 100, 128, 0.1)
 
 
 def test_identical_keys_give_that_key(orc):

@@ -126,3 +126,26 @@ def test_replay_power_of_two_scaling_is_exact(orc):
     h2 = (torch.from_numpy(_to_f64(h)) * 4).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     b = _to_f64(orc.swa_replay(h2, W, 3, 4))
     np.testing.assert_array_equal(b, 4 * a)
+
+
+@pytest.mark.parametrize("T,t_end", [(128, 1000), (256, 1000), (128, 127), (131, 5000)])
+def test_replay_then_attention_sees_the_logical_window(orc, T, t_end):
+    # A window rebuilt by replaying the last 128 tokens (t_end mod T need not be
+    # T - 1) and attended by the token at t_end covers exactly the replayed
+    # tokens t_end-127..t_end.  Expected: fp64 softmax attention over the same
+    # projected rows in token order, from a replay into a 128-row ring that
+    # ends at position 127 (token i on row i).
+    rng = np.random.default_rng(T + t_end)
+    n, dm, D, H, sc = 128, 64, 128, 16, 0.08
+    W = _bf16_bits((D, dm), rng, scale=0.125)
+    h = _bf16_bits((n, dm), rng)
+    ring = orc.swa_replay(h, W, t_end, T)
+    in_order = _to_f64(orc.swa_replay(h, W, n - 1, n))
+    q = rng.standard_normal((H, D))
+    o, lse = orc.attention(q, None, None, None, _to_f64(ring), t_end, 128, sc)
+    qt = torch.from_numpy(q)[None, :, None, :]
+    kt = torch.from_numpy(in_order)[None, None].expand(1, H, -1, -1)
+    o_ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=sc)[0, :, 0].numpy()
+    lse_ref = torch.logsumexp((qt @ kt.transpose(-1, -2)) * sc, -1)[0, :, 0].numpy()
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)

@@ -21,7 +21,7 @@ def _seq_and_layers(pattern, n, H=16, D=128, H_i=4, D_i=64, T=128, tag="s"):
             q=inputs.normal((H, D), f"{tag}q{l}", dtype=torch.bfloat16).double().numpy(),
             q_idx=inputs.bf16_bits(inputs.normal((H_i, D_i), f"{tag}qi{l}", dtype=torch.bfloat16)),
             swa=inputs.normal((T, D), f"{tag}swa{l}", dtype=torch.bfloat16).double().numpy(),
-            slot=T - 1))
+            q_pos=T - 1))
     return seq, layers
 
 
@@ -63,3 +63,14 @@ def test_mode_sequence_errors(orc):
         orc.run_stack("U", seq, layers[:1])
     with pytest.raises(ValueError):
         orc.run_stack("R", seq, layers[1:])
+
+
+def test_visible_entries_brute_force(orc):
+    # entry j covers tokens [ratio*j, ratio*j + ratio - 1] and is visible to
+    # token t once all of them are <= t: count such entries one by one
+    for ratio in (1, 2, 3, 4):
+        for t in range(0, 200):
+            n = sum(1 for j in range(0, 200) if all(ratio * j + i <= t for i in range(ratio)))
+            assert orc.visible_entries(t, ratio) == n, (t, ratio)
+    # decode at compression 1 sees every earlier token's entry and its own
+    assert orc.visible_entries(65535, 2) == 32768 and orc.visible_entries((1 << 20) - 1, 1) == 1 << 20
