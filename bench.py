@@ -202,43 +202,109 @@ def bench_replay(args):
     print(json.dumps(out), flush=True)
 
 
+def host_cpu():
+    """(threads to use, CPUs visible, CPU model name).  The pool is capped at the
+    16 CPUs a one-GPU machine is given, whatever the visible count."""
+    visible = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return min(16, visible), visible, model
+
+
 def cpu_baseline(inst, budget_s):
-    """Time the CPU oracle on whole query rows of the same workload until the
-    budget is used (at least one row)."""
+    """Time the CPU oracle on whole steps of the same workload (every query row
+    through the whole layer stack) on the host's cores: query rows run in
+    parallel, and each row's Full-mode scoring is split over entry chunks (the
+    same oracle calls on parts of the indexer K, identical scores).  Steps are
+    repeated until the budget is used (at least one step, or as many rows as
+    the budget allows when one step is longer)."""
+    import concurrent.futures
+
     import numpy as np
     import oracle
     from fp4_kv_cache_csa2_amd import inputs
     import torch
 
     oracle.build(force=False)
+    threads, visible, model = host_cpu()
     w = inst.w
-    done, t_total = 0, 0.0
+    rows = []
     for r in range(w.B * w.Q):
         b, q = divmod(r, w.Q)
         lo, hi = int(inst.offsets[b]), int(inst.offsets[b + 1])
         K_b = inputs.bf16_bits(inst.k_logical[lo:hi])
         qi = [None if L["q_idx"] is None else inputs.bf16_bits(L["q_idx"][b, q]) for L in inst.layers]
-        qs = [L["q"][b, q].double().cpu().numpy() for L in inst.layers]
-        sw = [L["swa"][b].double().cpu().numpy() for L in inst.layers]
-        nv = int(inst.n_vis_host[b, q])
-        # the FP4 cache rows the oracle will attend are encoded outside the timed region
-        sel, _ = oracle.select_stack(w.pattern, K_b, nv, qi, w.K, w.P)
-        ids = np.unique(np.concatenate([s[s >= 0] for s in sel]))
-        lat = inst.latent[torch.from_numpy(lo + ids).to(inst.latent.device)].cpu().numpy()
-        rc, rs = oracle.fp4_encode(lat)
-        t0 = time.perf_counter()
-        sel, _ = oracle.select_stack(w.pattern, K_b, nv, qi, w.K, w.P)
-        for l in range(w.layers):
-            idx_c = np.where(sel[l] >= 0, np.searchsorted(ids, sel[l]), -1).astype(np.int32)
-            oracle.attention(qs[l], rc, rs, idx_c, sw[l], int(inst.q_slot_host[b, q]), w.window, inst.sm_scale)
-        t_total += time.perf_counter() - t0
-        done += 1
-        if t_total >= budget_s:
+        nv = oracle.visible_entries(int(inst.q_pos_host[b, q]), w.ratio)
+        rows.append(dict(b=b, q=q, K=K_b, qi=qi, nv=nv, lo=lo,
+                         qs=[L["q"][b, q].double().cpu().numpy() for L in inst.layers],
+                         sw=[L["swa"][b].double().cpu().numpy() for L in inst.layers]))
+        if len(rows) >= 256:
             break
-    return {"value": done / t_total, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Q} query rows through the whole {w.pattern} stack at "
-                      f"N={inst.n_max} (scoring, Top-K, pool, Reindex, fp64 attention); single-threaded C; "
-                      f"{t_total:.1f} s"}
+    ex = concurrent.futures.ThreadPoolExecutor(threads)
+    chunk = 1 << 16
+
+    def scores(qi, K, nv):
+        parts = [(j, min(K.shape[0], j + chunk)) for j in range(0, K.shape[0], chunk)]
+        outs = ex.map(lambda ab: oracle.index_scores(qi, K[ab[0]:ab[1]], max(0, min(nv, ab[1]) - ab[0])), parts)
+        return np.concatenate(list(outs))
+
+    def select(rw):
+        """The layer schedule's selections (as oracle.select_stack, with the Full
+        scores computed chunk-parallel)."""
+        idx, pool, out = None, None, []
+        need_pool = "R" in w.pattern
+        for mode, qi in zip(w.pattern, rw["qi"]):
+            if mode == "F":
+                s = scores(qi, rw["K"], rw["nv"])
+                idx = oracle.topk(s, w.K)
+                if need_pool:
+                    pool = oracle.build_pool(s, w.P)
+            elif mode == "R":
+                idx = oracle.topk(oracle.reindex_scores(qi, rw["K"], rw["nv"], pool), w.K, pool)
+            out.append(idx)
+        return out
+
+    # the FP4 cache rows each row attends are encoded before timing
+    for rw in rows:
+        sel, _ = oracle.select_stack(w.pattern, rw["K"], rw["nv"], rw["qi"], w.K, w.P)
+        rw["ids"] = np.unique(np.concatenate([x[x >= 0] for x in sel]))
+        lat = inst.latent[torch.from_numpy(rw["lo"] + rw["ids"]).to(inst.latent.device)].cpu().numpy()
+        rw["rc"], rw["rs"] = oracle.fp4_encode(lat)
+
+    def attend(args):
+        rw, l, sel = args
+        idx_c = np.where(sel >= 0, np.searchsorted(rw["ids"], sel), -1).astype(np.int32)
+        oracle.attention(rw["qs"][l], rw["rc"], rw["rs"], idx_c, rw["sw"][l], int(inst.q_pos_host[rw["b"], rw["q"]]),
+                         w.window, inst.sm_scale)
+
+    done, t0 = 0, time.perf_counter()
+    while True:
+        # all rows' selections (rows in parallel when there are many, entry
+        # chunks in parallel inside each Full scan), then every (row, layer) attention
+        if len(rows) >= threads:
+            with concurrent.futures.ThreadPoolExecutor(threads) as rx:
+                sels = list(rx.map(select, rows))
+        else:
+            sels = [select(rw) for rw in rows]
+        list(ex.map(attend, [(rw, l, sels[i][l]) for i, rw in enumerate(rows) for l in range(w.layers)]))
+        done += len(rows)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            break
+    ex.shutdown()
+    steps = done / len(rows)
+    return {"value": done / dt, "unit": "query-tokens/s", "cores": threads, "cpus_visible": visible,
+            "cpu_model": model, "kind": "oracle",
+            "sample": f"{steps:g} repetitions of {len(rows)} query rows through the whole {w.pattern} stack at "
+                      f"N={inst.n_max} (scoring, Top-K, pool, Reindex, fp64 attention), plain C on {threads} "
+                      f"threads (rows and entry chunks in parallel); {dt:.1f} s"}
 
 
 def main():
@@ -277,24 +343,24 @@ def main():
     # everything a decode step stores about its new tokens, one launch per token:
     # the FP4 main-KV entry (re-quantised into the last Q entries of each
     # sequence), its indexer key, and every layer's window row at the token's
-    # ring slot (the rows already there, so the instance stays unchanged)
+    # ring row (the rows already there, so the instance stays unchanged)
     new = []
     for q in range(w.Q if decode else 0):
         last = inst.lengths - w.Q + q
         rows = torch.from_numpy(inst.offsets[:-1] + last).to(dev)
-        slot_h = inst.q_slot_host[:, q].astype(np.int64)
+        tok_h = inst.q_pos_host[:, q].astype(np.int64)
         bidx = torch.arange(w.B, device=dev)
-        slot_d = torch.from_numpy(slot_h).to(dev)
+        ring_row = torch.from_numpy(tok_h % inst.T).to(dev)
         new.append(dict(x=inst.latent[rows].contiguous(), pos=torch.from_numpy(last).to(dev),
                         k_new=inst.k_logical[rows].contiguous(),
-                        swa_new=[L["swa"][bidx, slot_d].contiguous() for L in inst.layers],
-                        slot=slot_d.to(torch.int32)))
+                        swa_new=[L["swa"][bidx, ring_row].contiguous() for L in inst.layers],
+                        tok=torch.from_numpy(tok_h.astype(np.int32)).to(dev)))
     swa_kv = [L["swa"] for L in inst.layers]
 
     def step():
         for a in new:
             api.csa2_append_token(a["x"], a["pos"], inst.cache, a["k_new"], inst.kview, a["swa_new"], swa_kv,
-                                  a["slot"])
+                                  a["tok"])
         run.step()
 
     for _ in range(args.warmup):
@@ -366,7 +432,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # bf16 indexer keys/queries scored by fp32 FMA chains; FP4 (E2M1 x E4M3)
+        # keys and bf16 queries/window rows as fp16 MFMA operands, fp32 accumulation
+        "dtype": "bf16+fp4 in, fp32 scan, fp16 mfma/fp32 acc",
         "data": "synthetic (seeded N(0,1); FP4 cache quantised on the GPU)",
         "config": {"workload": w.name, "B": w.B, "Q": w.Q, "N": inst.n_max, "pattern": w.pattern, "D": w.D,
                    "H": w.H, "H_i": w.H_i, "D_i": w.D_i, "K": w.K, "pool": f"{w.P}x8", "window": w.window},

@@ -15,6 +15,7 @@ i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
 f32 = ctypes.c_float
 sz = ctypes.c_size_t
 
+ABI_VERSION = 2
 CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EMODE, CSA2_EHIP = range(6)
 CSA2_F32, CSA2_BF16 = 0, 1
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
@@ -32,7 +33,7 @@ class IdxK(ctypes.Structure):
 
 class LayerArgs(ctypes.Structure):
     _fields_ = [("B", i32), ("Q", i32), ("H", i32), ("H_i", i32), ("K", i32), ("P", i32),
-                ("q", P), ("qt", ctypes.c_int), ("q_idx", P), ("swa_kv", P), ("T", i32), ("q_slot", P),
+                ("q", P), ("qt", ctypes.c_int), ("q_idx", P), ("swa_kv", P), ("T", i32), ("q_pos", P),
                 ("window", i32), ("sm_scale", f32), ("o", P), ("lse", P),
                 ("kv", ctypes.POINTER(Fp4KV)), ("k", ctypes.POINTER(IdxK)), ("n_vis", P), ("n_max", i32),
                 ("build_pool", i32), ("ws", P), ("ws_bytes", sz)]
@@ -41,7 +42,7 @@ class LayerArgs(ctypes.Structure):
 class AppendArgs(ctypes.Structure):
     _fields_ = [("B", i32), ("x", P), ("xt", ctypes.c_int), ("pos", P), ("kv", ctypes.POINTER(Fp4KV)),
                 ("k_new", P), ("k", ctypes.POINTER(IdxK)), ("n_layers", i32), ("swa_new", ctypes.POINTER(P)),
-                ("swa_kv", ctypes.POINTER(P)), ("T", i32), ("slot", P)]
+                ("swa_kv", ctypes.POINTER(P)), ("T", i32), ("tok", P)]
 
 
 class ReplayArgs(ctypes.Structure):
@@ -50,7 +51,8 @@ class ReplayArgs(ctypes.Structure):
 
 
 class GroupState(ctypes.Structure):
-    _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32), ("ws_clean", i32)]
+    _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32), ("ws_clean", i32), ("clean_rows", i32),
+                ("clean_ws", P)]
 
 
 # name -> (restype, argtypes); every symbol declared in include/csa2.h
@@ -91,6 +93,9 @@ def load() -> ctypes.CDLL:
             raise RuntimeError(f"CSA2 HIP library not built: {LIB_PATH} is missing "
                                "(run python -m fp4_kv_cache_csa2_amd.build)")
         lib = ctypes.CDLL(LIB_PATH)
+        if lib.csa2_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH}: ABI version {lib.csa2_abi_version()}, binding expects {ABI_VERSION} "
+                               "(rebuild with python -m fp4_kv_cache_csa2_amd.build)")
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype = res

@@ -66,6 +66,18 @@ class IndexerK:
         return _lib.IdxK(self.k.data_ptr(), _ptr(self.page_table), self.page_size, mp, self.seq_stride, self.D_i)
 
 
+def _check_rows(view, B: int, what: str):
+    """Contiguous views address B * seq_stride rows: they must exist in the
+    tensors handed over (the library only sees pointers)."""
+    if view is None or view.page_table is not None:
+        return
+    planes = [view.codes, view.scales] if isinstance(view, Fp4Cache) else [view.k]
+    for t in planes:
+        if B * view.seq_stride > t.shape[0]:
+            raise ValueError(f"{what}: {B} sequences x seq_stride {view.seq_stride} rows exceed the "
+                             f"{t.shape[0]} rows allocated")
+
+
 def csa2_abi_version() -> int:
     return _lib.load().csa2_abi_version()
 
@@ -81,15 +93,19 @@ def csa2_fp4_dequantize(codes, scales, y, stream=None):
 
 
 def csa2_fp4_append(x, pos, cache: Fp4Cache, stream=None):
+    _check_rows(cache, x.shape[0], "fp4_append")
     v = cache.view()
     _lib.check(_lib.load().csa2_fp4_append(_ptr(x), _dtype(x), x.shape[0], _ptr(pos), ctypes.byref(v),
                                            _stream(stream)))
 
 
 def csa2_append_token(x, pos, cache: Fp4Cache, k_new=None, kview: IndexerK | None = None, swa_new=(), swa_kv=(),
-                      slot=None, stream=None):
+                      tok=None, stream=None):
     """One launch per decode step: FP4 entry pos[b] from x[b], indexer-K entry
-    pos[b] from k_new[b], and slot slot[b] of every swa_kv[l] from swa_new[l][b]."""
+    pos[b] from k_new[b], and every window ring swa_kv[l] at row tok[b] mod T
+    from swa_new[l][b] (tok: the new token's absolute position)."""
+    _check_rows(cache, x.shape[0], "append_token")
+    _check_rows(kview, x.shape[0], "append_token")
     v = cache.view()
     kv = kview.view() if kview is not None else None
     n = len(swa_new)
@@ -100,7 +116,7 @@ def csa2_append_token(x, pos, cache: Fp4Cache, k_new=None, kview: IndexerK | Non
     T = swa_kv[0].shape[1] if n else 0
     a = _lib.AppendArgs(x.shape[0], x.data_ptr(), _dtype(x), pos.data_ptr(), ctypes.pointer(v),
                         None if k_new is None else k_new.data_ptr(), None if kv is None else ctypes.pointer(kv),
-                        n, new_arr, kv_arr, T, None if slot is None else slot.data_ptr())
+                        n, new_arr, kv_arr, T, None if tok is None else tok.data_ptr())
     _lib.check(_lib.load().csa2_append_token(ctypes.byref(a), _stream(stream)))
 
 
@@ -122,6 +138,7 @@ def csa2_swa_replay(h, W, swa_kv, t_end, stream=None):
 
 def csa2_index_full(q_idx, kview: IndexerK, n_vis, n_max, scores, block_max=None, stream=None):
     B, Q, H_i, _ = q_idx.shape
+    _check_rows(kview, B, "index_full")
     v = kview.view()
     _lib.check(_lib.load().csa2_index_full(_ptr(q_idx), B, Q, H_i, ctypes.byref(v), _ptr(n_vis), n_max, _ptr(scores),
                                            _ptr(block_max), _stream(stream)))
@@ -129,6 +146,7 @@ def csa2_index_full(q_idx, kview: IndexerK, n_vis, n_max, scores, block_max=None
 
 def csa2_index_reindex(q_idx, kview: IndexerK, n_vis, pool_blocks, pool_scores, stream=None):
     B, Q, H_i, _ = q_idx.shape
+    _check_rows(kview, B, "index_reindex")
     v = kview.view()
     _lib.check(_lib.load().csa2_index_reindex(_ptr(q_idx), B, Q, H_i, ctypes.byref(v), _ptr(n_vis),
                                               _ptr(pool_blocks), pool_blocks.shape[-1], _ptr(pool_scores),
@@ -152,6 +170,7 @@ def csa2_attn_workspace_size(B, Q, H, D) -> int:
 
 def csa2_sparse_attn_fp4(q, cache: Fp4Cache, idx, sm_scale, o, lse, ws=None, stream=None):
     B, Q, H, _ = q.shape
+    _check_rows(cache, B, "sparse_attn_fp4")
     v = cache.view()
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _lib.check(_lib.load().csa2_sparse_attn_fp4(_ptr(q), _dtype(q), B, Q, H, ctypes.byref(v), _ptr(idx),
@@ -159,10 +178,12 @@ def csa2_sparse_attn_fp4(q, cache: Fp4Cache, idx, sm_scale, o, lse, ws=None, str
                                                 _stream(stream)))
 
 
-def csa2_swa_attn(q, swa_kv, q_slot, window, sm_scale, merge, o, lse, ws=None, stream=None):
+def csa2_swa_attn(q, swa_kv, q_pos, window, sm_scale, merge, o, lse, ws=None, stream=None):
+    """Window attention; swa_kv [B][T][D] is a ring (token t in row t mod T),
+    q_pos [B][Q] the query tokens' absolute positions."""
     B, Q, H, D = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _lib.check(_lib.load().csa2_swa_attn(_ptr(q), _dtype(q), B, Q, H, D, _ptr(swa_kv), swa_kv.shape[1], _ptr(q_slot),
+    _lib.check(_lib.load().csa2_swa_attn(_ptr(q), _dtype(q), B, Q, H, D, _ptr(swa_kv), swa_kv.shape[1], _ptr(q_pos),
                                          window, float(sm_scale), int(merge), _ptr(o), _ptr(lse), _ptr(ws), nbytes,
                                          _stream(stream)))
 
@@ -177,16 +198,18 @@ class GroupState:
     def __init__(self, rows: int, K: int, P: int, device):
         self.idx = torch.empty(rows, K, dtype=torch.int32, device=device)
         self.pool = torch.empty(rows, max(P, 1), dtype=torch.int32, device=device)
-        self.c = _lib.GroupState(self.idx.data_ptr(), self.pool.data_ptr(), 0, 0, 0)
+        self.c = _lib.GroupState(self.idx.data_ptr(), self.pool.data_ptr(), 0, 0, 0, 0, None)
 
 
-def csa2_layer_forward(mode: str, *, q, q_idx, swa_kv, q_slot, window, sm_scale, o, lse, cache: Fp4Cache,
+def csa2_layer_forward(mode: str, *, q, q_idx, swa_kv, q_pos, window, sm_scale, o, lse, cache: Fp4Cache,
                        kview: IndexerK, n_vis, n_max, K, P, build_pool, ws, state: GroupState, stream=None):
     B, Q, H, _ = q.shape
+    _check_rows(cache, B, "layer_forward")
+    _check_rows(kview, B, "layer_forward")
     H_i = 0 if q_idx is None else q_idx.shape[2]
     kv, kk = cache.view(), kview.view()
     a = _lib.LayerArgs(B, Q, H, H_i, K, P, q.data_ptr(), _dtype(q), _ptr(q_idx), swa_kv.data_ptr(), swa_kv.shape[1],
-                       q_slot.data_ptr(), window, float(sm_scale), o.data_ptr(), lse.data_ptr(), ctypes.pointer(kv),
+                       q_pos.data_ptr(), window, float(sm_scale), o.data_ptr(), lse.data_ptr(), ctypes.pointer(kv),
                        ctypes.pointer(kk), _ptr(n_vis), n_max, int(build_pool), ws.data_ptr(),
                        ws.numel() * ws.element_size())
     _lib.check(_lib.load().csa2_layer_forward(MODES[mode], ctypes.byref(a), ctypes.byref(state.c), _stream(stream)))

@@ -43,9 +43,9 @@ struct AttnParams {
     const int32_t* idx;        // [rows][K]
     int32_t K, Kp;             // Kp = K rounded up to 16 (0 if no sparse part)
     // window
-    const uint16_t* swa;       // [B][T][D]
+    const uint16_t* swa;       // [B][T][D] ring: token t at row t mod T
     int32_t T;
-    const int32_t* q_slot;     // [rows]
+    const int32_t* q_pos;      // [rows] absolute position of the query token
     int32_t window, Wp;        // Wp = window rounded up to 16 (0 if no window part)
     float scale_log2;          // sm_scale * log2(e)
     int32_t merge;
@@ -637,8 +637,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
     const int n_sp_chunks = p.Kp / CHUNK_KEYS;
     const int c_lo = split * p.cps;
     const int c_hi = min(nchunks, c_lo + p.cps);
-    const int slot = p.Wp ? p.q_slot[row] : 0;
-    const int wlo = max(0, slot - p.window + 1);
+    // window: tokens wlo..qp, token t in ring row t mod T
+    const int qp = p.Wp ? p.q_pos[row] : -1;
+    const int wlo = max(0, qp - p.window + 1);
+    const int wrow0 = p.Wp ? wlo % p.T : 0;
 
     // ---- the index loads go first: they head the longest chain (index ->
     // physical row -> copy -> dequantisation); the query loads follow and fly
@@ -679,8 +681,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnParams p) {
         if (kpos < p.Kp) {
             if (kent[j] >= 0) r = phys_row(p.kvmap, b, kent[j]);
         } else {
-            const int t = wlo + (kpos - p.Kp);
-            if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
+            const int i_w = kpos - p.Kp;  // window key i: token wlo + i (window <= T: no row repeats)
+            if (wlo + i_w <= qp) r = (int64_t)b * p.T + (wrow0 + i_w >= p.T ? wrow0 + i_w - p.T : wrow0 + i_w);
         }
         krow[i] = r;
     }
@@ -913,8 +915,9 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     // whose keys have no row (finite copies of row 0, weight exactly 0)
     const int npad = nloc + (nloc & 1);
     const int n_sp = p.Kp / CHUNK_KEYS;
-    const int slot = p.Wp ? p.q_slot[row] : 0;
-    const int wlo = max(0, slot - p.window + 1);
+    const int qp = p.Wp ? p.q_pos[row] : -1;
+    const int wlo = max(0, qp - p.window + 1);
+    const int wrow0 = p.Wp ? wlo % p.T : 0;
     const int nk = nloc * CHUNK_KEYS;
     // a local chunk's kind (sparse or window); the padding chunk is copied as
     // the kind of the chunk after the range, or past the last chunk as the
@@ -950,8 +953,8 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
         } else if (kpos < p.Kp) {
             if (kent[j] >= 0) r = phys_row(p.kvmap, b, kent[j]);
         } else {
-            const int t = wlo + (kpos - p.Kp);
-            if (t <= slot && t < p.T) r = (int64_t)b * p.T + t;
+            const int i_w = kpos - p.Kp;
+            if (wlo + i_w <= qp) r = (int64_t)b * p.T + (wrow0 + i_w >= p.T ? wrow0 + i_w - p.T : wrow0 + i_w);
         }
         krow[i] = r;
     }
@@ -1120,7 +1123,7 @@ size_t attn_ws_bytes(int64_t rows, int H, int D) {
 // Shared launcher of the sparse-only, window-only and fused calls.
 csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                         const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,
-                        const int32_t* q_slot, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
+                        const int32_t* q_pos, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
                         void* ws, size_t ws_bytes, hipStream_t stream, const char* what) {
     CSA2_ARG(B >= 0 && Q >= 0, "%s: B=%d Q=%d must be >= 0", what, B, Q);
     CSA2_ARG((int64_t)B * Q <= 65535, "%s: B*Q=%lld rows exceeds 65535", what, (long long)B * Q);
@@ -1146,7 +1149,8 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
         p.scales = kv->scales;
     }
     if (window > 0) {
-        CSA2_ARG(swa && q_slot && T > 0, "%s: null window rows / q_slot or T <= 0", what);
+        CSA2_ARG(swa && q_pos && T > 0, "%s: null window rows / q_pos or T <= 0", what);
+        CSA2_ARG(window <= T, "%s: window=%d exceeds the ring's T=%d rows", what, window, T);
         CSA2_ARG(aligned(swa, 16), "%s: window rows must be 16-byte aligned", what);
     }
     p.q = q;
@@ -1157,7 +1161,7 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     p.Kp = (K + CHUNK_KEYS - 1) / CHUNK_KEYS * CHUNK_KEYS;
     p.swa = swa;
     p.T = T;
-    p.q_slot = q_slot;
+    p.q_pos = q_pos;
     p.window = window;
     p.Wp = (window + CHUNK_KEYS - 1) / CHUNK_KEYS * CHUNK_KEYS;
     p.scale_log2 = sm_scale * 1.4426950408889634f;
@@ -1245,11 +1249,11 @@ extern "C" csa2_status csa2_sparse_attn_fp4(const void* q, csa2_dtype qt, int32_
 }
 
 extern "C" csa2_status csa2_swa_attn(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
-                                     const uint16_t* swa_kv, int32_t T, const int32_t* q_slot, int32_t window,
+                                     const uint16_t* swa_kv, int32_t T, const int32_t* q_pos, int32_t window,
                                      float sm_scale, int32_t merge, float* o, float* lse, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
     clear_error();
     CSA2_ARG(window >= 1, "swa_attn: window=%d must be >= 1", window);
-    return attn_launch(q, qt, B, Q, H, D, nullptr, nullptr, 0, swa_kv, T, q_slot, window, sm_scale, merge, o, lse, ws,
+    return attn_launch(q, qt, B, Q, H, D, nullptr, nullptr, 0, swa_kv, T, q_pos, window, sm_scale, merge, o, lse, ws,
                        ws_bytes, stream, "swa_attn");
 }

@@ -14,15 +14,25 @@ namespace {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Layer workspace layout.  The selection counters (two selections' row
+// histograms and row states) come first: their place and size depend only on
+// the number of query rows, so a group state that records (workspace, rows)
+// knows whether they are still cleared even when n_max, K or P change between
+// calls.  Everything after them is scratch without initial contents.
 struct LayerWs {
-    size_t scores, block_max, pool_scores, topk, attn, total;
-    size_t topk_bytes, attn_bytes;
+    size_t counters, scores, block_max, pool_scores, lists, attn, total;
+    size_t attn_bytes;
 };
 
+inline size_t counter_region(int64_t rows) { return align256(2 * topk_counter_bytes(rows)); }
+
 LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
+    (void)K;
     LayerWs w{};
     const int64_t nblocks = (n_max + 7) / 8;
     size_t off = 0;
+    w.counters = off;
+    off += counter_region(rows);
     w.scores = off;
     off = align256(off + (size_t)(rows * n_max) * 4);
     w.block_max = off;
@@ -30,10 +40,8 @@ LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
     w.pool_scores = off;
     off = align256(off + (size_t)(rows * 8 * (int64_t)P) * 4);
     // two selections (entries, pool blocks) may run side by side
-    const size_t tk = (n_max > TOPK_ONEWG_N || 8 * (int64_t)P > TOPK_ONEWG_N) ? 2 * topk_large_ws_bytes(rows) : 0;
-    w.topk = off;
-    w.topk_bytes = tk;
-    off = align256(off + tk);
+    w.lists = off;
+    off = align256(off + 2 * topk_list_bytes(rows));
     w.attn = off;
     w.attn_bytes = attn_workspace_bytes(rows, H, D);
     off = align256(off + w.attn_bytes);
@@ -87,8 +95,8 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     float* scores = reinterpret_cast<float*>(ws + w.scores);
     float* block_max = reinterpret_cast<float*>(ws + w.block_max);
     float* pool_scores = reinterpret_cast<float*>(ws + w.pool_scores);
-    void* tk = ws + w.topk;
-    (void)w.topk_bytes;
+    char* counters = ws + w.counters;
+    char* lists = ws + w.lists;
     void* aw = ws + w.attn;
     const int rows32 = (int)rows;
     csa2_status s = CSA2_OK;
@@ -106,17 +114,18 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
         if (e_large) {
             se = &segs.seg[segs.nseg++];
             *se = TopkSeg{scores, n, a->K, nullptr, st->idx, a->n_vis, 1};
-            topk_carve(tk, rows, se);
+            topk_carve(counters, lists, rows, se);
         }
         if (b_large) {
             sb = &segs.seg[segs.nseg++];
             *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool, a->n_vis, 8};
-            topk_carve(static_cast<char*>(tk) + topk_large_ws_bytes(rows), rows, sb);
+            topk_carve(counters + topk_counter_bytes(rows), lists + topk_list_bytes(rows), rows, sb);
         }
         // the histograms and row states must start at zero: cleared here once
-        // per workspace, then left cleared by the finish pass of every call
+        // per (workspace, rows), then left cleared by the finish pass of every call
         topk_ws_used = segs.nseg > 0;
-        if (!st->ws_clean && segs.nseg) {
+        const bool clean = st->ws_clean && st->clean_ws == a->ws && st->clean_rows == rows32;
+        if (!clean && segs.nseg) {
             ZeroRanges z{};
             for (int i = 0; i < segs.nseg; ++i) {
                 z.ptr[z.n] = segs.seg[i].hist;
@@ -156,12 +165,16 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
         return s;
     }
     if (mode == CSA2_FULL) {
-        if (topk_ws_used) st->ws_clean = 1;
+        if (topk_ws_used) {
+            st->ws_clean = 1;
+            st->clean_ws = a->ws;
+            st->clean_rows = rows32;
+        }
         st->has_idx = 1;
         if (a->build_pool) st->has_pool = 1;
     } else if (mode == CSA2_REINDEX) {
         st->has_idx = 1;
     }
-    return attn_launch(a->q, a->qt, a->B, a->Q, a->H, a->kv->D, a->kv, st->idx, a->K, a->swa_kv, a->T, a->q_slot,
+    return attn_launch(a->q, a->qt, a->B, a->Q, a->H, a->kv->D, a->kv, st->idx, a->K, a->swa_kv, a->T, a->q_pos,
                        a->window, a->sm_scale, 0, a->o, a->lse, aw, w.attn_bytes, stream, "layer_forward");
 }

@@ -145,7 +145,7 @@ struct AppendParams {
     const void* x;
     int32_t D, D_i, B, n_layers, T;
     const int32_t* pos;
-    const int32_t* slot;
+    const int32_t* tok;
     RowMap kvmap, kmap;
     uint8_t* codes;
     uint8_t* scales;
@@ -180,7 +180,11 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendParams p) {
     } else {
         const int l = role - 2;
         const uint4* src = reinterpret_cast<const uint4*>(p.swa_new[l] + (int64_t)b * p.D);
-        uint4* dst = reinterpret_cast<uint4*>(p.swa_kv[l] + ((int64_t)b * p.T + p.slot[b]) * p.D);
+        // window ring: token t in row t mod T (a negative position names no token)
+        const int tk = p.tok[b];
+        if (tk < 0) return;
+        const int t_row = tk % p.T;
+        uint4* dst = reinterpret_cast<uint4*>(p.swa_kv[l] + ((int64_t)b * p.T + t_row) * p.D);
         for (int i = t; i < p.D / 8; i += blockDim.x) dst[i] = src[i];
     }
 }
@@ -224,7 +228,7 @@ extern "C" csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t 
         p.D_i = a->k->D_i;
     }
     if (a->n_layers > 0) {
-        CSA2_ARG(a->swa_new && a->swa_kv && a->slot && a->T > 0, "append_token: null window arrays / slot or T <= 0");
+        CSA2_ARG(a->swa_new && a->swa_kv && a->tok && a->T > 0, "append_token: null window arrays / tok or T <= 0");
         for (int l = 0; l < a->n_layers; ++l) {
             CSA2_ARG(a->swa_new[l] && a->swa_kv[l], "append_token: null window row pointer of layer %d", l);
             CSA2_ARG(aligned(a->swa_new[l], 16) && aligned(a->swa_kv[l], 16),
@@ -234,7 +238,7 @@ extern "C" csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t 
         }
         p.n_layers = a->n_layers;
         p.T = a->T;
-        p.slot = a->slot;
+        p.tok = a->tok;
     }
     const dim3 grid((unsigned)a->B, (unsigned)(2 + a->n_layers));
     if (a->xt == CSA2_BF16)

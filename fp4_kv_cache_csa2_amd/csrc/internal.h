@@ -56,8 +56,15 @@ struct TopkSegs {
     int32_t rows;
 };
 
-size_t topk_large_ws_bytes(int64_t rows);
-void topk_carve(void* ws, int64_t rows, TopkSeg* sg);
+// Workspace of one large selection: its counters (row histograms and row
+// states, which must be zero when the selection starts and are left zero by
+// it) and its lists (no initial contents).  The two parts are carved
+// separately so that a caller can keep the counters at a place that does not
+// move when other sizes (n, k) change.
+size_t topk_counter_bytes(int64_t rows);
+size_t topk_list_bytes(int64_t rows);
+size_t topk_large_ws_bytes(int64_t rows);  // both parts in one region (16-byte aligned)
+void topk_carve(void* counters, void* lists, int64_t rows, TopkSeg* sg);
 // zero the histograms and row states of every segment
 void topk_launch_zero(const TopkSegs& segs, hipStream_t stream);
 // build the first-digit histograms (not needed when the scan built them)
@@ -91,7 +98,7 @@ csa2_status index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t
 
 csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                         const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,
-                        const int32_t* q_slot, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
+                        const int32_t* q_pos, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
                         void* ws, size_t ws_bytes, hipStream_t stream, const char* what);
 size_t attn_workspace_bytes(int64_t rows, int H, int D);
 

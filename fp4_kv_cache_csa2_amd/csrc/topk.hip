@@ -187,11 +187,14 @@ __device__ void select_regs(const uint32_t (&key)[E], const uint32_t (&pos)[E], 
 
 // Slow general radix select over a row in global memory, restricted to the
 // elements matching prefix/mask (used only when a threshold bin overflows the
-// candidate buffer, e.g. long runs of equal scores).  Appends to sel[].
+// candidate buffer, e.g. long runs of equal scores).  Appends exactly `need`
+// elements of that subset to sel[]: the positions above the subset (already in
+// sel[]) are excluded from the final gather as well as from the passes.
 __device__ void select_global_row(const float* s, int n, uint32_t need, uint64_t prefix, uint64_t mask,
                                   SelectLds& sh, int* sel) {
     const int shifts[6] = {53, 42, 32, 21, 10, 0};
     const int widths[6] = {11, 11, 10, 11, 11, 10};
+    const uint64_t sub_prefix = prefix, sub_mask = mask;
     int pass = 0;
     while (pass < 6 && ((mask >> shifts[pass]) & 1u)) ++pass;  // skip decided digits
     uint32_t* h = sh.hist[0];
@@ -217,7 +220,9 @@ __device__ void select_global_row(const float* s, int n, uint32_t need, uint64_t
     }
     for (int i = threadIdx.x; i < n; i += WG) {
         const uint32_t k = key32(s[i]);
-        if (k != 0u && (composite(k, (uint32_t)i) & mask) >= prefix) sel[atomicAdd(&sh.nsel, 1u)] = i;
+        if (k == 0u) continue;
+        const uint64_t c = composite(k, (uint32_t)i);
+        if ((c & sub_mask) == sub_prefix && (c & mask) >= prefix) sel[atomicAdd(&sh.nsel, 1u)] = i;
     }
     __syncthreads();
 }
@@ -744,16 +749,17 @@ __global__ __launch_bounds__(WG) void topk_finish_kernel(TopkSegs segs) {
 
 }  // namespace
 
-size_t topk_large_ws_bytes(int64_t rows) {
-    return (size_t)rows * (NBINS1 * 4 + sizeof(TopkRowState) + TOPK_KMAX * 4 + TOPK_CAP * 8) + 256;
+size_t topk_counter_bytes(int64_t rows) {
+    return ((size_t)rows * (NBINS1 * 4 + sizeof(TopkRowState)) + 15) & ~(size_t)15;
 }
+size_t topk_list_bytes(int64_t rows) { return (size_t)rows * (TOPK_KMAX * 4 + TOPK_CAP * 8); }
+size_t topk_large_ws_bytes(int64_t rows) { return topk_counter_bytes(rows) + topk_list_bytes(rows) + 256; }
 
-void topk_carve(void* ws, int64_t rows, TopkSeg* sg) {
-    char* w = static_cast<char*>(ws);
-    sg->hist = reinterpret_cast<uint32_t*>(w);
-    w += (size_t)rows * NBINS1 * 4;
-    sg->state = reinterpret_cast<TopkRowState*>(w);
-    w += (size_t)rows * sizeof(TopkRowState);
+void topk_carve(void* counters, void* lists, int64_t rows, TopkSeg* sg) {
+    char* c = static_cast<char*>(counters);
+    sg->hist = reinterpret_cast<uint32_t*>(c);
+    sg->state = reinterpret_cast<TopkRowState*>(c + (size_t)rows * NBINS1 * 4);
+    char* w = static_cast<char*>(lists);
     sg->sel = reinterpret_cast<int*>(w);
     w += (size_t)rows * TOPK_KMAX * 4;
     sg->ckey = reinterpret_cast<uint32_t*>(w);
@@ -852,7 +858,7 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, i
     sg.k = k;
     sg.pool = pool_blocks;
     sg.out = out_idx;
-    topk_carve(ws, rows, &sg);
+    topk_carve(ws, static_cast<char*>(ws) + topk_counter_bytes(rows), rows, &sg);
     topk_launch_zero(segs, stream);
     topk_launch_hist(segs, stream);
     topk_launch_select(segs, stream);

@@ -133,11 +133,9 @@ WORKLOADS = {
 }
 
 
-def prefill_positions(w: Workload) -> tuple[np.ndarray, np.ndarray]:
-    """Query token positions t (the last Q tokens of an N*ratio-token context)
-    and the number of entries each may see.  With m tokens per entry, entry j
-    covers tokens [m*j, m*j + m - 1] and is visible to token t once complete:
-    n_vis(t) = floor((t + 1) / m)."""
+def query_positions(w: Workload) -> np.ndarray:
+    """Absolute token positions of the Q query tokens of every sequence when
+    all sequences hold N entries: the last Q tokens of an N*ratio-token
+    context (layout only; which entries each may see is decided by the path)."""
     T_tok = w.N * w.ratio
-    t = np.arange(T_tok - w.Q, T_tok, dtype=np.int64)
-    return t, ((t + 1) // w.ratio).astype(np.int32)
+    return np.arange(T_tok - w.Q, T_tok, dtype=np.int64)

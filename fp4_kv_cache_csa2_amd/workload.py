@@ -31,9 +31,9 @@ class Instance:
     cache: api.Fp4Cache
     kview: api.IndexerK
     page_table_host: np.ndarray | None
-    T: int
-    q_slot_host: np.ndarray      # [B][Q]
-    q_slot: torch.Tensor
+    T: int                       # rows of each layer's window ring (token t in row t mod T)
+    q_pos_host: np.ndarray       # [B][Q] absolute token position of each query row
+    q_pos: torch.Tensor
     layers: list = field(default_factory=list)  # per layer: dict(q, q_idx, swa)
 
     @property
@@ -104,17 +104,20 @@ def make_instance(w: Workload, seed: int = 0, device="cuda", lengths=None, Q: in
         table_host = None
         assert np.all(lengths == lengths.max())
 
-    # visibility and window slots
-    if w.Q == 1:  # decode: the query sees every entry of its sequence
-        n_vis_host = lengths.reshape(B, 1).repeat(w.Q, 1)
-        T = w.window
-        q_slot_host = np.full((B, w.Q), T - 1, np.int32)
+    # query positions, visibility and the window ring.  An entry covers `ratio`
+    # consecutive tokens and becomes visible to token t once complete: entry j
+    # (tokens ratio*j .. ratio*j + ratio-1) is visible iff ratio*j + ratio-1 <= t,
+    # so token t sees floor((t + 1) / ratio) entries.  The ring holds every
+    # token any query row's window reaches: the last Q + window - 1 tokens.
+    if w.Q == 1:  # decode: the query is each sequence's newest token and sees every entry
+        q_pos_host = (lengths.astype(np.int64) * w.ratio - 1).reshape(B, 1)
+        n_vis_host = lengths.reshape(B, 1).copy()
     else:
-        tok, nv = inputs.prefill_positions(w)
-        n_vis_host = np.broadcast_to(nv, (B, w.Q)).copy()
-        first = int(tok[0]) - (w.window - 1)
-        T = int(tok[-1]) - first + 1
-        q_slot_host = np.broadcast_to((tok - first).astype(np.int32), (B, w.Q)).copy()
+        tok = inputs.query_positions(w)
+        q_pos_host = np.broadcast_to(tok, (B, w.Q)).copy()
+        n_vis_host = (q_pos_host + 1) // w.ratio
+    T = w.Q + w.window - 1
+    q_pos_host = q_pos_host.astype(np.int32)
     n_vis_host = n_vis_host.astype(np.int32)
     layers = []
     for l, mode in enumerate(w.pattern):
@@ -126,8 +129,8 @@ def make_instance(w: Workload, seed: int = 0, device="cuda", lengths=None, Q: in
         layers.append(L)
     return Instance(w=w, lengths=lengths, n_vis_host=n_vis_host, n_vis=torch.from_numpy(n_vis_host).to(device),
                     n_max=int(lengths.max()), offsets=offsets, latent=latent, k_logical=k_log, cache=cache,
-                    kview=kview, page_table_host=table_host, T=T, q_slot_host=q_slot_host,
-                    q_slot=torch.from_numpy(q_slot_host).to(device), layers=layers)
+                    kview=kview, page_table_host=table_host, T=T, q_pos_host=q_pos_host,
+                    q_pos=torch.from_numpy(q_pos_host).to(device), layers=layers)
 
 
 class StackRunner:
@@ -154,7 +157,7 @@ class StackRunner:
         self.state.c.has_pool = 0
         for l, mode in enumerate(w.pattern):
             L = inst.layers[l]
-            api.csa2_layer_forward(mode, q=L["q"], q_idx=L["q_idx"], swa_kv=L["swa"], q_slot=inst.q_slot,
+            api.csa2_layer_forward(mode, q=L["q"], q_idx=L["q_idx"], swa_kv=L["swa"], q_pos=inst.q_pos,
                                    window=w.window, sm_scale=inst.sm_scale, o=self.o[l], lse=self.lse[l],
                                    cache=inst.cache, kview=inst.kview, n_vis=inst.n_vis, n_max=inst.n_max, K=w.K,
                                    P=w.P if self.has_pool else 0, build_pool=self.has_pool and mode == "F",

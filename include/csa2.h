@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum {
     CSA2_OK = 0,
@@ -117,14 +117,15 @@ csa2_status csa2_fp4_append(const void* x, csa2_dtype xt, int32_t B, const int32
  *   k_new   [B][D_i] bf16 or NULL: indexer key of the new entry, copied to
  *           entry pos[b] of the indexer-K view k
  *   swa_new [n_layers] host array of device pointers to [B][D] bf16 rows: each
- *           layer's window row of the new token, copied to slot slot[b] of the
- *           layer's swa_kv[l] ([B][T][D] bf16; a 128-slot ring when T = window:
- *           the window is a set, so slot order does not matter)
- * pos and slot are device [B] int32; every pos[b] must address an allocated row
- * of both views and 0 <= slot[b] < T.  0 <= n_layers <= 32.  Alignment: x,
- * k_new, k and every window pointer 16 bytes, codes 8.  Rows are written
- * in place; the caller orders this call before the layers that read them
- * (aprilzz.com, sections "FP4 KV 与部署层的几个改动" and "把 prefill 砍掉一半"). */
+ *           layer's window row of the new token, copied into the layer's window
+ *           ring swa_kv[l] ([B][T][D] bf16) at row tok[b] mod T
+ * pos and tok are device [B] int32: pos[b] the new entry's index (it must
+ * address an allocated row of both views), tok[b] >= 0 the new token's
+ * absolute position in its sequence (the window ring's row rule; see
+ * csa2_swa_attn).  0 <= n_layers <= 32.  Alignment: x, k_new, k and every
+ * window pointer 16 bytes, codes 8.  Rows are written in place; the caller
+ * orders this call before the layers that read them (aprilzz.com, sections
+ * "FP4 KV 与部署层的几个改动" and "把 prefill 砍掉一半"). */
 typedef struct csa2_append_args {
     int32_t B;
     const void* x;
@@ -137,7 +138,7 @@ typedef struct csa2_append_args {
     const uint16_t* const* swa_new;
     uint16_t* const* swa_kv;
     int32_t T;
-    const int32_t* slot;
+    const int32_t* tok;
 } csa2_append_args;
 csa2_status csa2_append_token(const csa2_append_args* a, hipStream_t stream);
 
@@ -229,15 +230,20 @@ csa2_status csa2_sparse_attn_fp4(const void* q, csa2_dtype qt, int32_t B, int32_
 
 /* Sliding-window attention over the layer's own bf16 latent rows
  * (aprilzz.com section "把 prefill 砍掉一半": 128-token window in every layer).
- *   swa_kv [B][T][D] bf16; q_slot [B][Q]: the query token's row in swa_kv;
- *   keys = rows max(0, slot-window+1) .. slot.
+ * Window ring: the layer's window row of token t (absolute position in its
+ * sequence) lives in swa_kv[b][t mod T] -- the rule csa2_append_token and
+ * csa2_swa_replay write by.
+ *   swa_kv [B][T][D] bf16 ring; q_pos [B][Q] int32: the query token's absolute
+ *   position p; keys = the rows of tokens max(0, p-window+1) .. p (the query
+ *   token included).  1 <= window <= T, so no two tokens of a window share a
+ *   row; p < 0 gives an empty window.
  *   merge == 0: write o/lse of this key set.  merge == 1: o/lse already hold a
  *   partial over a disjoint key set; combine both into one softmax (exact
  *   log-sum-exp merge) in place.
  * The window rows are converted to fp16 inside the kernel: values must satisfy
  * |v| < 65504 (smaller than 2^-14 lose precision as fp16 subnormals). */
 csa2_status csa2_swa_attn(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
-                          const uint16_t* swa_kv, int32_t T, const int32_t* q_slot, int32_t window, float sm_scale,
+                          const uint16_t* swa_kv, int32_t T, const int32_t* q_pos, int32_t window, float sm_scale,
                           int32_t merge, float* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -256,10 +262,10 @@ typedef struct csa2_layer_args {
     const void* q;           /* [B][Q][H][D] main query */
     csa2_dtype qt;
     const uint16_t* q_idx;   /* [B][Q][H_i][D_i] indexer query (FULL/REINDEX), may be NULL for REUSE */
-    const uint16_t* swa_kv;  /* [B][T][D] bf16 */
+    const uint16_t* swa_kv;  /* [B][T][D] bf16 window ring (row t mod T holds token t) */
     int32_t T;
-    const int32_t* q_slot;   /* [B][Q] */
-    int32_t window;
+    const int32_t* q_pos;    /* [B][Q] absolute token position of each query row */
+    int32_t window;          /* 1 <= window <= T */
     float sm_scale;
     float* o;                /* [B][Q][H][D] fp32 out */
     float* lse;              /* [B][Q][H] fp32 out */
@@ -278,10 +284,16 @@ typedef struct csa2_group_state {
     int32_t* pool;           /* [B*Q][P] device: pool blocks of the last pool-building FULL */
     int32_t has_idx;         /* host flags, maintained by csa2_layer_forward */
     int32_t has_pool;
-    int32_t ws_clean;        /* host flag: 0 for a fresh (or foreign) workspace.  A FULL layer
-                                clears the workspace's Top-K counters once and sets 1; every
-                                later call leaves them cleared again, so the same workspace must
-                                then stay with this state.  Reset to 0 after an error status. */
+    /* Host bookkeeping of the workspace's selection counters, maintained by
+     * csa2_layer_forward (initialise all three to 0).  The counters sit at the
+     * start of the workspace and depend only on B*Q; they are cleared once and
+     * every later call leaves them cleared again.  A call re-clears them when
+     * the workspace pointer or B*Q differs from the recorded ones, so one
+     * state may move between workspaces and shapes (n_max, K, P may change
+     * from call to call).  ws_clean is reset to 0 after an error status. */
+    int32_t ws_clean;
+    int32_t clean_rows;
+    const void* clean_ws;
 } csa2_group_state;
 
 size_t csa2_layer_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t n_max, int32_t K, int32_t P);

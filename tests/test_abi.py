@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa2_abi_version() == 1
+    assert lib.csa2_abi_version() == 2 == _lib.ABI_VERSION
     assert lib.csa2_status_string(_lib.CSA2_EMODE) == b"CSA2_EMODE"
 
 
@@ -95,6 +95,11 @@ def test_attention_argument_errors(lib):
                              None) == _lib.CSA2_EWORKSPACE
     assert lib.csa2_swa_attn(FAKE, 1, 4, 1, 64, 512, FAKE, 128, FAKE, 0, 0.1, 0, FAKE, FAKE, None, 0,
                              None) == _lib.CSA2_EINVAL
+    # a window longer than the ring would make two of its tokens share a row
+    big = 1 << 30
+    assert lib.csa2_swa_attn(FAKE, 1, 4, 1, 64, 512, FAKE, 100, FAKE, 128, 0.1, 0, FAKE, FAKE, FAKE, big,
+                             None) == _lib.CSA2_EINVAL
+    assert "ring" in _err(lib)
 
 
 def _layer_args(ws_bytes=1 << 40):
@@ -108,7 +113,7 @@ def _layer_args(ws_bytes=1 << 40):
 
 def test_layer_mode_errors(lib):
     a, kv, kk = _layer_args()
-    st = _lib.GroupState(FAKE.value, FAKE.value, 0, 0)
+    st = _lib.GroupState(FAKE.value, FAKE.value, 0, 0, 0, 0, None)
     assert lib.csa2_layer_forward(_lib.CSA2_REUSE, ctypes.byref(a), ctypes.byref(st), None) == _lib.CSA2_EMODE
     assert "Reuse" in _err(lib)
     assert lib.csa2_layer_forward(_lib.CSA2_REINDEX, ctypes.byref(a), ctypes.byref(st), None) == _lib.CSA2_EMODE

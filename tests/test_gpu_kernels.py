@@ -80,7 +80,7 @@ def test_append_token(paged, n_layers, with_k, xdtype):
     B, D, D_i, T, ps = 5, 512, 128, 128, 64
     lengths = np.array([100, 64, 3, 200, 128])
     pos = np.array([99, 0, 2, 150, 127], np.int32)
-    slot = (pos % T).astype(np.int32)
+    tok = pos + np.array([0, 1000, 7, 0, 129], np.int32)  # token positions (ring row = tok mod T)
     tag = f"apt{paged}{n_layers}"
     if paged:
         table, n_pages = inputs.random_page_table(lengths, ps, tag)
@@ -99,7 +99,7 @@ def test_append_token(paged, n_layers, with_k, xdtype):
     case(f"append_token paged={paged} n_layers={n_layers} k={with_k} {xdtype}")
     api.csa2_append_token(x.to(DEV), torch.from_numpy(pos).to(DEV), cache,
                           k_new.to(DEV) if with_k else None, kview, swa_new, swa_kv,
-                          torch.from_numpy(slot).to(DEV))
+                          torch.from_numpy(tok).to(DEV))
     torch.cuda.synchronize()
     rc, rs = oracle.fp4_encode(x.float().numpy())
     rows = [(table[b, pos[b] // ps] * ps + pos[b] % ps) if paged else b * stride + pos[b] for b in range(B)]
@@ -109,7 +109,7 @@ def test_append_token(paged, n_layers, with_k, xdtype):
         if with_k:
             assert torch.equal(kbuf[rows[b]].cpu(), k_new[b])
         for l in range(n_layers):
-            assert torch.equal(swa_kv[l][b, slot[b]].cpu(), swa_new[l][b].cpu())
+            assert torch.equal(swa_kv[l][b, tok[b] % T].cpu(), swa_new[l][b].cpu())
     # nothing else written
     assert int(codes.count_nonzero()) <= B * D // 2
     assert int((kbuf != 0).any(dim=1).sum()) == (B if with_k else 0)
@@ -294,9 +294,11 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
     q = inputs.normal((B, Q, H, D), tag + "/q", dtype=qdtype)
     idx = inputs.small_ints((B, Q, K), tag + "/idx", -1, n - 1, dtype=torch.int32)
     swa = inputs.normal((B, T, D), tag + "/swa", dtype=torch.bfloat16)
-    slot = inputs.small_ints((B, Q), tag + "/slot", 0, T - 1, dtype=torch.int32)
+    # query token positions: early ones (short windows) and wrapped rings
+    qpos = inputs.small_ints((B, Q), tag + "/qpos", 0, 5000, dtype=torch.int32)
+    qpos.view(-1)[0] = 3
     rc, rs = oracle.fp4_encode(lat.reshape(B * n, D).numpy())
-    return cache, q, idx, swa, slot, rc.reshape(B, n, -1), rs.reshape(B, n, -1)
+    return cache, q, idx, swa, qpos, rc.reshape(B, n, -1), rs.reshape(B, n, -1)
 
 
 @pytest.mark.parametrize("B,Q,H,D,K,qdtype,window", [
@@ -317,7 +319,7 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
     (300, 2, 64, 512, 200, torch.float32, 128)])
 def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype, window):
     n, T = (3000 if B < 100 else 520), 200
-    cache, q, idx, swa, slot, rc, rs = _attn_inputs(B, Q, H, D, n, K, T, qdtype, f"at{B}{H}{D}{K}")
+    cache, q, idx, swa, qpos, rc, rs = _attn_inputs(B, Q, H, D, n, K, T, qdtype, f"at{B}{H}{D}{K}")
     sc = 1 / math.sqrt(D)
     o = torch.empty(B, Q, H, D, device=DEV)
     lse = torch.empty(B, Q, H, device=DEV)
@@ -327,7 +329,7 @@ def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype, window):
     torch.cuda.synchronize()
     o1, l1 = to_np(o), to_np(lse)
     case(f"swa_attn merge window={window}")
-    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), slot.to(DEV), window, sc, 1, o, lse, ws=ws)
+    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), qpos.to(DEV), window, sc, 1, o, lse, ws=ws)
     torch.cuda.synchronize()
     o2, l2 = to_np(o), to_np(lse)
     qn = q.double().numpy()
@@ -340,15 +342,15 @@ def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype, window):
     for b, qq in rows:
         ra, la = oracle.attention(qn[b, qq], rc[b], rs[b], idx[b, qq].numpy(), None, 0, 0, sc)
         worst = max(worst, assert_attn_close(o1[b, qq], l1[b, qq], ra, la, "sparse"))
-        ru, lu = oracle.attention(qn[b, qq], rc[b], rs[b], idx[b, qq].numpy(), sw[b], int(slot[b, qq]), window, sc)
+        ru, lu = oracle.attention(qn[b, qq], rc[b], rs[b], idx[b, qq].numpy(), sw[b], int(qpos[b, qq]), window, sc)
         worst = max(worst, assert_attn_close(o2[b, qq], l2[b, qq], ru, lu, "merged"))
     print(f"worst row-relative error {worst:.2e}")
 
 
 def test_swa_only_short_window_and_empty_sparse():
     B, Q, H, D, T = 2, 1, 64, 512, 128
-    cache, q, idx, swa, slot, rc, rs = _attn_inputs(B, Q, H, D, 100, 16, T, torch.bfloat16, "swo")
-    slot = torch.tensor([[0], [5]], dtype=torch.int32)  # first tokens: windows of 1 and 6 rows
+    cache, q, idx, swa, qpos, rc, rs = _attn_inputs(B, Q, H, D, 100, 16, T, torch.bfloat16, "swo")
+    qpos = torch.tensor([[0], [5]], dtype=torch.int32)  # first tokens: windows of 1 and 6 rows
     idx[:] = -1  # no selected entries at all
     sc = 0.05
     o = torch.empty(B, Q, H, D, device=DEV)
@@ -359,11 +361,11 @@ def test_swa_only_short_window_and_empty_sparse():
     torch.cuda.synchronize()
     assert torch.all(torch.isneginf(lse)) and torch.all(o == 0)
     case("swa merge after empty sparse")
-    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), slot.to(DEV), 128, sc, 1, o, lse, ws=ws)
+    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), qpos.to(DEV), 128, sc, 1, o, lse, ws=ws)
     torch.cuda.synchronize()
     for b in range(B):
         ref, lr = oracle.attention(q[b, 0].double().numpy(), None, None, None, swa[b].double().numpy(),
-                                   int(slot[b, 0]), 128, sc)
+                                   int(qpos[b, 0]), 128, sc)
         assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ref, lr, "swa-only")
 
 
@@ -400,3 +402,141 @@ def test_sparse_attn_extreme_magnitudes(qdtype, qlog_lo, qlog_hi, sc):
         ra, la = oracle.attention(q[b, 0].double().numpy(), rc[b], rs[b], idx[b, 0].numpy(), None, 0, 0, sc)
         worst = max(worst, assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ra, la, "extreme"))
     print(f"worst row-relative error {worst:.2e}")
+
+
+# --------------------------------------------------------------------------- Top-K: overflowing threshold bin
+@pytest.mark.parametrize("k,n_above,n_ties,span", [
+    (512, 300, 10000, 70000),   # > 8192 candidates in the row, 300 positions above the bin
+    (2048, 300, 10000, 70000),  # k = 2048: the above-bin positions plus k would overrun a 2048-slot list
+    (2048, 1900, 9000, 70000),  # only 148 picked inside the bin
+    (512, 200, 5000, 16384),    # > 4096 candidates inside one 16384-position chunk (local overflow only)
+    (1024, 0, 9000, 70000)])    # no position above the bin
+def test_topk_overflowing_bin_with_positions_above(k, n_above, n_ties, span):
+    """The threshold bin holds more candidates than the candidate lists keep,
+    so the selection falls back to the whole row, while other positions lie
+    above the bin and are already selected: the fallback may pick only inside
+    the bin."""
+    rows, n = 2, 70000
+    rng = np.random.default_rng(k + n_above + span)
+    s = (rng.standard_normal((rows, n)) - 6.0).astype(np.float32)   # below the tie value's bin
+    s[:, ::13] = -np.inf
+    for r in range(rows):
+        tie_pos = rng.choice(span, n_ties, replace=False)
+        s[r, tie_pos] = 1.5
+        rest = np.setdiff1d(np.arange(n), tie_pos)
+        above = rng.choice(rest, n_above, replace=False)
+        s[r, above] = (10.0 + rng.random(n_above)).astype(np.float32)
+    out = torch.empty(rows, k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(api.csa2_topk_workspace_size(rows, n, k), dtype=torch.uint8, device=DEV)
+    case(f"topk overflow k={k} above={n_above} ties={n_ties} span={span}")
+    api.csa2_topk(torch.from_numpy(s).to(DEV), k, out, ws=ws)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], oracle.topk(s[r], k), err_msg=f"row {r}")
+
+
+# --------------------------------------------------------------------------- canary guards
+GUARD = 4096  # bytes before and after an output
+
+
+def _guarded(shape, dtype):
+    """(whole buffer, view): the view sits between two guard regions filled with 0xA5 bytes."""
+    nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    whole = torch.full((GUARD + nbytes + GUARD,), 0xA5, dtype=torch.uint8, device=DEV)
+    view = whole[GUARD:GUARD + nbytes].view(dtype).view(shape)
+    return whole, view
+
+
+def _guards_intact(whole, what):
+    g = to_np(whole)
+    assert (g[:GUARD] == 0xA5).all() and (g[-GUARD:] == 0xA5).all(), f"{what}: write outside the output"
+
+
+@pytest.mark.parametrize("rows,n,k", [(3, 5000, 512), (4, 16384, 2048), (2, 100000, 512), (2, 100000, 2048)])
+def test_topk_writes_only_its_output(rows, n, k):
+    s = _topk_case(rows, n, k, "coarse", f"guard{n}{k}")
+    whole, out = _guarded((rows, k), torch.int32)
+    ws = torch.empty(max(api.csa2_topk_workspace_size(rows, n, k), 16), dtype=torch.uint8, device=DEV)
+    case(f"topk guards rows={rows} n={n} k={k}")
+    api.csa2_topk(torch.from_numpy(s).to(DEV), k, out, ws=ws)
+    torch.cuda.synchronize()
+    _guards_intact(whole, "topk out")
+    for r in range(rows):
+        np.testing.assert_array_equal(to_np(out)[r], oracle.topk(s[r], k), err_msg=f"row {r}")
+
+
+@pytest.mark.parametrize("B,H,D,K", [(4, 64, 512, 512), (300, 64, 512, 512), (3, 16, 128, 100)])
+def test_attention_writes_only_its_outputs(B, H, D, K):
+    n, T, Q = 3000, 200, 1
+    cache, q, idx, swa, qpos, rc, rs = _attn_inputs(B, Q, H, D, n, K, T, torch.bfloat16, f"gd{B}{H}")
+    wo, o = _guarded((B, Q, H, D), torch.float32)
+    wl, lse = _guarded((B, Q, H), torch.float32)
+    ws = torch.empty(max(api.csa2_attn_workspace_size(B, Q, H, D), 16), dtype=torch.uint8, device=DEV)
+    sc = 1 / math.sqrt(D)
+    case(f"attention guards B={B} H={H} D={D}")
+    api.csa2_sparse_attn_fp4(q.to(DEV), cache, idx.to(DEV), sc, o, lse, ws=ws)
+    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), qpos.to(DEV), 128, sc, 1, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    _guards_intact(wo, "o")
+    _guards_intact(wl, "lse")
+    for b in (0, B - 1):
+        ru, lu = oracle.attention(q[b, 0].double().numpy(), rc[b], rs[b], idx[b, 0].numpy(), swa[b].double().numpy(),
+                                  int(qpos[b, 0]), 128, sc)
+        assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ru, lu, "guarded")
+
+
+# --------------------------------------------------------------------------- FP4 decode inside attention
+def _all_codes_cache(n, D):
+    """n entries whose code bytes run through all 256 values and whose scale
+    bytes run through every finite non-negative E4M3 code 0x00..0x7E."""
+    e = np.arange(n)[:, None]
+    codes = ((e * (D // 2) + np.arange(D // 2)[None]) % 256).astype(np.uint8)
+    scales = ((e * (D // 16) + np.arange(D // 16)[None]) % 127).astype(np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("D,H,qdtype,rows", [
+    (128, 16, torch.float32, 2), (128, 16, torch.bfloat16, 300), (256, 32, torch.bfloat16, 3),
+    (256, 64, torch.float32, 400), (512, 64, torch.float32, 4),
+    (512, 64, torch.bfloat16, 4),     # producer/consumer kernel, keys split over workgroups
+    (512, 64, torch.bfloat16, 300)])  # producer/consumer kernel, whole list per workgroup
+def test_attention_fp4_decode_bit_exact(D, H, qdtype, rows):
+    """A query row that selects exactly one entry (window empty) has softmax
+    weight exactly 1 on it, so its output is that entry's decoded value: the
+    decode attention performs in registers must equal the oracle's FP4 decode
+    bit for bit (signed zeros compare equal: the output sums from +0)."""
+    K = 512
+    n = 64  # entries 0 .. ceil(127 / (D/16)) - 1 already hold every code and scale byte
+    codes, scales = _all_codes_cache(n, D)
+    need = max(-(-127 // (D // 16)), -(-256 // (D // 2)))
+    ref = oracle.fp4_decode(codes, scales)
+    # every query row is its own sequence: one copy of the n entries per sequence
+    # (entry j of sequence b is physical row b * n + j)
+    codes_d = torch.from_numpy(np.tile(codes, (rows, 1))).to(DEV)
+    scales_d = torch.from_numpy(np.tile(scales, (rows, 1))).to(DEV)
+    cache = api.Fp4Cache(codes_d, scales_d, D, n)
+    assert rows * cache.seq_stride <= codes_d.shape[0] and rows * cache.seq_stride <= scales_d.shape[0]
+    sc = 1 / math.sqrt(D)
+    checked = set()
+    for g0 in range(0, n, rows):
+        ent = (np.arange(rows) + g0) % n
+        idx = np.full((rows, 1, K), -1, np.int32)
+        idx[np.arange(rows), 0, (ent * 37) % K] = ent      # the one selected entry at varying list positions
+        q = inputs.normal((rows, 1, H, D), f"fpx{D}{g0}", dtype=qdtype)
+        o = torch.empty(rows, 1, H, D, device=DEV)
+        lse = torch.empty(rows, 1, H, device=DEV)
+        ws = torch.empty(max(api.csa2_attn_workspace_size(rows, 1, H, D), 16), dtype=torch.uint8, device=DEV)
+        case(f"fp4 decode through attention D={D} H={H} {qdtype} rows={rows} group {g0}")
+        api.csa2_sparse_attn_fp4(q.to(DEV), cache, torch.from_numpy(idx).to(DEV), sc, o, lse, ws=ws)
+        torch.cuda.synchronize()
+        got = to_np(o).astype(np.float64)
+        for r in range(rows):
+            np.testing.assert_array_equal(got[r, 0], np.broadcast_to(ref[ent[r]], (H, D)),
+                                          err_msg=f"entry {ent[r]}")
+            checked.add(int(ent[r]))
+        if len(checked) >= need:
+            break
+    cb = np.unique(codes[sorted(checked)])
+    sb = np.unique(scales[sorted(checked)])
+    assert len(cb) == 256 and len(sb) == 127, (len(cb), len(sb))

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from fp4_kv_cache_csa2_amd import api, inputs
-from gpu_common import case, require_gpu, to_np
+from gpu_common import assert_attn_close, case, require_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -138,3 +138,30 @@ def test_replay_full_size_sampled():
                 hf = _f64(hb[b, i])
                 _assert_projection(got[l][b][p % T][None], ref[None], (hf @ Wf.T)[None],
                                    (np.abs(hf) @ np.abs(Wf).T)[None], dm, f"l={l} b={b} i={i}")
+
+
+@pytest.mark.parametrize("T,t_end", [(128, [1000, 4133]), (256, [1000, 300]), (131, [5000, 127])])
+def test_replayed_ring_attended_at_its_position(T, t_end):
+    """Rebuild a window ring by replay at positions whose ring row is not the
+    last one (t_end mod T != T - 1), then attend from the token at t_end: the
+    window must be exactly the replayed tokens t_end-127 .. t_end.  (The layer
+    dispatcher reads rings by the same rule; the ragged workload's rings wrap
+    at arbitrary rows.)"""
+    B, n, dm, D, H, W = 2, 128, 256, 512, 64, 128
+    h, Wp = _make(1, B, n, dm, D, T, f"rpatt{T}")
+    rings = [torch.zeros(B, T, D, dtype=torch.bfloat16, device=DEV)]
+    case(f"replay then window attention T={T} t_end={t_end}")
+    api.csa2_swa_replay([h[0].to(DEV)], [Wp[0].to(DEV)], rings, torch.tensor(t_end, dtype=torch.int32, device=DEV))
+    q = inputs.normal((B, 1, H, D), f"rpatt{T}/q", dtype=torch.bfloat16)
+    qpos = torch.tensor(t_end, dtype=torch.int32).reshape(B, 1)
+    sc = 1 / np.sqrt(D)
+    o = torch.empty(B, 1, H, D, device=DEV)
+    lse = torch.empty(B, 1, H, device=DEV)
+    ws = torch.empty(max(api.csa2_attn_workspace_size(B, 1, H, D), 16), dtype=torch.uint8, device=DEV)
+    api.csa2_swa_attn(q.to(DEV), rings[0], qpos.to(DEV), W, sc, 0, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    hb, Wb = _bits(h[0]), _bits(Wp[0])
+    for b in range(B):
+        ring_ref = oracle.swa_replay(hb[b], Wb, t_end[b], T)
+        ref, lref = oracle.attention(q[b, 0].double().numpy(), None, None, None, _f64(ring_ref), t_end[b], W, sc)
+        assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ref, lref, f"replayed ring b={b}")
