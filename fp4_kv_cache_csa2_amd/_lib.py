@@ -69,6 +69,7 @@ SIGNATURES = {
     "csa2_index_reindex": (ctypes.c_int, [P, i32, i32, i32, ctypes.POINTER(IdxK), P, P, i32, P, P]),
     "csa2_topk_workspace_size": (sz, [i32, i32, i32]),
     "csa2_topk": (ctypes.c_int, [P, i32, i32, i32, P, P, P, sz, P]),
+    "csa2_topk_noalloc": (ctypes.c_int, [P, i32, i32, i32, P, P, P]),
     "csa2_attn_workspace_size": (sz, [i32, i32, i32, i32]),
     "csa2_sparse_attn_fp4": (ctypes.c_int, [P, ctypes.c_int, i32, i32, i32, ctypes.POINTER(Fp4KV), P, i32, f32, P, P,
                                             P, sz, P]),

@@ -164,6 +164,13 @@ def csa2_topk(scores, k, out_idx, pool_blocks=None, ws=None, stream=None):
                                      _stream(stream)))
 
 
+def csa2_topk_noalloc(scores, k, out_idx, pool_blocks=None, stream=None):
+    """Top-K without a workspace (the library's built-in scratch, <= 64 rows past 32768 positions)."""
+    rows, n = scores.shape
+    _lib.check(_lib.load().csa2_topk_noalloc(_ptr(scores), rows, n, k, _ptr(pool_blocks), _ptr(out_idx),
+                                             _stream(stream)))
+
+
 def csa2_attn_workspace_size(B, Q, H, D) -> int:
     return _lib.load().csa2_attn_workspace_size(B, Q, H, D)
 

@@ -28,6 +28,9 @@
 //    counting sort on the positions' top bits.
 // Several independent selections (the Top-K entries and the pool blocks of a
 // Full layer) run in the same launches as separate segments.
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 namespace csa2 {
@@ -820,6 +823,46 @@ void launch_zero_ranges(const ZeroRanges& z, hipStream_t stream) {
     zero_ranges_kernel<<<(unsigned)((mx + 255) / 256), 256, 0, stream>>>(z);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free Top-K: the large path's workspace is a file-scope device
+// array, one per GPU, holding the counters and lists of up to
+// TOPK_NOALLOC_MAX_ROWS rows.  Host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name in host
+// code is not a device address).
+constexpr int TOPK_NOALLOC_MAX_ROWS = 64;
+constexpr size_t TOPK_NOALLOC_COUNTERS =
+    ((size_t)TOPK_NOALLOC_MAX_ROWS * (NBINS1 * 4 + sizeof(TopkRowState)) + 255) & ~(size_t)255;
+constexpr size_t TOPK_NOALLOC_BYTES =
+    TOPK_NOALLOC_COUNTERS + (size_t)TOPK_NOALLOC_MAX_ROWS * (TOPK_KMAX * 4 + TOPK_CAP * 8);
+
+static __device__ __align__(256) uint8_t scratch[TOPK_NOALLOC_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::atomic<void*> g_scratch_ptr[NOALLOC_MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (resolved once per device).
+static csa2_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    CSA2_REQUIRE(e == hipSuccess, CSA2_EHIP, "topk_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    CSA2_REQUIRE(dev >= 0 && dev < NOALLOC_MAX_DEVICES, CSA2_EUNSUPPORTED, "topk_noalloc: device %d out of range",
+                 dev);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            CSA2_REQUIRE(e == hipSuccess && p != nullptr, CSA2_EHIP, "topk_noalloc: hipGetSymbolAddress: %s",
+                         hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CSA2_OK;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -863,4 +906,43 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, i
     topk_launch_hist(segs, stream);
     topk_launch_select(segs, stream);
     return launch_status("topk");
+}
+
+extern "C" csa2_status csa2_topk_noalloc(const float* scores, int32_t rows, int32_t n, int32_t k,
+                                         const int32_t* pool_blocks, int32_t* out_idx, hipStream_t stream) {
+    clear_error();
+    CSA2_ARG(rows >= 0 && n >= 0, "topk_noalloc: rows=%d n=%d must be >= 0", rows, n);
+    CSA2_ARG(k >= 1 && k <= TOPK_KMAX, "topk_noalloc: k=%d must be in [1, %d]", k, TOPK_KMAX);
+    CSA2_ARG(pool_blocks == nullptr || n % 8 == 0, "topk_noalloc: with a pool map n=%d must be a multiple of 8", n);
+    CSA2_ARG(rows <= 65535, "topk_noalloc: rows=%d exceeds 65535", rows);
+    if (rows == 0) return CSA2_OK;
+    CSA2_ARG(out_idx != nullptr, "topk_noalloc: null out_idx");
+    CSA2_ARG(n == 0 || scores != nullptr, "topk_noalloc: null scores");
+    if (n <= TOPK_ONEWG_N) {  // one workgroup per row: no scratch at all
+        topk_launch_small(scores, rows, n, k, pool_blocks, out_idx, stream);
+        return launch_status("topk_noalloc");
+    }
+    CSA2_REQUIRE(rows <= TOPK_NOALLOC_MAX_ROWS, CSA2_EUNSUPPORTED,
+                 "topk_noalloc: rows=%d exceeds the %d rows its built-in scratch holds for n > %d "
+                 "(use csa2_topk with a workspace)",
+                 rows, TOPK_NOALLOC_MAX_ROWS, TOPK_ONEWG_N);
+    void* base = nullptr;
+    const csa2_status st = scratch_address(&base);
+    if (st != CSA2_OK) return st;
+    TopkSegs segs{};
+    segs.nseg = 1;
+    segs.rows = rows;
+    TopkSeg& sg = segs.seg[0];
+    sg.scores = scores;
+    sg.n = n;
+    sg.k = k;
+    sg.pool = pool_blocks;
+    sg.out = out_idx;
+    topk_carve(base, static_cast<char*>(base) + TOPK_NOALLOC_COUNTERS, rows, &sg);
+    // the counters must start at zero; the previous call on this GPU left
+    // them cleared, but a failed or interrupted one may not have
+    topk_launch_zero(segs, stream);
+    topk_launch_hist(segs, stream);
+    topk_launch_select(segs, stream);
+    return launch_status("topk_noalloc");
 }

@@ -211,6 +211,19 @@ size_t csa2_topk_workspace_size(int32_t rows, int32_t n, int32_t k);
 csa2_status csa2_topk(const float* scores, int32_t rows, int32_t n, int32_t k, const int32_t* pool_blocks,
                       int32_t* out_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Allocation-free Top-K, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and result as csa2_topk without the workspace:
+ * rows longer than 32768 positions use a scratch array built into the library
+ * (5,243,904 bytes per GPU, held until the process ends) that serves at most 64
+ * rows; more rows return CSA2_EUNSUPPORTED with nothing enqueued.  The call
+ * allocates nothing.  Every call on one GPU uses that GPU's single scratch
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.  The scratch's counters are cleared by
+ * a kernel each call (no memset node). */
+csa2_status csa2_topk_noalloc(const float* scores, int32_t rows, int32_t n, int32_t k, const int32_t* pool_blocks,
+                              int32_t* out_idx, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Sparse attention over the selected FP4 entries (partial, to be merged with
  * the window).  K = V = the dequantised latent entry (MQA over one latent).
