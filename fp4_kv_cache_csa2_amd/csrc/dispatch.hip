@@ -24,6 +24,7 @@ struct LayerWs {
     size_t attn_bytes;
 };
 
+// the two selections' counters
 inline size_t counter_region(int64_t rows) { return align256(2 * topk_counter_bytes(rows)); }
 
 LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
@@ -100,7 +101,16 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     void* aw = ws + w.attn;
     const int rows32 = (int)rows;
     csa2_status s = CSA2_OK;
-    bool topk_ws_used = false;
+    // every selection counter (row histograms and row states) must be zero
+    // when its kernel starts: cleared here once per (workspace, rows), then
+    // left cleared by the kernels that use them
+    if (!(st->ws_clean && st->clean_ws == a->ws && st->clean_rows == rows32)) {
+        ZeroRanges z{};
+        z.ptr[0] = reinterpret_cast<uint32_t*>(counters);
+        z.count[0] = (int64_t)(counter_region(rows) / 4);
+        z.n = 1;
+        launch_zero_ranges(z, stream);
+    }
     if (mode == CSA2_FULL) {
         // Top-K entries and pool blocks: large selections share the zero /
         // split / finish launches; their first-digit histograms come out of the scan
@@ -120,20 +130,6 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             sb = &segs.seg[segs.nseg++];
             *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool, a->n_vis, 8};
             topk_carve(counters + topk_counter_bytes(rows), lists + topk_list_bytes(rows), rows, sb);
-        }
-        // the histograms and row states must start at zero: cleared here once
-        // per (workspace, rows), then left cleared by the finish pass of every call
-        topk_ws_used = segs.nseg > 0;
-        const bool clean = st->ws_clean && st->clean_ws == a->ws && st->clean_rows == rows32;
-        if (!clean && segs.nseg) {
-            ZeroRanges z{};
-            for (int i = 0; i < segs.nseg; ++i) {
-                z.ptr[z.n] = segs.seg[i].hist;
-                z.count[z.n++] = rows * NBINS1;
-                z.ptr[z.n] = reinterpret_cast<uint32_t*>(segs.seg[i].state);
-                z.count[z.n++] = rows * (int64_t)(sizeof(TopkRowState) / 4);
-            }
-            launch_zero_ranges(z, stream);
         }
         // scores past a row's n_vis are neither written nor read.  Several query
         // rows per sequence: the scan shares each K block among them and the
@@ -160,21 +156,21 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             s = launch_status("layer_forward");
         }
     }
+    if (s == CSA2_OK)
+        s = attn_launch(a->q, a->qt, a->B, a->Q, a->H, a->kv->D, a->kv, st->idx, a->K, a->swa_kv, a->T, a->q_pos,
+                        a->window, a->sm_scale, 0, a->o, a->lse, aw, w.attn_bytes, stream, "layer_forward");
     if (s != CSA2_OK) {
         st->ws_clean = 0;
         return s;
     }
+    st->ws_clean = 1;
+    st->clean_ws = a->ws;
+    st->clean_rows = rows32;
     if (mode == CSA2_FULL) {
-        if (topk_ws_used) {
-            st->ws_clean = 1;
-            st->clean_ws = a->ws;
-            st->clean_rows = rows32;
-        }
         st->has_idx = 1;
         if (a->build_pool) st->has_pool = 1;
     } else if (mode == CSA2_REINDEX) {
         st->has_idx = 1;
     }
-    return attn_launch(a->q, a->qt, a->B, a->Q, a->H, a->kv->D, a->kv, st->idx, a->K, a->swa_kv, a->T, a->q_pos,
-                       a->window, a->sm_scale, 0, a->o, a->lse, aw, w.attn_bytes, stream, "layer_forward");
+    return CSA2_OK;
 }
