@@ -111,7 +111,47 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
         z.n = 1;
         launch_zero_ranges(z, stream);
     }
-    if (mode == CSA2_FULL) {
+    if (mode == CSA2_FULL && a->build_pool && a->P >= a->K) {
+        // The layer's Top-K lies inside its pool whenever P >= K: an entry e of
+        // the Top-K and every block ranked ahead of e's block (by block max,
+        // ties to the lower block) -- each such block holds an entry ranked
+        // ahead of e (its maximum: larger, or equal and at a lower position),
+        // a different one per block, so at most K - 1 blocks precede e's
+        // block.  The scan therefore writes only the block maxima (writing
+        // every entry's score into the read stream costs far more than its
+        // bytes), the pool is selected from them, and the Top-K is selected
+        // from the pool rescored with the same query: the Reindex computation,
+        // bit for bit the scores the scan saw.
+        const int32_t nb = (int32_t)((a->n_max + 7) / 8);
+        const bool b_large = nb > TOPK_ONEWG_N;
+        const bool multi = a->Q >= 2;
+        TopkSegs segs{};
+        segs.rows = rows32;
+        TopkSeg* sb = nullptr;
+        if (b_large) {
+            sb = &segs.seg[segs.nseg++];
+            *sb = TopkSeg{block_max, nb, a->P, nullptr, st->pool, a->n_vis, 8};
+            topk_carve(counters, lists, rows, sb);
+        }
+        s = index_full_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, a->n_max, nullptr, block_max, nullptr,
+                            nullptr, sb && !multi ? sb->hist : nullptr, sb && !multi ? sb->state : nullptr, true,
+                            stream);
+        if (s != CSA2_OK) {
+            st->ws_clean = 0;
+            return s;
+        }
+        if (sb && multi) topk_launch_hist(segs, stream);
+        if (sb)
+            topk_launch_select(segs, stream);
+        else
+            topk_launch_small(block_max, rows32, nb, a->P, nullptr, st->pool, stream, a->n_vis, 8);
+        s = index_reindex_hist(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, st->pool, a->P, pool_scores, nullptr,
+                               nullptr, stream);
+        if (s == CSA2_OK) {
+            topk_launch_small(pool_scores, rows32, 8 * a->P, a->K, st->pool, st->idx, stream);
+            s = launch_status("layer_forward");
+        }
+    } else if (mode == CSA2_FULL) {
         // Top-K entries and pool blocks: large selections share the zero /
         // split / finish launches; their first-digit histograms come out of the scan
         const int32_t n = a->n_max, nb = (int32_t)((a->n_max + 7) / 8);

@@ -163,8 +163,8 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
         reinterpret_cast<float*>(qbar_s)[t] = acc;
     }
     const bool hist = p.hist_e != nullptr;
-    const bool hist_b = !REINDEX && hist && p.hist_b != nullptr;
-    if (hist)
+    const bool hist_b = !REINDEX && p.hist_b != nullptr;
+    if (hist || hist_b)
         for (int i = t; i < NBINS1; i += WAVES * 64) (&hist_s[0][0])[i] = 0u;
     __syncthreads();
 
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
         }
         wave_sync();  // the tile is rewritten by the next iteration
         const float s = valid ? acc : -INFINITY;
-        if (pos < p.n_pos) p.scores[(int64_t)r * p.n_pos + pos] = s;
+        if (p.scores != nullptr && pos < p.n_pos) p.scores[(int64_t)r * p.n_pos + pos] = s;
         if (hist && valid) {
             const uint32_t d = key32(s) >> 21;
             atomicAdd(&hist_s[0][d >> 1], 1u << (16 * (d & 1)));
@@ -243,23 +243,25 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     if (!REINDEX && !p.skip_invisible) {
         for (; blk < p.blocks_per_row; blk += stride) {
             const int64_t pos = blk * EPB + lane;
-            if (pos < p.n_pos) p.scores[(int64_t)r * p.n_pos + pos] = -INFINITY;
+            if (p.scores != nullptr && pos < p.n_pos) p.scores[(int64_t)r * p.n_pos + pos] = -INFINITY;
             if (p.block_max != nullptr && (lane & 7) == 0 && (pos >> 3) < nblocks8)
                 p.block_max[(int64_t)r * nblocks8 + (pos >> 3)] = -INFINITY;
         }
     }
-    if (hist) {
+    if (hist || hist_b) {
         // valid counts: one atomic per wave; bins: only the non-empty ones
         for (int off = 32; off > 0; off >>= 1) {
             n_valid += __shfl_xor(n_valid, off);
             n_valid_b += __shfl_xor(n_valid_b, off);
         }
-        if (lane == 0 && n_valid) atomicAdd(&p.state_e[r].valid, n_valid);
+        if (hist && lane == 0 && n_valid) atomicAdd(&p.state_e[r].valid, n_valid);
         if (hist_b && lane == 0 && n_valid_b) atomicAdd(&p.state_b[r].valid, n_valid_b);
         __syncthreads();
         for (int i = t; i < NBINS1; i += WAVES * 64) {
-            const uint32_t ce = (hist_s[0][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-            if (ce) atomicAdd(&p.hist_e[(int64_t)r * NBINS1 + i], ce);
+            if (hist) {
+                const uint32_t ce = (hist_s[0][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                if (ce) atomicAdd(&p.hist_e[(int64_t)r * NBINS1 + i], ce);
+            }
             if (hist_b) {
                 const uint32_t cb = (hist_s[1][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
                 if (cb) atomicAdd(&p.hist_b[(int64_t)r * NBINS1 + i], cb);
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
             if (rr >= nr) break;
             const int64_t r = r0 + rr;
             const float s = (pos < nvr[rr] && pos < p.n_pos) ? acc[rr] : -INFINITY;
-            if (pos < p.n_pos) p.scores[r * p.n_pos + pos] = s;
+            if (p.scores != nullptr && pos < p.n_pos) p.scores[r * p.n_pos + pos] = s;
             if (p.block_max != nullptr) {
                 float m = s;
                 m = fmaxf(m, __shfl_xor(m, 1));
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void index_multi_kernel(IndexParams 
             const int64_t pos = blk * EPB + lane;
             for (int rr = 0; rr < nr; ++rr) {
                 const int64_t r = r0 + rr;
-                if (pos < p.n_pos) p.scores[r * p.n_pos + pos] = -INFINITY;
+                if (p.scores != nullptr && pos < p.n_pos) p.scores[r * p.n_pos + pos] = -INFINITY;
                 if (p.block_max != nullptr && (lane & 7) == 0 && (pos >> 3) < nblocks8)
                     p.block_max[r * nblocks8 + (pos >> 3)] = -INFINITY;
             }
@@ -414,7 +416,7 @@ csa2_status launch_index(IndexParams& p, int rows, int D_i, bool reindex, hipStr
     if (gx < 1) gx = 1;
     const dim3 block(WAVES * 64);
     const bool contig = !reindex && p.kmap.page_table == nullptr;
-    if (!reindex && p.hist_e == nullptr && p.Q >= 2) {
+    if (!reindex && p.hist_e == nullptr && p.hist_b == nullptr && p.Q >= 2) {
         // RB rows of a sequence per workgroup
         const int rb = p.Q >= 8 ? 8 : (p.Q >= 4 ? 4 : 2);
         const int groups = (rows / p.Q) * ((p.Q + rb - 1) / rb);
@@ -463,7 +465,8 @@ csa2_status csa2::index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, i
     RowMap map;
     csa2_status st = check_common("index_full", q_idx, B, Q, H_i, k, n_vis, n_max, &map);
     if (st != CSA2_OK || (int64_t)B * Q == 0 || n_max == 0) return st;
-    CSA2_ARG(scores != nullptr, "index_full: null scores");
+    // (the dispatcher may ask for the block maxima alone)
+    CSA2_ARG(scores != nullptr || block_max != nullptr, "index_full: null scores and block maxima");
     IndexParams p{};
     p.q_idx = q_idx;
     p.H_i = H_i;
@@ -486,6 +489,7 @@ extern "C" csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t
                                        const csa2_idx_k* k, const int32_t* n_vis, int32_t n_max, float* scores,
                                        float* block_max, hipStream_t stream) {
     clear_error();
+    CSA2_ARG(scores != nullptr || (int64_t)B * Q == 0 || n_max == 0, "index_full: null scores");
     return index_full_hist(q_idx, B, Q, H_i, k, n_vis, n_max, scores, block_max, nullptr, nullptr, nullptr, nullptr,
                            false, stream);
 }

@@ -271,6 +271,7 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     __shared__ uint32_t wave_t[NW], wave_m[NW];
     __shared__ uint32_t counts, tie_n;
     __shared__ uint64_t cstar_s;
+    __shared__ int32_t out_s[TOPK_KMAX];  // the selection in position order, copied out coalesced
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * (int64_t)n;
@@ -314,8 +315,11 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
         nv += key[e] != 0u;
     }
     if (c <= 64) {
-        uint32_t v = 0u;  // largest V with #{lanes: mt >= V} >= c
-        for (int bit = 31; bit >= 0; --bit) {
+        // largest V (a multiple of 2^16) with #{lanes: mt >= V} >= c: the top
+        // 16 key bits bound the selection almost as tightly as all 32, in half
+        // the ballot steps
+        uint32_t v = 0u;
+        for (int bit = 31; bit >= 16; --bit) {
             const uint32_t cand = v | (1u << bit);
             if (__popcll(__ballot(mt >= cand)) >= (uint32_t)c) v = cand;
         }
@@ -413,14 +417,17 @@ __global__ __launch_bounds__(WG) void topk_small_kernel(const float* __restrict_
     }
     uint32_t total;
     uint32_t o = block_excl_scan((uint32_t)__popc(fs), sh, &total);
+    // selected positions into LDS at their output slots, then one coalesced
+    // copy (padded with -1) instead of scattered per-key stores
 #pragma unroll
     for (int e = 0; e < E_SMALL; ++e) {
         if ((fs >> e) & 1u) {
             const int p = t * E_SMALL + e;
-            out[row * (int64_t)k + o++] = pool ? pool_s[p >> 3] * 8 + (p & 7) : p;
+            out_s[o++] = pool ? pool_s[p >> 3] * 8 + (p & 7) : p;
         }
     }
-    for (int i = (int)total + t; i < k; i += WG) out[row * (int64_t)k + i] = -1;
+    __syncthreads();
+    for (int i = t; i < k; i += WG) out[row * (int64_t)k + i] = i < (int)total ? out_s[i] : -1;
 }
 
 // ---------------------------------------------------------------------------

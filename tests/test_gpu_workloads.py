@@ -146,6 +146,27 @@ def test_short_context_pool_is_whole_context():
     check_instance(inst, range(2), range(2))
 
 
+@pytest.mark.parametrize("distinct", [8, 96])
+def test_tied_scores_pool_and_topk(distinct):
+    """Indexer-K rows drawn from a few distinct vectors: scores and block
+    maxima tie in large groups, so the pool and every Top-K are decided by the
+    lower-position rule.  A pool-building Full layer takes its Top-K from its
+    pool (K <= P), which must still equal the Top-K over every entry; the
+    pool-less Full layer and the P < K layer take theirs from all scores."""
+    import dataclasses
+    base = inputs.Workload("tied", B=2, Q=1, N=30000, D=128, H=16, H_i=4, D_i=64, pattern="FRU", P=2048)
+    for w in (base, dataclasses.replace(base, name="tied_small_pool", P=300),
+              dataclasses.replace(base, name="tied_no_pool", pattern="FUU")):
+        inst = workload.make_instance(w)
+        g = torch.Generator(device="cpu").manual_seed(11 + distinct)
+        rows = torch.randn(distinct, w.D_i, generator=g).to(torch.bfloat16)
+        pick = torch.randint(0, distinct, (inst.k_logical.shape[0],), generator=g)
+        # the contiguous view shares the logical K tensor
+        assert inst.kview.k.data_ptr() == inst.k_logical.data_ptr()
+        inst.k_logical.copy_(rows[pick].to(inst.k_logical.device))
+        check_instance(inst, range(2), range(2))
+
+
 def test_full_decode_n4k():
     inst = workload.make_instance(inputs.WORKLOADS["full_decode_n4k"])
     check_instance(inst, [0], [0])
