@@ -889,10 +889,13 @@ __device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, ui
 }
 
 // SPLIT: keys split over workgroups (partials merged afterwards); without it
-// every workgroup takes its row's whole list.
-template <bool SPLIT>
-__global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
-    constexpr int D = PC_D, NW = PC_CONS;
+// every workgroup takes its row's whole list.  NW consumer waves: 4 (wave w:
+// heads 16w..16w+15), or 1 (heads 16z..16z+15 of grid z): a few decode rows
+// split their heads over four workgroups as well as their keys, so that each
+// workgroup loads a quarter of the query and writes a quarter of the partial.
+template <bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p) {
+    constexpr int D = PC_D, NT = 64 * (NW + 4);
     constexpr int NBLK = D / 32, NDT = D / 16, CPR = D / 8;
     using S = Stage<D>;
     __shared__ uint4 ktile[PC_TILES][CHUNK_KEYS * (CPR + KROW_PAD)];
@@ -906,7 +909,8 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     const int64_t row = blockIdx.y;
     const int split = blockIdx.x;
     const int b = (int)(row / p.Q);
-    const int head = 16 * wv + c16;  // (consumers)
+    const int hg = NW == 1 ? (int)blockIdx.z : wv;  // (consumers) head group
+    const int head = 16 * hg + c16;
     const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
     // this workgroup's chunks: c_lo + c for local c in [0, nloc)
     const int c_lo = SPLIT ? split * p.cps : 0;
@@ -928,11 +932,11 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     };
 
     // ---- index loads first, then the consumers' query loads
-    constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + CHUNK_KEYS + PC_NT - 1) / PC_NT;
+    constexpr int KR_IT = (MAX_CPS * CHUNK_KEYS + CHUNK_KEYS + NT - 1) / NT;
     int32_t kent[KR_IT];
 #pragma unroll
     for (int j = 0; j < KR_IT; ++j) {
-        const int i = tid + j * PC_NT;
+        const int i = tid + j * NT;
         const int kpos = c_lo * CHUNK_KEYS + i;
         kent[j] = (i < nk && kpos < p.K) ? p.idx[row * p.K + kpos] : -1;
     }
@@ -945,7 +949,7 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     // ---- physical rows of every key (-1: none), the padding chunk included
 #pragma unroll
     for (int j = 0; j < KR_IT; ++j) {
-        const int i = tid + j * PC_NT;
+        const int i = tid + j * NT;
         if (i >= npad * CHUNK_KEYS) break;
         const int kpos = c_lo * CHUNK_KEYS + i;
         int64_t r = -1;
@@ -1027,7 +1031,7 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pc_kernel(AttnParams p) {
     }
     if (consumer) {
         if (SPLIT)
-            attn_store_partial<D>(p, row, split, wv, lane, head, oacc, m_run, l_run);
+            attn_store_partial<D>(p, row, split, hg, lane, head, oacc, m_run, l_run);
         else
             attn_store<D>(p, row, head, g, oacc, m_run, l_run);
     }
@@ -1191,8 +1195,12 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     // the split instance is separate so that the prefill one keeps its
     // registers for the unsplit loop
     const bool wide = D == 512 && nw == 4 && !f32;
-    if (wide && p.nsplit > 1) attn_pc_kernel<true><<<grid, dim3(PC_NT), 0, stream>>>(p);
-    if (wide && p.nsplit == 1) attn_pc_kernel<false><<<grid, dim3(PC_NT), 0, stream>>>(p);
+    // few rows: the head groups split over workgroups too, while every
+    // workgroup still fits in one round over the CUs (one per CU)
+    const bool hsplit = wide && p.nsplit > 1 && rows * p.nsplit * nw <= 256;
+    if (hsplit) attn_pc_kernel<true, 1><<<dim3(grid.x, grid.y, (unsigned)nw), dim3(64 * 5), 0, stream>>>(p);
+    if (wide && p.nsplit > 1 && !hsplit) attn_pc_kernel<true, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
+    if (wide && p.nsplit == 1) attn_pc_kernel<false, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
 #define CSA2_ATTN_NW(DD, F, NWV) \
     if (!wide && nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
 #define CSA2_ATTN(DD)                                                                                   \
