@@ -24,6 +24,7 @@ namespace {
 
 constexpr int WAVES = 4;      // wavefronts per workgroup
 constexpr int EPB = 64;       // entries per wave block (one per lane)
+constexpr int BM_STASH = 32;  // blocks per wave whose maxima are held back (the launch gives at most 32)
 
 struct IndexParams {
     const uint16_t* q_idx;     // [rows][H_i][DI]
@@ -136,6 +137,10 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     // 16-bit bin counters, two per word; a workgroup scores at most 65535
     // positions (the launch guarantees it), so a half never overflows
     __shared__ uint32_t hist_s[2][NBINS1 / 2];
+    // Full mode: each wave's block maxima wait here and are written after its
+    // last block (interleaved with the K stream, these small writes cost
+    // several times their bytes in read bandwidth)
+    __shared__ float bm_stash[WAVES][REINDEX ? 1 : BM_STASH * 8];
 
     const int t = threadIdx.x;
     const int lane = t & 63, w = t >> 6;
@@ -147,6 +152,7 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     // neither depends on it, so their round trips overlap
     const int64_t stride = (int64_t)gridDim.x * WAVES;
     int64_t blk = (int64_t)blockIdx.x * WAVES + w;
+    const int64_t blk_first = blk;
     const int64_t nbv = REINDEX ? p.blocks_per_row : (min(nv, p.n_pos) + EPB - 1) / EPB;
     // paged Full scan: run blocks skip the per-lane row lookups
     constexpr bool PFAST = !CONTIG && !REINDEX;
@@ -173,7 +179,8 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
     uint32_t n_valid = 0, n_valid_b = 0;  // lane counts for the histograms
 
     // (Full mode: only blocks holding a visible entry are read)
-    for (; blk < nbv; blk += stride) {
+    int it = 0;  // this wave's blocks so far
+    for (; blk < nbv; blk += stride, ++it) {
         const int64_t pos = blk * EPB + lane;
         const bool valid = CONTIG ? (pos < nv && pos < p.n_pos) : (full || row_next != NOROW);
         // An opaque zero, fresh every block: LDS addresses are recomputed each
@@ -230,13 +237,24 @@ __global__ __launch_bounds__(WAVES * 64, REINDEX ? 1 : 2) void index_kernel(Inde
             m = fmaxf(m, __shfl_xor(m, 2));
             m = fmaxf(m, __shfl_xor(m, 4));
             if ((lane & 7) == 0 && (pos >> 3) < nblocks8) {
-                p.block_max[(int64_t)r * nblocks8 + (pos >> 3)] = m;
+                if (it < BM_STASH)
+                    bm_stash[w][REINDEX ? 0 : it * 8 + (lane >> 3)] = m;
+                else
+                    p.block_max[(int64_t)r * nblocks8 + (pos >> 3)] = m;
                 if (hist_b && m != -INFINITY) {
                     const uint32_t d = key32(m) >> 21;
                     atomicAdd(&hist_s[1][d >> 1], 1u << (16 * (d & 1)));
                     ++n_valid_b;
                 }
             }
+        }
+    }
+    if (!REINDEX && p.block_max != nullptr) {
+        wave_sync();
+        // stashed maxima: block blk_first + j stride holds stash entries 8j..8j+7
+        for (int i = lane; i < min(it, BM_STASH) * 8; i += 64) {
+            const int64_t b8 = (blk_first + (int64_t)(i >> 3) * stride) * 8 + (i & 7);
+            if (b8 < nblocks8) p.block_max[(int64_t)r * nblocks8 + b8] = bm_stash[w][REINDEX ? 0 : i];
         }
     }
     // blocks without a visible entry: -inf, unless the readers skip them
