@@ -397,10 +397,13 @@ def main():
     ms_step = t0.elapsed_time(t1) / args.steps
 
     # the dominant kernel alone (Full-mode scan of all B x N entries), timed with
-    # events on the stream it is launched on; same inputs as the step
+    # events on the stream it is launched on; same inputs and outputs as in the
+    # step: a pool-building group (P >= K) writes the block maxima alone, its
+    # Top-K coming from the rescored pool
     rows = inst.rows
     nb = (inst.n_max + 7) // 8
-    scan_scores = torch.empty(rows, inst.n_max, dtype=torch.float32, device=dev)
+    pool_scan = "R" in w.pattern and w.P >= w.K
+    scan_scores = None if pool_scan else torch.empty(rows, inst.n_max, dtype=torch.float32, device=dev)
     scan_bmax = torch.empty(rows, nb, dtype=torch.float32, device=dev)
     ev = []
     for _ in range(args.scan_reps):

@@ -20,15 +20,16 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // knows whether they are still cleared even when n_max, K or P change between
 // calls.  Everything after them is scratch without initial contents.
 struct LayerWs {
-    size_t counters, scores, block_max, pool_scores, lists, attn, total;
-    size_t attn_bytes;
+    size_t counters, scores, block_max, pool_scores, lists, attn, screen, total;
+    size_t attn_bytes, screen_bytes;
 };
 
 // the two selections' counters
 inline size_t counter_region(int64_t rows) { return align256(2 * topk_counter_bytes(rows)); }
 
-LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
+LayerWs layer_ws(int32_t B, int32_t Q, int H, int D, int64_t n_max, int K, int P) {
     (void)K;
+    const int64_t rows = (int64_t)B * Q;
     LayerWs w{};
     const int64_t nblocks = (n_max + 7) / 8;
     size_t off = 0;
@@ -46,6 +47,10 @@ LayerWs layer_ws(int64_t rows, int H, int D, int64_t n_max, int K, int P) {
     w.attn = off;
     w.attn_bytes = attn_workspace_bytes(rows, H, D);
     off = align256(off + w.attn_bytes);
+    // many query rows of short sequences: the screened selection's buffers
+    w.screen = off;
+    w.screen_bytes = screen_ws_bytes(B, Q, (int32_t)n_max);
+    off = align256(off + w.screen_bytes);
     w.total = off;
     return w;
 }
@@ -58,7 +63,7 @@ using namespace csa2;
 extern "C" size_t csa2_layer_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t n_max, int32_t K,
                                             int32_t P) {
     if (B <= 0 || Q <= 0 || n_max < 0 || K <= 0 || P < 0) return 0;
-    return layer_ws((int64_t)B * Q, H, D, n_max, K, P).total;
+    return layer_ws(B, Q, H, D, n_max, K, P).total;
 }
 
 extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args* a, csa2_group_state* st,
@@ -87,7 +92,7 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     // group passes the same P and shares the workspace (and the zeroed Reindex
     // histogram kept in it)
     CSA2_ARG(a->P >= 0 && a->P <= 2048, "layer_forward: P=%d must be in [0, 2048]", a->P);
-    const LayerWs w = layer_ws(rows, a->H, a->kv->D, a->n_max, a->K, a->P);
+    const LayerWs w = layer_ws(a->B, a->Q, a->H, a->kv->D, a->n_max, a->K, a->P);
     CSA2_REQUIRE(a->ws != nullptr && a->ws_bytes >= w.total, CSA2_EWORKSPACE,
                  "layer_forward: workspace of %zu bytes required, %zu given", w.total,
                  a->ws ? a->ws_bytes : (size_t)0);
@@ -151,6 +156,10 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             topk_launch_small(pool_scores, rows32, 8 * a->P, a->K, st->pool, st->idx, stream);
             s = launch_status("layer_forward");
         }
+    } else if (mode == CSA2_FULL && !a->build_pool && screen_applicable(a->B, a->Q, a->k->D_i, a->n_max, a->K)) {
+        // many query rows: matrix-core screen, exact rescoring of the candidates
+        s = screen_select(a->q_idx, a->B, a->Q, a->H_i, a->k, a->n_vis, a->n_max, a->K, ws + w.screen,
+                          w.screen_bytes, scores, st->idx, stream);
     } else if (mode == CSA2_FULL) {
         // Top-K entries and pool blocks: large selections share the zero /
         // split / finish launches; their first-digit histograms come out of the scan

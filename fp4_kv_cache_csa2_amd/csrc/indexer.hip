@@ -507,7 +507,6 @@ extern "C" csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t
                                        const csa2_idx_k* k, const int32_t* n_vis, int32_t n_max, float* scores,
                                        float* block_max, hipStream_t stream) {
     clear_error();
-    CSA2_ARG(scores != nullptr || (int64_t)B * Q == 0 || n_max == 0, "index_full: null scores");
     return index_full_hist(q_idx, B, Q, H_i, k, n_vis, n_max, scores, block_max, nullptr, nullptr, nullptr, nullptr,
                            false, stream);
 }

@@ -96,6 +96,15 @@ csa2_status index_full_hist(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t
                             TopkRowState* st_e, uint32_t* hist_b, TopkRowState* st_b, bool skip_invisible,
                             hipStream_t stream);
 
+// Screened many-row Full selection (matrix-core screen, exact rescoring of the
+// candidates, exact selection): the Top-K of every row into out[rows][K];
+// scratch [rows][n_max] fp32 holds the exact scores of rows selected in full.
+bool screen_applicable(int32_t B, int32_t Q, int32_t D_i, int32_t n_max, int32_t K);
+size_t screen_ws_bytes(int32_t B, int32_t Q, int32_t n_max);
+csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
+                          const int32_t* n_vis, int32_t n_max, int32_t K, void* ws, size_t ws_bytes, float* scratch,
+                          int32_t* out, hipStream_t stream);
+
 csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                         const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,
                         const int32_t* q_pos, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,

@@ -176,11 +176,14 @@ csa2_status csa2_swa_replay(const csa2_replay_args* a, hipStream_t stream);
  *   q_idx  [B][Q][H_i][D_i] bf16 indexer queries (row r = b*Q + q)
  *   k      indexer-K view of B sequences, shared by all heads and layers
  *   n_vis  [B][Q] int32: entries 0..n_vis-1 of sequence b are visible to row r
- *   scores [B*Q][n_max] fp32 out: s_j = sum_h dot(q_h, k_j) for j < n_vis,
- *          -inf for n_vis <= j < n_max.  fp32 evaluation: qbar_c = sum_h q_hc
- *          (h ascending), then an FMA chain over channels ascending, from +0.
+ *   scores [B*Q][n_max] fp32 out, or NULL: s_j = sum_h dot(q_h, k_j) for
+ *          j < n_vis, -inf for n_vis <= j < n_max.  fp32 evaluation: qbar_c =
+ *          sum_h q_hc (h ascending), then an FMA chain over channels
+ *          ascending, from +0.
  *   block_max [B*Q][ceil(n_max/8)] fp32 out or NULL: max score of each aligned
  *          8-entry block (-inf when no entry of the block is visible).
+ *          At least one of scores / block_max is given; block maxima alone
+ *          are what a pool needs (its Top-K follows from the rescored pool).
  * D_i in {64, 128}; 1 <= H_i <= 64; n_vis[r] <= n_max.
  */
 csa2_status csa2_index_full(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,

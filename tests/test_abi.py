@@ -80,6 +80,9 @@ def test_indexer_argument_errors(lib):
     kp = _lib.IdxK(FAKE.value, FAKE.value, 64, 2, 0, 128)   # 2 pages cannot hold 4096 entries
     assert lib.csa2_index_full(FAKE, 1, 1, 8, ctypes.byref(kp), FAKE, 4096, FAKE, None, None) == _lib.CSA2_EINVAL
     assert lib.csa2_index_full(FAKE, 1, 1, 0, ctypes.byref(k), FAKE, 100, FAKE, None, None) == _lib.CSA2_EINVAL
+    # scores may be left out when block maxima are asked for, not both
+    assert lib.csa2_index_full(FAKE, 1, 1, 8, ctypes.byref(k), FAKE, 100, None, None, None) == _lib.CSA2_EINVAL
+    assert "block maxima" in _err(lib)
 
 
 def test_attention_argument_errors(lib):

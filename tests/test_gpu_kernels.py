@@ -180,6 +180,30 @@ def test_index_full_multi_row_bit_exact(Q, paged):
             np.testing.assert_array_equal(bm[b * Q + qq], oracle.block_max(ref))
 
 
+@pytest.mark.parametrize("Q,paged", [(1, False), (1, True), (4, False)])
+def test_index_full_block_max_only(Q, paged):
+    """Scores left out, block maxima only (what a pool needs): the maxima must
+    equal the oracle's, with several blocks per wave held back and written
+    after the stream, ragged visibility and a partial last block."""
+    B, n_max, D_i, H_i = 3, 300001, 128, 8
+    K, kview = _k_view(B, n_max, D_i, f"bmK{Q}{paged}", paged)
+    q = inputs.normal((B, Q, H_i, D_i), f"bmq{Q}", dtype=torch.bfloat16)
+    n_vis = np.tile(np.array([[n_max], [n_max - 2], [12345]], np.int32), (1, Q))
+    if Q > 1:
+        n_vis[:, 1:] -= np.arange(1, Q, dtype=np.int32)
+    nb = (n_max + 7) // 8
+    bmax = torch.full((B * Q, nb), 7.0, device=DEV)
+    case(f"index_full block maxima only Q={Q} paged={paged}")
+    api.csa2_index_full(q.to(DEV), kview, torch.from_numpy(n_vis).to(DEV), n_max, None, bmax)
+    torch.cuda.synchronize()
+    bm = to_np(bmax)
+    for b in range(B):
+        Kb = inputs.bf16_bits(K[b])
+        for qq in range(Q):
+            ref = oracle.index_scores(inputs.bf16_bits(q[b, qq]), Kb, n_vis[b, qq])
+            np.testing.assert_array_equal(bm[b * Q + qq], oracle.block_max(ref))
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_index_reindex_bit_exact(paged):
     B, n_max, D_i, H_i, P = 2, 40000, 128, 8, 700

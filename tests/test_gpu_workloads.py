@@ -167,6 +167,64 @@ def test_tied_scores_pool_and_topk(distinct):
         check_instance(inst, range(2), range(2))
 
 
+def _set_positions(inst, q_pos):
+    """Give every query row its own token position (and so its visible count)."""
+    q_pos = np.asarray(q_pos, np.int32).reshape(inst.w.B, inst.w.Q)
+    inst.q_pos_host = q_pos
+    inst.q_pos = torch.from_numpy(q_pos).to(inst.q_pos.device)
+    inst.n_vis_host = ((q_pos + 1) // inst.w.ratio).astype(np.int32)
+    inst.n_vis = torch.from_numpy(inst.n_vis_host).to(inst.q_pos.device)
+
+
+def _screen_instance(name, N, Q=80, B=2, seed=0):
+    w = inputs.Workload(name, B=B, Q=Q, N=N, D=128, H=16, H_i=8, D_i=128, pattern="FU", window=64)
+    inst = workload.make_instance(w, seed=seed)
+    assert inst.kview.k.data_ptr() == inst.k_logical.data_ptr()
+    return inst
+
+
+def test_screened_selection_many_rows():
+    """Many query rows (the matrix-core screen with exact rescoring): every
+    row's Top-K equals the oracle's, with row tiles and entry tiles both cut
+    short (80 rows of 2 sequences, 5000 entries) and visible counts from 0 to
+    all, including rows with fewer than K entries or blocks."""
+    inst = _screen_instance("screen_rows", N=5000)
+    rng = np.random.default_rng(5)
+    q_pos = rng.integers(0, 5000, size=(2, 80))
+    q_pos[0, :6] = [0, 1, 100, 511, 512, 4999]
+    q_pos[1, :4] = [4999, 4998, 8190 // 2, 7000 // 2]
+    _set_positions(inst, q_pos)
+    check_instance(inst, range(160), [0, 5, 81], heads=slice(0, 16, 4))
+
+
+@pytest.mark.parametrize("kind", ["ties", "near_ties_all_candidates", "near_ties_overflow"])
+def test_screened_selection_adversarial(kind):
+    """Scores that the screen cannot separate: exact ties (K rows from four
+    vectors), and near-ties (one vector plus single-ulp changes) whose scores
+    all fall inside the screen's error band -- every entry is a candidate
+    (exact ranking among them), or more than the candidate buffer holds (the
+    full exact fallback)."""
+    N = 3000 if kind == "near_ties_all_candidates" else 6000
+    inst = _screen_instance("screen_" + kind, N=N, Q=64, B=1, seed=3)
+    n = inst.k_logical.shape[0]
+    g = torch.Generator(device="cpu").manual_seed(17)
+    if kind == "ties":
+        base = torch.randn(4, 128, generator=g).to(torch.bfloat16)
+        k = base[torch.randint(0, 4, (n,), generator=g)]
+    else:
+        base = torch.randn(128, generator=g).to(torch.bfloat16)
+        bits = base.view(torch.int16).repeat(n, 1)
+        # one ulp up or down on three random channels of every row
+        ch = torch.randint(0, 128, (n, 3), generator=g)
+        step = torch.randint(0, 2, (n, 3), generator=g).to(torch.int16) * 2 - 1
+        bits.scatter_add_(1, ch, step)
+        k = bits.view(torch.bfloat16)
+    inst.k_logical.copy_(k.to(inst.k_logical.device))
+    rng = np.random.default_rng(9)
+    _set_positions(inst, rng.integers(N // 2, N, size=(1, 64)))
+    check_instance(inst, range(64), [0, 63], heads=slice(0, 16, 8))
+
+
 def test_full_decode_n4k():
     inst = workload.make_instance(inputs.WORKLOADS["full_decode_n4k"])
     check_instance(inst, [0], [0])
