@@ -20,7 +20,7 @@
 //  3. candidates: the entries with S~ + eps >= tau -- every entry whose exact
 //     score is >= tau, the exact Top-K among them;
 //  4. exact scores of the candidates, then the exact selection by composite
-//     key (score, position) among them.  A row with more candidates than the
+//     key (score, position) among them (one wave per row).  A row with more candidates than the
 //     buffer holds, or whose candidates do not hold K exact scores >= tau,
 //     is scored and selected exactly in full instead.
 #include "select.h"
@@ -30,11 +30,12 @@ namespace {
 
 constexpr int SC_DI = 128;                // indexer width the screen supports
 constexpr int SC_TM = 128;                // query rows per screening workgroup (4 waves x 2 tiles of 16)
-constexpr int SC_TN = 128;                // entries per screening workgroup (8 tiles of 16)
+constexpr int SC_TN = 128;                // entries per staged sub-tile (8 MFMA tiles of 16)
+constexpr int SC_SUB = 8;                 // sub-tiles per screening workgroup (1024 entries)
 constexpr int SC_KROW = SC_DI / 8 + 2;    // 16-byte chunks per staged K row (2 of padding: no bank conflicts)
-constexpr int SC_LCAP = 32;               // candidates per row a screening workgroup gathers in LDS
-constexpr int SC_CAP = 4096;              // candidates kept per row (4 per selecting thread)
-constexpr int SC_MAXN = TOPK_ONEWG_N;     // longest row the screen serves
+constexpr int SC_CAP = 4096;              // candidates kept per row
+constexpr int SC_WCAP = 1024;             // candidates a one-wave selection holds (16 per lane)
+constexpr int SC_MAXN = TOPK_ONEWG_N;     // longest row the screen serves (its position bitmap: 4 KB)
 constexpr float SC_EPS = 0x1p-8f;
 constexpr float SC_UP = 1.0f + 0x1p-20f;  // rounds a computed norm up past its fp32 rounding
 
@@ -52,9 +53,14 @@ struct ScreenParams {
     float* tau;             // [rows]
     uint32_t* ccnt;         // [rows] candidate counts
     int32_t* cand;          // [rows][SC_CAP]
+    float* cscore;          // [rows][SC_CAP] exact scores of the candidates
+    float* kn;              // [B][n_max] ||k||_2 of the entries, rounded up
+    uint32_t* slow;         // [0] rows queued for the workgroup selection, [1] rows taken, [2..] the rows
     float* scratch;         // [rows][n_max] exact scores of a row selected in full
     int32_t* out;           // [rows][K]
 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -74,226 +80,18 @@ __device__ __forceinline__ float key_float(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // qbar of a row, channel c (h ascending, fp32), as the indexer scan sums it
 __device__ __forceinline__ float qbar_channel(const ScreenParams& p, int64_t r, int c) {
     const uint16_t* qr = p.q_idx + r * p.H_i * SC_DI + c;
     float acc = 0.0f;
     for (int h = 0; h < p.H_i; ++h) acc = acc + __uint_as_float((uint32_t)qr[(int64_t)h * SC_DI] << 16);
     return acc;
-}
-
-// ---- 0: bf16(qbar) and ||qbar||_2 of every row (one wave per row)
-__global__ __launch_bounds__(256) void sc_prep_kernel(ScreenParams p) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + w;
-    if (r >= p.rows) return;
-    const float a = qbar_channel(p, r, 2 * lane), b = qbar_channel(p, r, 2 * lane + 1);
-    reinterpret_cast<uint32_t*>(p.qhi + r * SC_DI)[lane] = (uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16);
-    float ss = fmaf(a, a, b * b);
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if (lane == 0) p.qn[r] = (ss < INFINITY) ? sqrtf(ss) * SC_UP : INFINITY;
-}
-
-// ---- 1 and 2: screening products of SC_TM rows x SC_TN entries of one
-// sequence on the matrix cores.  PASS 1 writes the block lower bounds, PASS 2
-// the candidates.  The K tile is staged in LDS (row (key) k at k * SC_KROW
-// chunks), the A operand of v_mfma_f32_16x16x32_bf16 is entry (lane % 16),
-// channels 32 blk + 8 (lane / 16) .. +7, the B operand row (lane % 16) of the
-// wave's 16-row tile; the accumulator holds entries 4 (lane / 16) .. +3 of row
-// (lane % 16).
-template <int PASS>
-__global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p) {
-    __shared__ uint4 kt[SC_TN * SC_KROW];
-    __shared__ __attribute__((aligned(16))) float kns[SC_TN];
-    __shared__ uint32_t nvmax_s;
-    __shared__ uint32_t lc[PASS == 2 ? SC_TM : 1];
-    __shared__ int32_t lcand[PASS == 2 ? SC_TM * SC_LCAP : 1];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, c16 = lane & 15, g = lane >> 4;
-    const int b = blockIdx.z;
-    const int q0 = blockIdx.y * SC_TM;
-    const int64_t e0 = (int64_t)blockIdx.x * SC_TN;
-
-    // the lane's rows (two 16-row tiles per wave)
-    int64_t rr[2];
-    int nvr[2];
-    bool rok[2];
-    uint32_t nvl = 0;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int ql = q0 + 32 * w + 16 * rt + c16;
-        rok[rt] = ql < p.Q;
-        rr[rt] = (int64_t)b * p.Q + (rok[rt] ? ql : 0);
-        nvr[rt] = rok[rt] ? min(max(p.n_vis[rr[rt]], 0), p.n_max) : 0;
-        nvl = max(nvl, (uint32_t)nvr[rt]);
-    }
-    // B operands and the row constants load while the visible range is agreed on
-    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-    bf16x8 qb[2][4];
-    float qnr[2], taur[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const uint4* qp = reinterpret_cast<const uint4*>(p.qhi + rr[rt] * SC_DI);
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint4 v = rok[rt] ? qp[4 * blk + g] : make_uint4(0u, 0u, 0u, 0u);
-            qb[rt][blk] = __builtin_bit_cast(bf16x8, v);
-        }
-        qnr[rt] = p.qn[rr[rt]];
-        taur[rt] = PASS == 2 ? p.tau[rr[rt]] : 0.0f;
-    }
-    if (t == 0) nvmax_s = 0u;
-    if (PASS == 2 && t < SC_TM) lc[t] = 0u;
-    __syncthreads();
-    nvl = wave_umax(nvl);
-    if (lane == 0) atomicMax(&nvmax_s, nvl);
-    __syncthreads();
-    const int64_t nvmax = nvmax_s;
-    if (e0 >= nvmax) return;  // no row of this workgroup sees these entries
-
-    // ---- stage the K tile (entries past every row's view read as zeros) and
-    // the entries' norms: load i of thread t is chunk t % 16 of entry 16 i + t / 16
-#pragma unroll
-    for (int i = 0; i < SC_TN * 16 / 256; ++i) {
-        const int el = 16 * i + (t >> 4), c = t & 15;
-        const int64_t e = e0 + el;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (e < nvmax) v = *reinterpret_cast<const uint4*>(p.k + phys_row(p.kmap, b, e) * SC_DI + 8 * c);
-        kt[el * SC_KROW + c] = v;
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        float ss = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ss = fmaf(bf16_lo(wv[j]), bf16_lo(wv[j]), ss);
-            ss = fmaf(bf16_hi(wv[j]), bf16_hi(wv[j]), ss);
-        }
-        ss += __shfl_xor(ss, 1);
-        ss += __shfl_xor(ss, 2);
-        ss += __shfl_xor(ss, 4);
-        ss += __shfl_xor(ss, 8);
-        if (c == 0) kns[el] = (ss < INFINITY) ? sqrtf(ss) * SC_UP : INFINITY;
-    }
-    __syncthreads();
-
-    float lbv[2][SC_TN / 16];
-#pragma unroll
-    for (int j = 0; j < SC_TN / 16; ++j) {
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, kt[(16 * j + c16) * SC_KROW + 4 * blk + g]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][blk], acc[rt], 0, 0, 0);
-        }
-        const float4 kn4 = *reinterpret_cast<const float4*>(&kns[16 * j + 4 * g]);
-        const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w};
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t e = e0 + 16 * j + 4 * g + i;
-                const bool valid = e < nvr[rt];
-                const float eps = SC_EPS * qnr[rt] * knv[i];
-                if (PASS == 1) {
-                    const float lo = acc[rt][i] - eps;
-                    if (valid && lo == lo) m = fmaxf(m, lo);  // (NaN: no bound)
-                } else if (valid && !(acc[rt][i] + eps < taur[rt])) {  // (NaN: a candidate)
-                    const int rl = 32 * w + 16 * rt + c16;
-                    const uint32_t slot = atomicAdd(&lc[rl], 1u);
-                    if (slot < (uint32_t)SC_LCAP) {
-                        lcand[rl * SC_LCAP + slot] = (int32_t)e;
-                    } else {
-                        const uint32_t gs = atomicAdd(&p.ccnt[rr[rt]], 1u);
-                        if (gs < (uint32_t)SC_CAP) p.cand[rr[rt] * SC_CAP + gs] = (int32_t)e;
-                    }
-                }
-            }
-            if (PASS == 1) lbv[rt][j] = row4_max(m);
-        }
-    }
-    if (PASS == 1) {
-        if (g == 0) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                if (!rok[rt]) continue;
-#pragma unroll
-                for (int j = 0; j < SC_TN / 16; ++j) {
-                    const int64_t bi = e0 / 16 + j;
-                    if (bi < p.nb16) p.lb[rr[rt] * p.nb16 + bi] = lbv[rt][j];
-                }
-            }
-        }
-    } else {
-        __syncthreads();
-        if (t < SC_TM && q0 + t < p.Q) {
-            const uint32_t n = min(lc[t], (uint32_t)SC_LCAP);
-            if (n) {
-                const int64_t r = (int64_t)b * p.Q + q0 + t;
-                const uint32_t base = atomicAdd(&p.ccnt[r], n);
-                for (uint32_t i = 0; i < n && base + i < (uint32_t)SC_CAP; ++i)
-                    p.cand[r * SC_CAP + base + i] = lcand[t * SC_LCAP + i];
-            }
-        }
-    }
-}
-
-// ---- between the passes: tau = the K-th largest block lower bound of each
-// row (-inf when the row has fewer than K blocks or bounds: every visible
-// entry is then a candidate), four 8-bit radix passes over the keys; clears
-// the row's candidate count.
-constexpr int TAU_NT = 256;
-__global__ __launch_bounds__(TAU_NT) void sc_tau_kernel(ScreenParams p) {
-    __shared__ uint32_t h[256];
-    __shared__ uint32_t wsum[TAU_NT / 64];
-    __shared__ uint32_t s_d, s_need;
-    const int64_t r = blockIdx.x;
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const int nv = min(max(p.n_vis[r], 0), p.n_max);
-    const int nb = (nv + 15) / 16;
-    if (t == 0) p.ccnt[r] = 0u;
-    constexpr int E = (SC_MAXN / 16 + TAU_NT - 1) / TAU_NT;
-    uint32_t key[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = t + TAU_NT * e;
-        key[e] = i < nb ? key32(p.lb[r * p.nb16 + i]) : 0u;
-    }
-    uint32_t prefix = 0, need = (uint32_t)p.K;
-    bool ok = nb >= p.K;
-    for (int pass = 0; pass < 4 && ok; ++pass) {
-        const int sh = 24 - 8 * pass;
-        h[t] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (key[e] != 0u && (pass == 0 || (key[e] >> (sh + 8)) == (prefix >> (sh + 8))))
-                atomicAdd(&h[(key[e] >> sh) & 255u], 1u);
-        __syncthreads();
-        // bins from the top: thread t holds bin 255 - t
-        const uint32_t x = h[255 - t];
-        const uint32_t incl = wave_incl_scan(x);
-        if (lane == 63) wsum[wid] = incl;
-        __syncthreads();
-        uint32_t above = incl - x, total = 0;
-#pragma unroll
-        for (int v = 0; v < TAU_NT / 64; ++v) {
-            above += (v < wid) ? wsum[v] : 0u;
-            total += wsum[v];
-        }
-        if (above < need && need <= above + x) {
-            s_d = (uint32_t)(255 - t);
-            s_need = need - above;
-        }
-        __syncthreads();
-        if (total < need) {
-            ok = false;  // (block-uniform) fewer valid bounds than K
-        } else {
-            prefix |= s_d << sh;
-            need = s_need;
-        }
-        __syncthreads();
-    }
-    if (t == 0) p.tau[r] = ok ? key_float(prefix) : -INFINITY;
 }
 
 // exact score of entry j of sequence b (the indexer scan's FMA chain).  qbar
@@ -328,101 +126,506 @@ __device__ __forceinline__ float exact_score(const ScreenParams& p, int b, int64
     return acc;
 }
 
-// ---- 3: exact scores of the candidates and the exact selection (one
-// workgroup per row).  Candidate scores are computed one entry per thread at
-// a time into LDS, then taken into registers as keys (SC_CAP / WG per
-// thread); the full fallback scores the row into its scratch and selects
-// from there.
-__global__ __launch_bounds__(WG) void sc_select_kernel(ScreenParams p) {
+// ---- 0: bf16(qbar) and ||qbar||_2 of every row (one wave per row); clears
+// the queue of rows for the workgroup selection
+__global__ __launch_bounds__(256) void sc_prep_kernel(ScreenParams p) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && threadIdx.x < 2) p.slow[threadIdx.x] = 0u;
+    const int64_t r = (int64_t)blockIdx.x * 4 + w;
+    if (r >= p.rows) return;
+    const float a = qbar_channel(p, r, 2 * lane), b = qbar_channel(p, r, 2 * lane + 1);
+    reinterpret_cast<uint32_t*>(p.qhi + r * SC_DI)[lane] = (uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16);
+    float ss = fmaf(a, a, b * b);
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) p.qn[r] = (ss < INFINITY) ? sqrtf(ss) * SC_UP : INFINITY;
+}
+
+// ---- 1 and 2: screening products of SC_TM rows x SC_SUB sub-tiles of SC_TN
+// entries of one sequence on the matrix cores.  PASS 1 writes the block lower
+// bounds and the entries' norms, PASS 2 the candidates (one global atomic per
+// row and workgroup).  Sub-tiles are staged in two LDS buffers (row (entry) e
+// at e * SC_KROW chunks): the next one's loads fly while the current one is
+// multiplied.  The A operand of v_mfma_f32_16x16x32_bf16 is entry (lane % 16),
+// channels 32 blk + 8 (lane / 16) .. +7, the B operand row (lane % 16) of the
+// wave's 16-row tile; the accumulator holds entries 4 (lane / 16) .. +3 of
+// row (lane % 16).  (kb, lbo, kno: restrict pointers, so that the compiler
+// need not wait for a store before the next K load.)
+template <int PASS, bool CONTIG>
+__global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p, const uint16_t* __restrict__ kb,
+                                                         float* __restrict__ lbo, float* __restrict__ kno) {
+    __shared__ uint4 kt[2][SC_TN * SC_KROW];
+    __shared__ __attribute__((aligned(16))) float kns[2][SC_TN];
+    __shared__ uint32_t nvmax_s;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, c16 = lane & 15, g = lane >> 4;
+    const int b = blockIdx.z;
+    const int q0 = blockIdx.y * SC_TM;
+    const int64_t ew = (int64_t)blockIdx.x * SC_TN * SC_SUB;
+
+    // the lane's rows (two 16-row tiles per wave)
+    int64_t rr[2];
+    int nvr[2];
+    bool rok[2];
+    uint32_t nvl = 0;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int ql = q0 + 32 * w + 16 * rt + c16;
+        rok[rt] = ql < p.Q;
+        rr[rt] = (int64_t)b * p.Q + (rok[rt] ? ql : 0);
+        const int nvl_r = p.n_vis[rr[rt]];  // (loads stay unconditional: rr is a valid row)
+        nvr[rt] = rok[rt] ? min(max(nvl_r, 0), p.n_max) : 0;
+        nvl = max(nvl, (uint32_t)nvr[rt]);
+    }
+    // B operands and the row constants load while the visible range is agreed on
+    bf16x8 qb[2][4];
+    float qe[2], taur[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const uint4* qp = reinterpret_cast<const uint4*>(p.qhi + rr[rt] * SC_DI);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            uint4 v = qp[4 * blk + g];
+            if (!rok[rt]) v = make_uint4(0u, 0u, 0u, 0u);
+            qb[rt][blk] = __builtin_bit_cast(bf16x8, v);
+        }
+        qe[rt] = SC_EPS * p.qn[rr[rt]];
+        taur[rt] = PASS == 2 ? p.tau[rr[rt]] : 0.0f;
+    }
+    if (t == 0) nvmax_s = 0u;
+    __syncthreads();
+    nvl = wave_umax(nvl);
+    if (lane == 0) atomicMax(&nvmax_s, nvl);
+    __syncthreads();
+    const int64_t nvmax = nvmax_s;
+    if (ew >= nvmax) return;  // no row of this workgroup sees these entries
+    const int nloc = (int)min((int64_t)SC_TN * SC_SUB, nvmax - ew);  // entries of this workgroup someone sees
+    const int nsub = (nloc + SC_TN - 1) / SC_TN;
+
+    // staging: load i of thread t is chunk t % 16 of entry 16 i + t / 16 of a
+    // sub-tile, at a 32-bit offset from the workgroup's first entry; entries
+    // nobody sees read the last seen entry (loads stay unconditional: a
+    // conditional load makes the compiler wait for it at once) and are zeroed
+    // when stored
+    constexpr int NLD = SC_TN * 16 / 256;
+    const uint16_t* kw = CONTIG ? kb + ((int64_t)b * p.kmap.seq_stride + ew) * SC_DI : kb;
+    uint4 v[NLD];
+    auto load = [&](int s) {
+        if (CONTIG) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int el = min(s * SC_TN + 16 * i + (t >> 4), nloc - 1);
+                v[i] = *reinterpret_cast<const uint4*>(kw + (uint32_t)el * SC_DI + 8 * (t & 15));
+            }
+        } else {
+            int64_t row[NLD];  // all page lookups first, then all loads
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) row[i] = phys_row(p.kmap, b, ew + min(s * SC_TN + 16 * i + (t >> 4), nloc - 1));
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) v[i] = *reinterpret_cast<const uint4*>(kb + row[i] * SC_DI + 8 * (t & 15));
+        }
+    };
+    auto store = [&](int s, int buf) {
+        float knl[NLD];
+        if (PASS == 2) {
+            // norms from the first pass (the same workgroup coordinates wrote them)
+            if (t < SC_TN) kns[buf][t] = s * SC_TN + t < nloc ? kno[(int64_t)b * p.n_max + ew + s * SC_TN + t] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int el = 16 * i + (t >> 4), c = t & 15;
+            if (s * SC_TN + el >= nloc) v[i] = make_uint4(0u, 0u, 0u, 0u);
+            kt[buf][el * SC_KROW + c] = v[i];
+            if (PASS == 1) {
+                // ||k||^2 of the entry: bf16 pair dot products, then the 16 lanes
+                // holding its chunks (one DPP row) summed
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const uint32_t wv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                float ss = 0.0f;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const bf16x2 x = __builtin_bit_cast(bf16x2, wv[jj]);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+                }
+                ss += __uint_as_float(dpp_src<0xB1>(__float_as_uint(ss)));
+                ss += __uint_as_float(dpp_src<0x4E>(__float_as_uint(ss)));
+                ss += __uint_as_float(dpp_src<0x141>(__float_as_uint(ss)));
+                ss += __uint_as_float(dpp_src<0x140>(__float_as_uint(ss)));
+                knl[i] = (ss < INFINITY) ? sqrtf(ss) * SC_UP : INFINITY;
+            }
+        }
+        if (PASS == 1) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int el = 16 * i + (t >> 4);
+                if ((t & 15) == 0) {
+                    kns[buf][el] = knl[i];
+                    // (every row tile writes the same values: the second pass of the
+                    // same coordinates reads the entries its rows see)
+                    if (s * SC_TN + el < nloc) kno[(int64_t)b * p.n_max + ew + s * SC_TN + el] = knl[i];
+                }
+            }
+        }
+    };
+    load(0);
+    store(0, 0);
+    __syncthreads();
+
+    uint32_t cm[2][SC_SUB];  // PASS 2: candidate bits of sub-tile s, bit 4j + i = entry 16j + 4g + i
+#pragma unroll
+    for (int s = 0; s < SC_SUB; ++s) {
+        cm[0][s] = 0u;
+        cm[1][s] = 0u;
+        if (s < nsub) {
+            const int buf = s & 1;
+            if (s + 1 < nsub) load(s + 1);
+            const int64_t es = ew + (int64_t)s * SC_TN;
+            // entry 16 j + 4 g + i of the sub-tile is visible to row rt iff 16 j + i < lim4[rt]
+            int lim4[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) lim4[rt] = (int)min(max((int64_t)nvr[rt] - es, (int64_t)0), (int64_t)SC_TN) - 4 * g;
+            float lbv[2][SC_TN / 16];
+#pragma unroll
+            for (int j = 0; j < SC_TN / 16; ++j) {
+                f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, kt[buf][(16 * j + c16) * SC_KROW + 4 * blk + g]);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][blk], acc[rt], 0, 0, 0);
+                }
+                const float4 kn4 = *reinterpret_cast<const float4*>(&kns[buf][16 * j + 4 * g]);
+                const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w};
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool valid = 16 * j + i < lim4[rt];
+                        if (PASS == 1) {
+                            // (a NaN bound is dropped by the maximum)
+                            m = fmaxf(m, valid ? fmaf(-qe[rt], knv[i], acc[rt][i]) : -INFINITY);
+                        } else {
+                            // (NaN: a candidate)
+                            const bool c = valid && !(fmaf(qe[rt], knv[i], acc[rt][i]) < taur[rt]);
+                            cm[rt][s] |= (uint32_t)c << (4 * j + i);
+                        }
+                    }
+                    if (PASS == 1) lbv[rt][j] = row4_max(m);
+                }
+            }
+            if (PASS == 1 && g == 0) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    if (!rok[rt]) continue;
+#pragma unroll
+                    for (int j = 0; j < SC_TN / 16; ++j) {
+                        const int64_t bi = es / 16 + j;
+                        if (bi < p.nb16) lbo[rr[rt] * p.nb16 + bi] = lbv[rt][j];
+                    }
+                }
+            }
+            // (the next sub-tile's LDS writes stay after this one's reads: hoisted
+            // above them they would wait for its loads before the products)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < nsub) store(s + 1, buf ^ 1);
+            __syncthreads();
+        }
+    }
+    if (PASS == 2) {
+        // one atomic per row: the four lanes of a row (lane / 16 = 0..3) take
+        // consecutive slots in lane order
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            uint32_t n = 0;
+#pragma unroll
+            for (int s = 0; s < SC_SUB; ++s) n += (uint32_t)__popc(cm[rt][s]);
+            const uint32_t n0 = __shfl(n, c16), n1 = __shfl(n, c16 + 16), n2 = __shfl(n, c16 + 32),
+                           n3 = __shfl(n, c16 + 48);
+            const uint32_t total = n0 + n1 + n2 + n3;
+            uint32_t base = 0;
+            if (g == 0 && rok[rt] && total) base = atomicAdd(&p.ccnt[rr[rt]], total);
+            base = __shfl(base, c16);
+            uint32_t at = base + (g > 0 ? n0 : 0u) + (g > 1 ? n1 : 0u) + (g > 2 ? n2 : 0u);
+#pragma unroll
+            for (int s = 0; s < SC_SUB; ++s) {
+                uint32_t bits = cm[rt][s];
+                while (bits) {
+                    const int bit = __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    if (at < (uint32_t)SC_CAP)
+                        p.cand[rr[rt] * SC_CAP + at] =
+                            (int32_t)(ew + (int64_t)s * SC_TN + 16 * (bit >> 2) + 4 * g + (bit & 3));
+                    ++at;
+                }
+            }
+        }
+    }
+}
+
+// ---- between the passes: tau = the K-th largest block lower bound of each
+// row (-inf when the row has fewer than K blocks or bounds: every visible
+// entry is then a candidate), bit by bit over the keys (one wave per row,
+// SC_MAXN / 16 / 64 bounds per lane); clears the row's candidate count.
+__global__ __launch_bounds__(256) void sc_tau_kernel(ScreenParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= p.rows) return;
+    const int nv = min(max(p.n_vis[r], 0), p.n_max);
+    const int nb = (nv + 15) / 16;
+    if (lane == 0) p.ccnt[r] = 0u;
+    constexpr int E = SC_MAXN / 16 / 64;
+    uint32_t key[E];
+    uint32_t nz = 0;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = p.lb[r * p.nb16 + min(lane + 64 * e, p.nb16 - 1)];  // (unconditional loads)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        key[e] = lane + 64 * e < nb ? key32(x[e]) : 0u;
+        nz += key[e] != 0u;
+    }
+    nz = wave_sum(nz);
+    float tau = -INFINITY;
+    if (nz >= (uint32_t)p.K) {
+        uint32_t v = 0u;  // the largest v with #{key >= v} >= K
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = v | (1u << bit);
+            uint32_t n = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) n += key[e] >= c;
+            if (wave_sum(n) >= (uint32_t)p.K) v = c;
+        }
+        tau = key_float(v);
+    }
+    if (lane == 0) p.tau[r] = tau;
+}
+
+// ---- 3: exact scores of the candidates (one workgroup per row, one
+// candidate per thread at a time: many rows' gathers in flight per CU)
+__global__ __launch_bounds__(256) void sc_rescore_kernel(ScreenParams p) {
+    __shared__ __attribute__((aligned(16))) float qb[SC_DI];
+    const int64_t r = blockIdx.x;
+    const int t = threadIdx.x;
+    const int b = (int)(r / p.Q);
+    const uint32_t n = min(p.ccnt[r], (uint32_t)SC_CAP);
+    if (t < SC_DI) qb[t] = qbar_channel(p, r, t);
+    __syncthreads();
+#pragma unroll 1
+    for (uint32_t i = t; i < n; i += 256) p.cscore[r * SC_CAP + i] = exact_score(p, b, p.cand[r * SC_CAP + i], qb);
+}
+
+// ---- 4: the exact selection among the scored candidates, one wave per row
+// (up to SC_WCAP candidates, SC_WCAP / 64 per lane).  The K-th largest
+// composite key is found bit by bit (the score key, then the position among
+// equal scores), and the selected positions leave in ascending order through
+// a per-wave bitmap of the row's positions.  Rows with more candidates, or
+// whose candidates fail the count check, are queued for the workgroup
+// selection.
+constexpr int SC_WE = SC_WCAP / 64;
+__global__ __launch_bounds__(256) void sc_select_wave_kernel(ScreenParams p) {
+    __shared__ uint32_t bm[4][SC_MAXN / 32];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * 4 + w;
+    if (r >= p.rows) return;
+    const int nv = min(max(p.n_vis[r], 0), p.n_max);
+    const uint32_t cnt = p.ccnt[r];
+    const float tau = p.tau[r];
+    if (cnt > (uint32_t)SC_WCAP) {
+        if (lane == 0) p.slow[2 + atomicAdd(&p.slow[0], 1u)] = (uint32_t)r;
+        return;
+    }
+    const uint32_t ktau = tau == -INFINITY ? 0u : key32(tau);
+    // (loads unconditional: a slot past the count reads slot 0, masked after;
+    // a conditional load would make the compiler wait for it at once)
+    uint32_t key[SC_WE], pos[SC_WE];
+    float sc[SC_WE];
+#pragma unroll
+    for (int e = 0; e < SC_WE; ++e) {
+        const uint32_t i = (uint32_t)(lane + 64 * e);
+        const uint32_t ic = i < cnt ? i : 0u;
+        pos[e] = (uint32_t)p.cand[r * SC_CAP + ic];
+        sc[e] = p.cscore[r * SC_CAP + ic];
+    }
+    uint32_t nval = 0, nge = 0;
+#pragma unroll
+    for (int e = 0; e < SC_WE; ++e) {
+        key[e] = (uint32_t)(lane + 64 * e) < cnt ? key32(sc[e]) : 0u;
+        nval += key[e] != 0u;
+        nge += key[e] != 0u && key[e] >= ktau;
+    }
+    nval = wave_sum(nval);
+    nge = wave_sum(nge);
+    const bool ok = tau == -INFINITY ? cnt == (uint32_t)nv : nge >= (uint32_t)p.K;
+    if (!ok) {
+        if (lane == 0) p.slow[2 + atomicAdd(&p.slow[0], 1u)] = (uint32_t)r;
+        return;
+    }
+    // threshold: score key v, and among keys == v the positions <= pv
+    uint32_t v = 0u, pv = 0xFFFFFFFFu;
+    const uint32_t K = (uint32_t)p.K;
+    if (nval > K) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = v | (1u << bit);
+            uint32_t n = 0;
+#pragma unroll
+            for (int e = 0; e < SC_WE; ++e) n += key[e] >= c;
+            if (wave_sum(n) >= K) v = c;
+        }
+        uint32_t above = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < SC_WE; ++e) {
+            above += key[e] > v;
+            eq += key[e] == v;
+        }
+        above = wave_sum(above);
+        eq = wave_sum(eq);
+        const uint32_t need = K - above;  // 1 <= need <= eq
+        if (need < eq) {
+            // the smallest pv with #{key == v, pos <= pv} >= need (bit by bit
+            // from the top: keep a bit clear while enough positions lie below)
+            pv = 0u;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = pv | ((1u << bit) - 1u);
+                uint32_t n = 0;
+#pragma unroll
+                for (int e = 0; e < SC_WE; ++e) n += key[e] == v && pos[e] <= c;
+                if (wave_sum(n) < need) pv |= 1u << bit;
+            }
+        }
+    }
+    // selected positions into the bitmap, then out in ascending order
+    uint32_t* bmw = bm[w];
+    const int nwords = (p.n_max + 31) / 32;
+    for (int i = lane; i < nwords; i += 64) bmw[i] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int e = 0; e < SC_WE; ++e)
+        if (key[e] != 0u && (key[e] > v || (key[e] == v && pos[e] <= pv)))
+            atomicOr(&bmw[pos[e] >> 5], 1u << (pos[e] & 31));
+    wave_lds_sync();
+    // lane l owns words l * per .. l * per + per - 1
+    const int per = (nwords + 63) / 64;
+    uint32_t mine = 0;
+    for (int i = 0; i < per; ++i) {
+        const int wi = lane * per + i;
+        if (wi < nwords) mine += (uint32_t)__popc(bmw[wi]);
+    }
+    const uint32_t incl = wave_incl_scan(mine);
+    uint32_t at = incl - mine;
+    const uint32_t total = __shfl(incl, 63);
+    int32_t* orow = p.out + r * p.K;
+    for (int i = 0; i < per; ++i) {
+        const int wi = lane * per + i;
+        if (wi >= nwords) break;
+        uint32_t bits = bmw[wi];
+        while (bits) {
+            const int bit = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            if (at < K) orow[at] = wi * 32 + bit;
+            ++at;
+        }
+    }
+    for (uint32_t i = total + lane; i < K; i += 64) orow[i] = -1;
+}
+
+// ---- 5: the queued rows, one workgroup at a time: up to SC_CAP scored
+// candidates selected by radix passes, or (more candidates,
+// or a failed count check) every visible entry scored into the row's scratch
+// and selected from there.
+__global__ __launch_bounds__(WG) void sc_select_wg_kernel(ScreenParams p) {
     __shared__ SelectLds sh;
     __shared__ int sel[TOPK_KMAX];
     __shared__ int tmp[TOPK_KMAX];
     __shared__ __attribute__((aligned(16))) float qb[SC_DI];
-    __shared__ float cs[SC_CAP];
-    __shared__ uint32_t s_valid, s_ge;
-    const int64_t r = blockIdx.x;
-    const int b = (int)(r / p.Q);
+    __shared__ uint32_t s_valid, s_ge, s_row;
     const int t = threadIdx.x;
-    const int nv = min(max(p.n_vis[r], 0), p.n_max);
-    const uint32_t cnt = p.ccnt[r];
-    const float tau = p.tau[r];
-    if (t < SC_DI) qb[t] = qbar_channel(p, r, t);
-    for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
-    if (t == 0) {
-        sh.nsel = 0u;
-        s_valid = 0u;
-        s_ge = 0u;
-    }
-    __syncthreads();
-    const uint32_t ktau = tau == -INFINITY ? 0u : key32(tau);
-    const bool screened = cnt <= (uint32_t)SC_CAP;
-    constexpr int EC = SC_CAP / WG;
-    uint32_t key[EC], pos[EC];
-    if (screened) {
-#pragma unroll 1
-        for (uint32_t i = t; i < cnt; i += WG) cs[i] = exact_score(p, b, p.cand[r * SC_CAP + i], qb);
+    const uint32_t queued = p.slow[0];
+    for (;;) {
         __syncthreads();
-        uint32_t nvalid = 0, nge = 0;
+        if (t == 0) s_row = atomicAdd(&p.slow[1], 1u);
+        __syncthreads();
+        const uint32_t qi = s_row;
+        if (qi >= queued) break;
+        const int64_t r = p.slow[2 + qi];
+        const int b = (int)(r / p.Q);
+        const int nv = min(max(p.n_vis[r], 0), p.n_max);
+        const uint32_t cnt = p.ccnt[r];
+        const float tau = p.tau[r];
+        if (t < SC_DI) qb[t] = qbar_channel(p, r, t);
+        for (int i = t; i < NBINS1; i += WG) sh.hist[0][i] = 0u;
+        if (t == 0) {
+            sh.nsel = 0u;
+            s_valid = 0u;
+            s_ge = 0u;
+        }
+        __syncthreads();
+        const uint32_t ktau = tau == -INFINITY ? 0u : key32(tau);
+        const bool screened = cnt <= (uint32_t)SC_CAP;
+        constexpr int EC = SC_CAP / WG;
+        uint32_t key[EC], pos[EC];
+        if (screened) {
+            uint32_t nvalid = 0, nge = 0;
 #pragma unroll
-        for (int e = 0; e < EC; ++e) {
-            const uint32_t i = (uint32_t)(t + WG * e);
-            key[e] = i < cnt ? key32(cs[i]) : 0u;
-            pos[e] = i < cnt ? (uint32_t)p.cand[r * SC_CAP + i] : 0u;
-            nvalid += key[e] != 0u;
-            nge += key[e] != 0u && key[e] >= ktau;
+            for (int e = 0; e < EC; ++e) {
+                const uint32_t i = (uint32_t)(t + WG * e);
+                key[e] = i < cnt ? key32(p.cscore[r * SC_CAP + i]) : 0u;
+                pos[e] = i < cnt ? (uint32_t)p.cand[r * SC_CAP + i] : 0u;
+                nvalid += key[e] != 0u;
+                nge += key[e] != 0u && key[e] >= ktau;
+            }
+            nvalid = wave_sum(nvalid);
+            nge = wave_sum(nge);
+            if ((t & 63) == 0) {
+                atomicAdd(&s_valid, nvalid);
+                atomicAdd(&s_ge, nge);
+            }
         }
-        nvalid = wave_sum(nvalid);
-        nge = wave_sum(nge);
-        if ((t & 63) == 0) {
-            atomicAdd(&s_valid, nvalid);
-            atomicAdd(&s_ge, nge);
-        }
-    }
-    __syncthreads();
-    // the candidates hold the answer when they hold K exact scores >= tau, or
-    // (tau = -inf: every visible entry is a candidate) all visible entries
-    const bool use = screened && (tau == -INFINITY ? cnt == (uint32_t)nv : s_ge >= (uint32_t)p.K);
-    uint32_t total;
-    if (use) {
-        total = min((uint32_t)p.K, s_valid);
-        if (s_valid > (uint32_t)p.K) {
-            uint64_t prefix = 0, mask = 0;
-            select_regs<EC>(key, pos, (uint32_t)p.K, 0, prefix, mask, sh);
+        __syncthreads();
+        const bool use = screened && (tau == -INFINITY ? cnt == (uint32_t)nv : s_ge >= (uint32_t)p.K);
+        uint32_t total;
+        if (use) {
+            total = min((uint32_t)p.K, s_valid);
+            if (s_valid > (uint32_t)p.K) {
+                uint64_t prefix = 0, mask = 0;
+                select_regs<EC>(key, pos, (uint32_t)p.K, 0, prefix, mask, sh);
 #pragma unroll
-            for (int e = 0; e < EC; ++e)
-                if (key[e] != 0u && (composite(key[e], pos[e]) & mask) >= prefix) sel[atomicAdd(&sh.nsel, 1u)] = (int)pos[e];
-        } else {
+                for (int e = 0; e < EC; ++e)
+                    if (key[e] != 0u && (composite(key[e], pos[e]) & mask) >= prefix)
+                        sel[atomicAdd(&sh.nsel, 1u)] = (int)pos[e];
+            } else {
 #pragma unroll
-            for (int e = 0; e < EC; ++e)
-                if (key[e] != 0u) sel[atomicAdd(&sh.nsel, 1u)] = (int)pos[e];
-        }
-        __syncthreads();
-    } else {
-        // every visible entry, exactly, into the row's scratch; the selection
-        // then runs its radix passes over the scratch
-        float* srow = p.scratch + r * p.n_max;
-        uint32_t nval = 0;
-#pragma unroll 1
-        for (int j = t; j < nv; j += WG) {
-            const float sc = exact_score(p, b, j, qb);
-            srow[j] = sc;
-            nval += key32(sc) != 0u;
-        }
-        nval = wave_sum(nval);
-        if (t == 0) s_valid = 0u;
-        __syncthreads();
-        if ((t & 63) == 0) atomicAdd(&s_valid, nval);
-        __syncthreads();
-        total = min((uint32_t)p.K, s_valid);
-        if (s_valid > (uint32_t)p.K) {
-            select_global_row(srow, nv, (uint32_t)p.K, 0, 0, sh, sel);
-        } else {
-            for (int j = t; j < nv; j += WG)
-                if (key32(srow[j]) != 0u) sel[atomicAdd(&sh.nsel, 1u)] = j;
+                for (int e = 0; e < EC; ++e)
+                    if (key[e] != 0u) sel[atomicAdd(&sh.nsel, 1u)] = (int)pos[e];
+            }
             __syncthreads();
+        } else {
+            // every visible entry, exactly, into the row's scratch; the
+            // selection then runs its radix passes over the scratch
+            float* srow = p.scratch + r * p.n_max;
+            uint32_t nval = 0;
+#pragma unroll 1
+            for (int j = t; j < nv; j += WG) {
+                const float sc = exact_score(p, b, j, qb);
+                srow[j] = sc;
+                nval += key32(sc) != 0u;
+            }
+            nval = wave_sum(nval);
+            if (t == 0) s_valid = 0u;
+            __syncthreads();
+            if ((t & 63) == 0) atomicAdd(&s_valid, nval);
+            __syncthreads();
+            total = min((uint32_t)p.K, s_valid);
+            if (s_valid > (uint32_t)p.K) {
+                select_global_row(srow, nv, (uint32_t)p.K, 0, 0, sh, sel);
+            } else {
+                for (int j = t; j < nv; j += WG)
+                    if (key32(srow[j]) != 0u) sel[atomicAdd(&sh.nsel, 1u)] = j;
+                __syncthreads();
+            }
         }
+        emit_sorted(sel, (int)total, p.n_max, p.K, sh, tmp, p.out, nullptr, r);
     }
-    emit_sorted(sel, (int)total, p.n_max, p.K, sh, tmp, p.out, nullptr, r);
 }
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -438,7 +641,8 @@ size_t screen_ws_bytes(int32_t B, int32_t Q, int32_t n_max) {
     if (Q < 2 || n_max <= 0 || n_max > SC_MAXN) return 0;
     const int64_t rows = (int64_t)B * Q;
     const int64_t nb16 = (n_max + 15) / 16;
-    return al256(rows * SC_DI * 2) + 3 * al256(rows * 4) + al256(rows * nb16 * 4) + al256(rows * SC_CAP * 4) + 256;
+    return al256(rows * SC_DI * 2) + 3 * al256(rows * 4) + al256(rows * nb16 * 4) + 2 * al256(rows * SC_CAP * 4) +
+           al256((rows + 2) * 4) + al256((int64_t)B * n_max * 4) + 256;
 }
 
 csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
@@ -475,14 +679,32 @@ csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H
     p.lb = reinterpret_cast<float*>(w);
     w += al256(rows * (int64_t)p.nb16 * 4);
     p.cand = reinterpret_cast<int32_t*>(w);
+    w += al256(rows * SC_CAP * 4);
+    p.cscore = reinterpret_cast<float*>(w);
+    w += al256(rows * SC_CAP * 4);
+    p.slow = reinterpret_cast<uint32_t*>(w);
+    w += al256((rows + 2) * 4);
+    p.kn = reinterpret_cast<float*>(w);
     p.scratch = scratch;
     p.out = out;
-    sc_prep_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(p);
-    const dim3 grid((unsigned)((n_max + SC_TN - 1) / SC_TN), (unsigned)((Q + SC_TM - 1) / SC_TM), (unsigned)B);
-    sc_gemm_kernel<1><<<grid, 256, 0, stream>>>(p);
-    sc_tau_kernel<<<(unsigned)rows, TAU_NT, 0, stream>>>(p);
-    sc_gemm_kernel<2><<<grid, 256, 0, stream>>>(p);
-    sc_select_kernel<<<(unsigned)rows, WG, 0, stream>>>(p);
+    const unsigned row_blocks = (unsigned)((rows + 3) / 4);
+    sc_prep_kernel<<<row_blocks, 256, 0, stream>>>(p);
+    const dim3 grid((unsigned)((n_max + SC_TN * SC_SUB - 1) / (SC_TN * SC_SUB)), (unsigned)((Q + SC_TM - 1) / SC_TM),
+                    (unsigned)B);
+    const bool contig = p.kmap.page_table == nullptr;
+    if (contig)
+        sc_gemm_kernel<1, true><<<grid, 256, 0, stream>>>(p, p.k, p.lb, p.kn);
+    else
+        sc_gemm_kernel<1, false><<<grid, 256, 0, stream>>>(p, p.k, p.lb, p.kn);
+    sc_tau_kernel<<<row_blocks, 256, 0, stream>>>(p);
+    if (contig)
+        sc_gemm_kernel<2, true><<<grid, 256, 0, stream>>>(p, p.k, p.lb, p.kn);
+    else
+        sc_gemm_kernel<2, false><<<grid, 256, 0, stream>>>(p, p.k, p.lb, p.kn);
+    sc_rescore_kernel<<<(unsigned)rows, 256, 0, stream>>>(p);
+    sc_select_wave_kernel<<<row_blocks, 256, 0, stream>>>(p);
+    // the queued rows: a few workgroups take them in turn (none: they exit at once)
+    sc_select_wg_kernel<<<(unsigned)(rows < 64 ? rows : 64), WG, 0, stream>>>(p);
     return launch_status("screen");
 }
 
