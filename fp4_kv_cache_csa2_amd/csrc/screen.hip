@@ -55,6 +55,9 @@ struct ScreenParams {
     int32_t* cand;          // [rows][SC_CAP]
     float* cscore;          // [rows][SC_CAP] exact scores of the candidates
     float* kn;              // [B][n_max] ||k||_2 of the entries, rounded up
+    float* qbf;             // [rows][128] qbar in fp32 (the exact scores' query)
+    uint2* seg;             // [rows][nwx] (first slot, count) of each screening workgroup's candidates
+    int32_t nwx;            // screening workgroups along the entries
     uint32_t* slow;         // [0] rows queued for the workgroup selection, [1] rows taken, [2..] the rows
     float* scratch;         // [rows][n_max] exact scores of a row selected in full
     int32_t* out;           // [rows][K]
@@ -135,6 +138,7 @@ __global__ __launch_bounds__(256) void sc_prep_kernel(ScreenParams p) {
     if (r >= p.rows) return;
     const float a = qbar_channel(p, r, 2 * lane), b = qbar_channel(p, r, 2 * lane + 1);
     reinterpret_cast<uint32_t*>(p.qhi + r * SC_DI)[lane] = (uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16);
+    reinterpret_cast<float2*>(p.qbf + r * SC_DI)[lane] = make_float2(a, b);
     float ss = fmaf(a, a, b * b);
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     if (lane == 0) p.qn[r] = (ss < INFINITY) ? sqrtf(ss) * SC_UP : INFINITY;
@@ -344,7 +348,10 @@ __global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p, const u
                            n3 = __shfl(n, c16 + 48);
             const uint32_t total = n0 + n1 + n2 + n3;
             uint32_t base = 0;
-            if (g == 0 && rok[rt] && total) base = atomicAdd(&p.ccnt[rr[rt]], total);
+            if (g == 0 && rok[rt]) {
+                if (total) base = atomicAdd(&p.ccnt[rr[rt]], total);
+                p.seg[rr[rt] * p.nwx + blockIdx.x] = make_uint2(base, total);
+            }
             base = __shfl(base, c16);
             uint32_t at = base + (g > 0 ? n0 : 0u) + (g > 1 ? n1 : 0u) + (g > 2 ? n2 : 0u);
 #pragma unroll
@@ -401,18 +408,94 @@ __global__ __launch_bounds__(256) void sc_tau_kernel(ScreenParams p) {
     if (lane == 0) p.tau[r] = tau;
 }
 
-// ---- 3: exact scores of the candidates (one workgroup per row, one
-// candidate per thread at a time: many rows' gathers in flight per CU)
-__global__ __launch_bounds__(256) void sc_rescore_kernel(ScreenParams p) {
-    __shared__ __attribute__((aligned(16))) float qb[SC_DI];
-    const int64_t r = blockIdx.x;
-    const int t = threadIdx.x;
-    const int b = (int)(r / p.Q);
-    const uint32_t n = min(p.ccnt[r], (uint32_t)SC_CAP);
-    if (t < SC_DI) qb[t] = qbar_channel(p, r, t);
+// ---- 3: exact scores of the candidates, by the screening workgroups'
+// coordinates: the workgroup of rows q0..q0+127 and entries ew..ew+1023 takes
+// the candidates the second pass found there (their K rows were just read by
+// the same coordinates, so they come from this XCD's L2), with the rows'
+// qbar staged in LDS; one candidate per thread at a time, the next one located
+// while the current one is scored.
+constexpr int RS_NT = 512;  // threads of the rescoring workgroup
+__global__ __launch_bounds__(RS_NT, 2) void sc_rescore_kernel(ScreenParams p) {
+    // (rows padded by 4 floats: lanes reading one channel of different rows hit
+    // different banks)
+    __shared__ __attribute__((aligned(16))) float qs[SC_TM][SC_DI + 4];
+    __shared__ uint32_t cbase[SC_TM], cnum[SC_TM], cpre[SC_TM + 1];
+    __shared__ uint32_t nvmax_s;
+    const int t = threadIdx.x, lane = t & 63;
+    const int b = blockIdx.z;
+    const int q0 = blockIdx.y * SC_TM;
+    const int64_t ew = (int64_t)blockIdx.x * SC_TN * SC_SUB;
+    if (t == 0) nvmax_s = 0u;
     __syncthreads();
+    // the same visible range as the screening passes (their early exit)
+    uint32_t nvl = 0;
+    if (t < SC_TM && q0 + t < p.Q) nvl = (uint32_t)min(max(p.n_vis[(int64_t)b * p.Q + q0 + t], 0), p.n_max);
+    nvl = wave_umax(nvl);
+    if (lane == 0) atomicMax(&nvmax_s, nvl);
+    __syncthreads();
+    if (ew >= (int64_t)nvmax_s) return;
+    if (t < SC_TM) {
+        uint2 sg = make_uint2(0u, 0u);
+        if (q0 + t < p.Q) {
+            const int64_t r = (int64_t)b * p.Q + q0 + t;
+            sg = p.seg[r * p.nwx + blockIdx.x];
+            const uint32_t cap = (uint32_t)SC_CAP;
+            sg.y = sg.x < cap ? min(sg.y, cap - sg.x) : 0u;  // slots past the buffer are not kept
+        }
+        cbase[t] = sg.x;
+        cnum[t] = sg.y;
+    }
+    // the rows' qbar (rows past Q: zeros, never used)
+    for (int i = t; i < SC_TM * SC_DI / 4; i += RS_NT) {
+        const int rl = i / (SC_DI / 4), c4 = i % (SC_DI / 4);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q0 + rl < p.Q) v = reinterpret_cast<const float4*>(p.qbf + ((int64_t)b * p.Q + q0 + rl) * SC_DI)[c4];
+        *reinterpret_cast<float4*>(&qs[rl][4 * c4]) = v;
+    }
+    __syncthreads();
+    if (t < 64) {
+        // exclusive prefix of the counts (two per lane)
+        const uint32_t a = cnum[2 * t], c = cnum[2 * t + 1];
+        const uint32_t incl = wave_incl_scan(a + c);
+        cpre[2 * t] = incl - a - c;
+        cpre[2 * t + 1] = incl - c;
+        if (t == 63) cpre[SC_TM] = incl;
+    }
+    __syncthreads();
+    const uint32_t total = cpre[SC_TM];
+    // flat index pi -> (row, slot, entry); the next one's lookup and entry load
+    // are issued before the current one is scored
+    auto locate = [&](uint32_t pi, int& rl, uint32_t& slot, int32_t& e) {
+        int lo = 0, hi = SC_TM - 1;  // the last rl with cpre[rl] <= pi
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cpre[mid] <= pi) lo = mid; else hi = mid - 1;
+        }
+        rl = lo;
+        slot = cbase[rl] + (pi - cpre[rl]);
+        e = p.cand[((int64_t)b * p.Q + q0 + rl) * SC_CAP + slot];
+    };
+    uint32_t pi = t;
+    if (pi >= total) return;
+    int rl;
+    uint32_t slot;
+    int32_t e;
+    locate(pi, rl, slot, e);
 #pragma unroll 1
-    for (uint32_t i = t; i < n; i += 256) p.cscore[r * SC_CAP + i] = exact_score(p, b, p.cand[r * SC_CAP + i], qb);
+    while (true) {
+        const uint32_t pn = pi + RS_NT;
+        int rl_n = 0;
+        uint32_t slot_n = 0;
+        int32_t e_n = 0;
+        if (pn < total) locate(pn, rl_n, slot_n, e_n);
+        const int64_t r = (int64_t)b * p.Q + q0 + rl;
+        p.cscore[r * SC_CAP + slot] = exact_score(p, b, e, qs[rl]);
+        if (pn >= total) break;
+        pi = pn;
+        rl = rl_n;
+        slot = slot_n;
+        e = e_n;
+    }
 }
 
 // ---- 4: the exact selection among the scored candidates, one wave per row
@@ -641,8 +724,10 @@ size_t screen_ws_bytes(int32_t B, int32_t Q, int32_t n_max) {
     if (Q < 2 || n_max <= 0 || n_max > SC_MAXN) return 0;
     const int64_t rows = (int64_t)B * Q;
     const int64_t nb16 = (n_max + 15) / 16;
+    const int64_t nwx = (n_max + SC_TN * SC_SUB - 1) / (SC_TN * SC_SUB);
     return al256(rows * SC_DI * 2) + 3 * al256(rows * 4) + al256(rows * nb16 * 4) + 2 * al256(rows * SC_CAP * 4) +
-           al256((rows + 2) * 4) + al256((int64_t)B * n_max * 4) + 256;
+           al256((rows + 2) * 4) + al256((int64_t)B * n_max * 4) + al256(rows * SC_DI * 4) + al256(rows * nwx * 8) +
+           256;
 }
 
 csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H_i, const csa2_idx_k* k,
@@ -685,6 +770,11 @@ csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H
     p.slow = reinterpret_cast<uint32_t*>(w);
     w += al256((rows + 2) * 4);
     p.kn = reinterpret_cast<float*>(w);
+    w += al256((int64_t)B * n_max * 4);
+    p.qbf = reinterpret_cast<float*>(w);
+    w += al256(rows * SC_DI * 4);
+    p.nwx = (int32_t)((n_max + SC_TN * SC_SUB - 1) / (SC_TN * SC_SUB));
+    p.seg = reinterpret_cast<uint2*>(w);
     p.scratch = scratch;
     p.out = out;
     const unsigned row_blocks = (unsigned)((rows + 3) / 4);
@@ -701,7 +791,7 @@ csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H
         sc_gemm_kernel<2, true><<<grid, 256, 0, stream>>>(p, p.k, p.lb, p.kn);
     else
         sc_gemm_kernel<2, false><<<grid, 256, 0, stream>>>(p, p.k, p.lb, p.kn);
-    sc_rescore_kernel<<<(unsigned)rows, 256, 0, stream>>>(p);
+    sc_rescore_kernel<<<grid, RS_NT, 0, stream>>>(p);
     sc_select_wave_kernel<<<row_blocks, 256, 0, stream>>>(p);
     // the queued rows: a few workgroups take them in turn (none: they exit at once)
     sc_select_wg_kernel<<<(unsigned)(rows < 64 ? rows : 64), WG, 0, stream>>>(p);
