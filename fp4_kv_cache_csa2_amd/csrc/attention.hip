@@ -474,15 +474,16 @@ __device__ __forceinline__ void mfma_pipeline_hint() {
 }
 
 template <int NDT>
-__device__ __forceinline__ f16x8 attn_weights2(const f32x4& sa, const f32x4& sb, const int64_t* kra,
-                                               const int64_t* krb, int gz, float zscale, f32x4 (&oacc)[NDT],
-                                               float& m_run, float& l_run) {
+__device__ __forceinline__ f16x8 attn_weights2(const f32x4& sa, const f32x4& sb, uint32_t mk, int gz, float zscale,
+                                               f32x4 (&oacc)[NDT], float& m_run, float& l_run) {
+    // mk: validity bits of A's keys (bits 0-15) and B's (bits 16-31)
     float z[8];
     float mloc = -INFINITY;
+    const uint32_t ma = mk >> (4 * gz), mb = mk >> (16 + 4 * gz);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        z[i] = (kra[4 * gz + i] >= 0) ? sa[i] * zscale : -INFINITY;
-        z[4 + i] = (krb[4 * gz + i] >= 0) ? sb[i] * zscale : -INFINITY;
+        z[i] = ((ma >> i) & 1u) ? sa[i] * zscale : -INFINITY;
+        z[4 + i] = ((mb >> i) & 1u) ? sb[i] * zscale : -INFINITY;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) mloc = fmaxf(mloc, z[i]);
@@ -507,6 +508,32 @@ __device__ __forceinline__ f16x8 attn_weights2(const f32x4& sa, const f32x4& sb,
     }
     l_run = l_run * alpha + rows_sum(psum);
     return pb;
+}
+
+// S^T of two chunks A, B at once, their MFMAs interleaved (A block 0, B
+// block 0, A block 1, ...) over four accumulator chains (A even blocks, B even,
+// A odd, B odd: a dependent MFMA follows three others), each operand read
+// eight MFMAs ahead of its use from a ring of eight registers.
+template <int D>
+__device__ __forceinline__ void attn_scores2(const uint4* ka, const uint4* kb, int cz, int gz,
+                                             const f16x8 (&qhi)[D / 32], f32x4& sa, f32x4& sb) {
+    constexpr int NM = 2 * (D / 32), CPR = D / 8, AHEAD = 8;
+    const int ro = cz * (CPR + KROW_PAD) + gz;
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 op[AHEAD];
+    auto rd = [&](int m) { return ((m & 1) ? kb : ka)[ro + 4 * (m >> 1)]; };
+#pragma unroll
+    for (int m = 0; m < AHEAD; ++m) op[m] = rd(m);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&op[m % AHEAD]);
+        acc[m & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qhi[m >> 1], acc[m & 3], 0, 0, 0);
+        if (m + AHEAD < NM) op[m % AHEAD] = rd(m + AHEAD);
+    }
+    sa = acc[0] + acc[2];
+    sb = acc[1] + acc[3];
 }
 
 template <int D>
@@ -901,6 +928,7 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p)
     __shared__ uint4 ktile[PC_TILES][CHUNK_KEYS * (CPR + KROW_PAD)];
     __shared__ __attribute__((aligned(16))) uint8_t ring[PC_RING * S::SLOT];
     __shared__ int64_t krow[MAX_CPS * CHUNK_KEYS + CHUNK_KEYS];
+    __shared__ uint32_t kval[MAX_CPS + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -947,10 +975,11 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p)
         for (int blk = 0; blk < NBLK; ++blk) qraw[blk] = *reinterpret_cast<const uint4*>(qr + 32 * blk + 8 * g);
     }
     // ---- physical rows of every key (-1: none), the padding chunk included
+    // and one validity bit per key (bit k of kval[c]: key k of chunk c has a
+    // row), from a wave ballot: the 16 keys of a chunk are 16 lanes of a wave
 #pragma unroll
     for (int j = 0; j < KR_IT; ++j) {
         const int i = tid + j * NT;
-        if (i >= npad * CHUNK_KEYS) break;
         const int kpos = c_lo * CHUNK_KEYS + i;
         int64_t r = -1;
         if (i >= nk) {
@@ -960,7 +989,11 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p)
             const int i_w = kpos - p.Kp;
             if (wlo + i_w <= qp) r = (int64_t)b * p.T + (wrow0 + i_w >= p.T ? wrow0 + i_w - p.T : wrow0 + i_w);
         }
-        krow[i] = r;
+        const uint64_t valid = __ballot(r >= 0);
+        if (i < npad * CHUNK_KEYS) {
+            krow[i] = r;
+            if ((lane & 15) == 0) kval[i >> 4] = (uint32_t)(valid >> (lane & 48)) & 0xFFFFu;
+        }
     }
     lds_barrier();
 
@@ -1017,11 +1050,11 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p)
             const int lz = lane + zz, cz = lz & 15, gz = lz >> 4;
             const uint4* ka = ktile[c % PC_TILES];
             const uint4* kb = ktile[(c + 1) % PC_TILES];
-            const f32x4 sa = attn_scores<D, false>(ka, cz, gz, qhi, qlo);
-            const f32x4 sb = attn_scores<D, false>(kb, cz, gz, qhi, qlo);
+            f32x4 sa, sb;
+            attn_scores2<D>(ka, kb, cz, gz, qhi, sa, sb);
             mfma_pipeline_hint<2 * NBLK, 1, 8>();
-            const f16x8 pb = attn_weights2<NDT>(sa, sb, krow + c * CHUNK_KEYS, krow + (c + 1) * CHUNK_KEYS, gz,
-                                                zscale, oacc, m_run, l_run);
+            const uint32_t mk = kval[c] | (kval[c + 1] << 16);
+            const f16x8 pb = attn_weights2<NDT>(sa, sb, mk, gz, zscale, oacc, m_run, l_run);
             attn_pv2<D>(ka, kb, cz, gz, pb, oacc);
         } else if (c + 2 < npad) {
             produce(c + 2);
