@@ -514,10 +514,10 @@ __device__ __forceinline__ f16x8 attn_weights2(const f32x4& sa, const f32x4& sb,
 // block 0, A block 1, ...) over four accumulator chains (A even blocks, B even,
 // A odd, B odd: a dependent MFMA follows three others), each operand read
 // eight MFMAs ahead of its use from a ring of eight registers.
-template <int D>
+template <int D, int AHEAD = 8>
 __device__ __forceinline__ void attn_scores2(const uint4* ka, const uint4* kb, int cz, int gz,
                                              const f16x8 (&qhi)[D / 32], f32x4& sa, f32x4& sb) {
-    constexpr int NM = 2 * (D / 32), CPR = D / 8, AHEAD = 8;
+    constexpr int NM = 2 * (D / 32), CPR = D / 8;
     const int ro = cz * (CPR + KROW_PAD) + gz;
     f32x4 acc[4];
 #pragma unroll
@@ -550,22 +550,17 @@ __device__ __forceinline__ void attn_pv2(const uint4* ka, const uint4* kb, int c
         const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(bb + 32 * dt));
         return __builtin_bit_cast(f16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // operands read eight tiles ahead of the MFMAs that use them
-    constexpr int PG = 8;
-    f16x8 vop[2][PG];
+    // each operand read eight MFMAs ahead of its use, from a ring of eight
+    constexpr int AHEAD = 8;
+    f16x8 vop[AHEAD];
 #pragma unroll
-    for (int j = 0; j < PG; ++j) vop[0][j] = vread(j);
+    for (int j = 0; j < AHEAD; ++j) vop[j] = vread(j);
 #pragma unroll
-    for (int grp = 0; grp < NDT / PG; ++grp) {
-        if (grp + 1 < NDT / PG) {
-#pragma unroll
-            for (int j = 0; j < PG; ++j) vop[(grp + 1) & 1][j] = vread(PG * (grp + 1) + j);
-        }
-#pragma unroll
-        for (int j = 0; j < PG; ++j)
-            oacc[PG * grp + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[grp & 1][j], pb, oacc[PG * grp + j], 0, 0, 0);
+    for (int dt = 0; dt < NDT; ++dt) {
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[dt % AHEAD], pb, oacc[dt], 0, 0, 0);
+        if (dt + AHEAD < NDT) vop[dt % AHEAD] = vread(dt + AHEAD);
     }
-    mfma_pipeline_hint<NDT, 2, 8>();
+    mfma_pipeline_hint<NDT, 2, AHEAD>();
 }
 
 template <int D, bool QF32>
@@ -1070,6 +1065,214 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p)
     }
 }
 
+// Many rows without a key split: one workgroup per CU takes the rows
+// blockIdx.x, blockIdx.x + gridDim.x, ... in turn, so that a row's set-up and
+// output overlap its neighbours' work instead of leaving the CU idle: the
+// producers load the next row's key indices while the current row runs and,
+// during its last chunk pair, turn them into key rows, issue the next row's
+// first copies and dequantise its first pair; meanwhile the consumers store
+// the current output and load the next row's query.  Chunks are numbered across rows (tile buffer
+// and ring slot = running chunk number mod 4), so the next row's first pair
+// lands in the buffers the current row's last pair does not use.  Producer pw
+// sets up the rows of its own keys 4pw..4pw+3 of every chunk (it alone reads
+// them) and one byte per chunk of the validity bits (byte pw of kvb[c]).
+__global__ __launch_bounds__(PC_NT, 1) void attn_pcr_kernel(AttnParams p, int64_t rows) {
+    constexpr int D = PC_D, NW = PC_CONS;
+    constexpr int NBLK = D / 32, NDT = D / 16, CPR = D / 8;
+    constexpr int KPL = (MAX_CPS + 1) * 4 / 64;  // (chunk, key) pairs per producer lane
+    using S = Stage<D>;
+    __shared__ uint4 ktile[PC_TILES][CHUNK_KEYS * (CPR + KROW_PAD)];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[PC_RING * S::SLOT];
+    __shared__ int64_t krow[2][MAX_CPS * CHUNK_KEYS + CHUNK_KEYS];
+    __shared__ uint32_t kvb[2][MAX_CPS + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = gridDim.x;
+    const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
+    const int npad = nchunks + (nchunks & 1);
+    const int n_sp = p.Kp / CHUNK_KEYS;
+    int64_t row = blockIdx.x;
+
+    if (wv < NW) {
+        // ---------------------------------------------------------- consumers
+        const int g = lane >> 4, c16 = lane & 15;
+        const int head = 16 * wv + c16;
+        auto load_q = [&](int64_t r, uint4(&qraw)[NBLK]) {
+            const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (r * p.H + head) * D;
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk) qraw[blk] = *reinterpret_cast<const uint4*>(qr + 32 * blk + 8 * g);
+        };
+        // validity bits of chunk c: producer pw's four keys in byte pw
+        auto bits16 = [](uint32_t x) {
+            return (x & 0xFu) | ((x >> 4) & 0xF0u) | ((x >> 8) & 0xF00u) | ((x >> 12) & 0xF000u);
+        };
+        f16x8 qhi[NBLK];
+        f16x8 qlo[1];
+        const float qf[1][8] = {};
+        float zscale;
+        {
+            uint4 qraw[NBLK];
+            load_q(row, qraw);
+            zscale = q_operand<D, false>(qf, qraw, p.scale_log2, qhi, qlo);
+        }
+        f32x4 oacc[NDT];
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.0f;
+        int gb = 0, buf = 0;  // running number of this row's chunk 0; key-row buffer
+        lds_barrier();
+        for (;;) {
+            const uint32_t* kv = kvb[buf];
+            auto pair = [&](int c, f32x4& sa, f32x4& sb) {
+                int zz;
+                asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+                const int lz = lane + zz, cz = lz & 15, gz = lz >> 4;
+                attn_scores2<D, 6>(ktile[(gb + c) & 3], ktile[(gb + c + 1) & 3], cz, gz, qhi, sa, sb);
+                mfma_pipeline_hint<2 * NBLK, 1, 6>();
+                (void)gz;
+            };
+            auto finish = [&](int c, const f32x4& sa, const f32x4& sb) {
+                int zz;
+                asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+                const int lz = lane + zz, cz = lz & 15, gz = lz >> 4;
+                const uint32_t mk = bits16(kv[c]) | (bits16(kv[c + 1]) << 16);
+                const f16x8 pb = attn_weights2<NDT>(sa, sb, mk, gz, zscale, oacc, m_run, l_run);
+                attn_pv2<D>(ktile[(gb + c) & 3], ktile[(gb + c + 1) & 3], cz, gz, pb, oacc);
+            };
+            for (int c = 0; c < npad - 2; c += 2) {
+                f32x4 sa, sb;
+                pair(c, sa, sb);
+                finish(c, sa, sb);
+                lds_barrier();
+            }
+            // last pair, this row's output, then the next row's query (its
+            // load overlaps the producers' set-up of the next row)
+            const bool more = row + G < rows;
+            f32x4 sa, sb;
+            pair(npad - 2, sa, sb);
+            finish(npad - 2, sa, sb);
+            attn_store<D>(p, row, head, g, oacc, m_run, l_run);
+            if (!more) {
+                lds_barrier();
+                break;
+            }
+            // an opaque zero after the stores: the compiler may not clear the
+            // accumulators early (two live copies of them do not fit)
+            float z0;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(z0)::"memory");
+            {
+                uint4 qraw[NBLK];
+                load_q(row + G, qraw);
+                zscale = q_operand<D, false>(qf, qraw, p.scale_log2, qhi, qlo);
+            }
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{z0, z0, z0, z0};
+            m_run = -INFINITY;
+            l_run = 0.0f;
+            row += G;
+            gb += npad;
+            buf ^= 1;
+            lds_barrier();
+        }
+    } else {
+        // ---------------------------------------------------------- producers
+        const int pw = wv - NW;
+        // (chunk, key) pair t = lane + 64 j of this producer: chunk t / 4,
+        // key 4 pw + t % 4 of it, position 16 (t / 4) + 4 pw + t % 4
+        int32_t kent[KPL];
+        auto load_idx = [&](int64_t r) {
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const int t = lane + 64 * j;
+                const int kpos = (t >> 2) * CHUNK_KEYS + 4 * pw + (t & 3);
+                kent[j] = (kpos < p.K && (t >> 2) < npad) ? p.idx[r * p.K + kpos] : -1;
+            }
+        };
+        // key rows of row r into krow[bf], validity bits into byte pw of kvb[bf]
+        auto set_rows = [&](int64_t r, int bf) {
+            const int b = (int)(r / p.Q);
+            const int qp = p.Wp ? p.q_pos[r] : -1;
+            const int wlo = max(0, qp - p.window + 1);
+            const int wrow0 = p.Wp ? wlo % p.T : 0;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const int t = lane + 64 * j;
+                const int c = t >> 2;
+                const int kpos = c * CHUNK_KEYS + 4 * pw + (t & 3);
+                int64_t rr = -1;
+                if (c >= nchunks) {
+                } else if (kpos < p.Kp) {
+                    if (kent[j] >= 0) rr = phys_row(p.kvmap, b, kent[j]);
+                } else {
+                    const int i_w = kpos - p.Kp;
+                    if (wlo + i_w <= qp)
+                        rr = (int64_t)b * p.T + (wrow0 + i_w >= p.T ? wrow0 + i_w - p.T : wrow0 + i_w);
+                }
+                const uint64_t valid = __ballot(rr >= 0);
+                if (c < npad) {
+                    krow[bf][kpos] = rr;
+                    if ((t & 3) == 0)
+                        reinterpret_cast<uint8_t*>(kvb[bf])[4 * c + pw] = (uint8_t)((valid >> (lane & 60)) & 0xFu);
+                }
+            }
+        };
+        int gb = 0, buf = 0, issued = 0;
+        auto sparse_chunk = [&](int c) { return c < n_sp || (c >= nchunks && p.Wp == 0); };
+        auto issue = [&](int c) {
+            pc_issue(p, sparse_chunk(c), krow[buf] + c * CHUNK_KEYS, ring + ((gb + c) % PC_RING) * S::SLOT, pw, lane);
+        };
+        auto produce = [&](int c) {
+            int later = 0;
+            for (int ch = c + 1; ch < issued; ++ch) later += pc_copies(sparse_chunk(ch));
+            wait_vm_at_most(later);
+            int zz;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
+            const int co = lane + zz;
+            const uint8_t* st = ring + ((gb + c) % PC_RING) * S::SLOT;
+            uint4* kt = ktile[(gb + c) & 3];
+            if (sparse_chunk(c))
+                pc_store<true>(st, pw, co, kt);
+            else
+                pc_store<false>(st, pw, co, kt);
+            if (issued < npad) {
+                issue(issued);
+                ++issued;
+            }
+        };
+        // a row's first copies and first pair
+        auto start_row = [&]() {
+            issued = min(npad, PC_RING);
+            for (int ch = 0; ch < issued; ++ch) issue(ch);
+            produce(0);
+            produce(1);
+        };
+        load_idx(row);
+        set_rows(row, 0);
+        if (row + G < rows) load_idx(row + G);
+        start_row();
+        lds_barrier();
+        for (;;) {
+            for (int c = 0; c < npad - 2; c += 2) {
+                produce(c + 2);
+                produce(c + 3);
+                lds_barrier();
+            }
+            if (row + G >= rows) {
+                lds_barrier();
+                break;
+            }
+            row += G;
+            gb += npad;
+            buf ^= 1;
+            set_rows(row, buf);
+            if (row + G < rows) load_idx(row + G);
+            start_row();
+            lds_barrier();
+        }
+    }
+}
+
 // Merge the split partials: exact log-sum-exp combination, optionally together
 // with the (o, lse) already in the output.  One workgroup (one wave: many
 // small workgroups spread the loads over all CUs) = one row x one 16-head
@@ -1132,6 +1335,19 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
 }
 
 constexpr int MAX_SPLIT = 64;
+
+// compute units of the current device (cached per device)
+int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 int choose_nsplit(int64_t rows, int nchunks) {
     if (nchunks <= 1) return 1;
@@ -1233,7 +1449,11 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     const bool hsplit = wide && p.nsplit > 1 && rows * p.nsplit * nw <= 256;
     if (hsplit) attn_pc_kernel<true, 1><<<dim3(grid.x, grid.y, (unsigned)nw), dim3(64 * 5), 0, stream>>>(p);
     if (wide && p.nsplit > 1 && !hsplit) attn_pc_kernel<true, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
-    if (wide && p.nsplit == 1) attn_pc_kernel<false, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
+    // many rows: one persistent workgroup per CU walks over them
+    const int64_t ncu = device_cus();
+    const bool persist = wide && p.nsplit == 1 && rows > ncu && nchunks >= 2;
+    if (persist) attn_pcr_kernel<<<dim3((unsigned)ncu), dim3(PC_NT), 0, stream>>>(p, rows);
+    if (wide && p.nsplit == 1 && !persist) attn_pc_kernel<false, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
 #define CSA2_ATTN_NW(DD, F, NWV) \
     if (!wide && nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
 #define CSA2_ATTN(DD)                                                                                   \
