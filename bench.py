@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -100,6 +101,9 @@ def parse():
     ap.add_argument("--scan-reps", type=int, default=21, help="timed launches of the indexer scan")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-footprint-mib", type=int, default=512,
+                    help="rotate up to 8 copies of the inputs so that consecutive timed steps touch at least "
+                         "this much memory (more than the last-level cache holds)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run three plain device-to-device copies of this many MiB (the calibration "
                          "kernel for the HBM byte counters)")
@@ -335,63 +339,79 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    inst = workload.make_instance(w)
-    run = workload.StackRunner(inst)
-    dev = inst.latent.device
+
+    def build():
+        inst = workload.make_instance(w)
+        run = workload.StackRunner(inst)
+        dev = inst.latent.device
+        # everything a decode step stores about its new tokens, one launch per
+        # token: the FP4 main-KV entry (re-quantised into the last Q entries of
+        # each sequence), its indexer key, and every layer's window row at the
+        # token's ring row (the rows already there, so the instance stays
+        # unchanged)
+        new = []
+        for q in range(w.Q if decode else 0):
+            last = inst.lengths - w.Q + q
+            rows = torch.from_numpy(inst.offsets[:-1] + last).to(dev)
+            tok_h = inst.q_pos_host[:, q].astype(np.int64)
+            bidx = torch.arange(w.B, device=dev)
+            ring_row = torch.from_numpy(tok_h % inst.T).to(dev)
+            new.append(dict(x=inst.latent[rows].contiguous(), pos=torch.from_numpy(last).to(dev),
+                            k_new=inst.k_logical[rows].contiguous(),
+                            swa_new=[L["swa"][bidx, ring_row].contiguous() for L in inst.layers],
+                            tok=torch.from_numpy(tok_h.astype(np.int32)).to(dev)))
+        swa_kv = [L["swa"] for L in inst.layers]
+
+        def step():
+            for a in new:
+                api.csa2_append_token(a["x"], a["pos"], inst.cache, a["k_new"], inst.kview, a["swa_new"], swa_kv,
+                                      a["tok"])
+            run.step()
+
+        return inst, step
+
+    inst, step0 = build()
     stream = torch.cuda.current_stream()
+    ab = alg_bytes(w, int(inst.lengths.sum()))
+    # a step whose inputs would stay in the 256 MB last-level cache between
+    # steps is measured over rotating copies of them (same data, other
+    # addresses), so that the steps timed together touch min_footprint bytes
+    n_copies = max(1, min(8, math.ceil(args.min_footprint_mib * 2**20 / ab["total"])))
+    sets = [(inst, step0)] + [build() for _ in range(n_copies - 1)]
 
-    # everything a decode step stores about its new tokens, one launch per token:
-    # the FP4 main-KV entry (re-quantised into the last Q entries of each
-    # sequence), its indexer key, and every layer's window row at the token's
-    # ring row (the rows already there, so the instance stays unchanged)
-    new = []
-    for q in range(w.Q if decode else 0):
-        last = inst.lengths - w.Q + q
-        rows = torch.from_numpy(inst.offsets[:-1] + last).to(dev)
-        tok_h = inst.q_pos_host[:, q].astype(np.int64)
-        bidx = torch.arange(w.B, device=dev)
-        ring_row = torch.from_numpy(tok_h % inst.T).to(dev)
-        new.append(dict(x=inst.latent[rows].contiguous(), pos=torch.from_numpy(last).to(dev),
-                        k_new=inst.k_logical[rows].contiguous(),
-                        swa_new=[L["swa"][bidx, ring_row].contiguous() for L in inst.layers],
-                        tok=torch.from_numpy(tok_h.astype(np.int32)).to(dev)))
-    swa_kv = [L["swa"] for L in inst.layers]
-
-    def step():
-        for a in new:
-            api.csa2_append_token(a["x"], a["pos"], inst.cache, a["k_new"], inst.kview, a["swa_new"], swa_kv,
-                                  a["tok"])
-        run.step()
-
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, n_copies)):
+        sets[i % n_copies][1]()
     torch.cuda.synchronize()
 
     # eager timing (every call launched from Python)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        sets[i % n_copies][1]()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / args.steps
 
-    # the whole step captured once as a HIP graph, then replayed: the timed region
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(args.warmup):
-        graph.replay()
+    # each copy's whole step captured once as a HIP graph, then the graphs
+    # replayed in turn: the timed region
+    graphs = []
+    for _, step in sets:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        graphs.append(graph)
+    for i in range(max(args.warmup, n_copies)):
+        graphs[i % n_copies].replay()
     torch.cuda.synchronize()
     t0.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
+    for i in range(args.steps):
+        graphs[i % n_copies].replay()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
@@ -401,23 +421,23 @@ def main():
     # step: a pool-building group (P >= K) writes the block maxima alone, its
     # Top-K coming from the rescored pool
     rows = inst.rows
+    dev = inst.latent.device
     nb = (inst.n_max + 7) // 8
     pool_scan = "R" in w.pattern and w.P >= w.K
     scan_scores = None if pool_scan else torch.empty(rows, inst.n_max, dtype=torch.float32, device=dev)
     scan_bmax = torch.empty(rows, nb, dtype=torch.float32, device=dev)
     ev = []
-    for _ in range(args.scan_reps):
+    for i in range(args.scan_reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ci = sets[i % n_copies][0]
         e0.record(stream)
-        api.csa2_index_full(inst.layers[0]["q_idx"], inst.kview, inst.n_vis, inst.n_max, scan_scores, scan_bmax)
+        api.csa2_index_full(ci.layers[0]["q_idx"], ci.kview, ci.n_vis, ci.n_max, scan_scores, scan_bmax)
         e1.record(stream)
         ev.append((e0, e1))
     torch.cuda.synchronize()
     scan_ms = [a.elapsed_time(b) for a, b in ev]
     scan_avg_ms = sum(scan_ms[1:]) / max(1, len(scan_ms) - 1)  # the first launch warms the caches' TLBs
 
-    n_total = int(inst.lengths.sum())
-    ab = alg_bytes(w, n_total)
     # several query rows per sequence: one workgroup scores them all from each K block
     scan_kernel = SCAN_KERNEL if w.Q == 1 else "index_multi_kernel<128, true, %d>" % (8 if w.Q >= 8 else 4 if w.Q >= 4 else 2)
     qtok = rows / (ms_step / 1e3)
@@ -442,6 +462,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Q": w.Q, "N": inst.n_max, "pattern": w.pattern, "D": w.D,
                    "H": w.H, "H_i": w.H_i, "D_i": w.D_i, "K": w.K, "pool": f"{w.P}x8", "window": w.window},
         "step_alg_bytes": ab["total"],
+        "input_copies": n_copies,
         "step_hbm_GBps": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": scan_kernel + " (Full-mode indexer scan)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
