@@ -393,6 +393,52 @@ def test_swa_only_short_window_and_empty_sparse():
         assert_attn_close(to_np(o)[b, 0], to_np(lse)[b, 0], ref, lr, "swa-only")
 
 
+@pytest.mark.parametrize("B,K,window", [(300, 512, 128), (290, 200, 24)])
+def test_many_rows_paged_cache(B, K, window):
+    """More query rows than compute units at D = 512, H = 64 (persistent
+    workgroups, each walking several rows) over a paged FP4 cache, so that every
+    key row goes through the page table; the second case's 13 sparse chunks
+    give an odd count (padding chunk).  Sampled rows against the oracle, the
+    window merged into the sparse output."""
+    H, D, n, T, ps = 64, 512, 640, 200, 64
+    tag = f"mrp{B}{K}"
+    lat = inputs.normal((B, n, D), tag + "/lat")
+    c_log = torch.empty(B * n, D // 2, dtype=torch.uint8, device=DEV)
+    s_log = torch.empty(B * n, D // 16, dtype=torch.uint8, device=DEV)
+    api.csa2_fp4_quantize(lat.reshape(B * n, D).to(DEV), c_log, s_log)
+    table, n_pages = inputs.random_page_table(np.full(B, n), ps, tag + "/pages")
+    phys = (table.astype(np.int64)[:, :, None] * ps + np.arange(ps)[None, None, :]).reshape(-1)
+    codes = torch.zeros(n_pages * ps, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(n_pages * ps, D // 16, dtype=torch.uint8, device=DEV)
+    pr = torch.from_numpy(phys).to(DEV)
+    codes[pr] = c_log
+    scales[pr] = s_log
+    cache = api.Fp4Cache(codes, scales, D, 0, torch.from_numpy(table).to(DEV), ps)
+    q = inputs.normal((B, 1, H, D), tag + "/q", dtype=torch.bfloat16)
+    idx = inputs.small_ints((B, 1, K), tag + "/idx", -1, n - 1, dtype=torch.int32)
+    swa = inputs.normal((B, T, D), tag + "/swa", dtype=torch.bfloat16)
+    qpos = inputs.small_ints((B, 1), tag + "/qpos", 0, 5000, dtype=torch.int32)
+    qpos.view(-1)[1] = 5
+    rc, rs = oracle.fp4_encode(lat.reshape(B * n, D).numpy())
+    rc, rs = rc.reshape(B, n, -1), rs.reshape(B, n, -1)
+    sc = 1 / math.sqrt(D)
+    o = torch.empty(B, 1, H, D, device=DEV)
+    lse = torch.empty(B, 1, H, device=DEV)
+    ws = torch.empty(max(api.csa2_attn_workspace_size(B, 1, H, D), 16), dtype=torch.uint8, device=DEV)
+    case(f"many rows paged B={B} K={K} window={window}")
+    api.csa2_sparse_attn_fp4(q.to(DEV), cache, idx.to(DEV), sc, o, lse, ws=ws)
+    api.csa2_swa_attn(q.to(DEV), swa.to(DEV), qpos.to(DEV), window, sc, 1, o, lse, ws=ws)
+    torch.cuda.synchronize()
+    og, lg = to_np(o), to_np(lse)
+    qn, sw = q.double().numpy(), swa.double().numpy()
+    pick = [0, 1, B - 1] + list(np.random.default_rng(B + K).choice(B, 13, replace=False))
+    worst = 0.0
+    for b in pick:
+        ru, lu = oracle.attention(qn[b, 0], rc[b], rs[b], idx[b, 0].numpy(), sw[b], int(qpos[b, 0]), window, sc)
+        worst = max(worst, assert_attn_close(og[b, 0], lg[b, 0], ru, lu, f"row {b}"))
+    print(f"worst row-relative error {worst:.2e}")
+
+
 @pytest.mark.parametrize("qdtype,qlog_lo,qlog_hi,sc", [
     (torch.bfloat16, -6.0, 1.5, None), (torch.float32, -6.0, 1.5, None),
     (torch.bfloat16, 3.0, 6.0, 1e-6), (torch.float32, 3.0, 6.0, 1e-6)])
