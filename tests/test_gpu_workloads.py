@@ -257,8 +257,13 @@ def test_ragged_paged_b64():
 
 def test_encoder_prefill_q2k_n32k():
     inst = workload.make_instance(inputs.WORKLOADS["encoder_prefill_q2k_n32k"])
-    # indices of every query row; attention of sampled rows
-    check_instance(inst, range(2048), [0, 1, 2, 100, 1023, 1024, 1500, 2046, 2047], heads=slice(0, 64, 4))
+    # indices of every query row; attention of every head of 32 rows, among
+    # them all eight rows of the first and of the last persistent workgroup
+    # (rows w, w + 256, ...: each row's set-up overlaps the previous row's end)
+    rows = sorted({w + 256 * i for w in (0, 255) for i in range(8)} | {1, 2, 100, 700, 1300, 1500, 1800, 1999, 2046,
+                                                                       2030, 77, 333, 901, 1777, 1100, 1650})
+    assert len(rows) == 32
+    check_instance(inst, range(2048), rows)
 
 
 def test_multi_decode_b4_q4_n1m():
