@@ -15,7 +15,7 @@ i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
 f32 = ctypes.c_float
 sz = ctypes.c_size_t
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EMODE, CSA2_EHIP = range(6)
 CSA2_F32, CSA2_BF16 = 0, 1
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
@@ -52,7 +52,7 @@ class ReplayArgs(ctypes.Structure):
 
 class GroupState(ctypes.Structure):
     _fields_ = [("idx", P), ("pool", P), ("has_idx", i32), ("has_pool", i32), ("ws_clean", i32), ("clean_rows", i32),
-                ("clean_ws", P)]
+                ("clean_ws", P), ("has_stage", i32), ("stage_n", i32)]
 
 
 # name -> (restype, argtypes); every symbol declared in include/csa2.h

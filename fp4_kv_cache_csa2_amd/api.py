@@ -205,7 +205,7 @@ class GroupState:
     def __init__(self, rows: int, K: int, P: int, device):
         self.idx = torch.empty(rows, K, dtype=torch.int32, device=device)
         self.pool = torch.empty(rows, max(P, 1), dtype=torch.int32, device=device)
-        self.c = _lib.GroupState(self.idx.data_ptr(), self.pool.data_ptr(), 0, 0, 0, 0, None)
+        self.c = _lib.GroupState(self.idx.data_ptr(), self.pool.data_ptr(), 0, 0, 0, 0, None, 0, 0)
 
 
 def csa2_layer_forward(mode: str, *, q, q_idx, swa_kv, q_pos, window, sm_scale, o, lse, cache: Fp4Cache,

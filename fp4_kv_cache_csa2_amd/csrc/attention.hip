@@ -42,6 +42,9 @@ struct AttnParams {
     RowMap kvmap;
     const int32_t* idx;        // [rows][K]
     int32_t K, Kp;             // Kp = K rounded up to 16 (0 if no sparse part)
+    // fp16 copy of the FP4 entries by logical position (k16[b n_stage + j][D]), or null
+    const uint16_t* k16;
+    int64_t n_stage;
     // window
     const uint16_t* swa;       // [B][T][D] ring: token t at row t mod T
     int32_t T;
@@ -816,6 +819,21 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 #undef CSA2_VMW
 }
 
+// the same for n up to 31 (vmcnt's two high bits sit at bits 14-15 of the
+// s_waitcnt immediate)
+__device__ __forceinline__ void wait_vm_at_most32(int n) {
+#define CSA2_VMW(N) \
+    case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+    switch (n) {
+        CSA2_VMW(0) CSA2_VMW(1) CSA2_VMW(2) CSA2_VMW(3) CSA2_VMW(4) CSA2_VMW(5) CSA2_VMW(6) CSA2_VMW(7)
+        CSA2_VMW(8) CSA2_VMW(9) CSA2_VMW(10) CSA2_VMW(11) CSA2_VMW(12) CSA2_VMW(13) CSA2_VMW(14) CSA2_VMW(15)
+        CSA2_VMW(16) CSA2_VMW(17) CSA2_VMW(18) CSA2_VMW(19) CSA2_VMW(20) CSA2_VMW(21) CSA2_VMW(22) CSA2_VMW(23)
+        CSA2_VMW(24) CSA2_VMW(25) CSA2_VMW(26) CSA2_VMW(27) CSA2_VMW(28) CSA2_VMW(29) CSA2_VMW(30)
+        default: __builtin_amdgcn_s_waitcnt(15 | (1 << 14) | (1 << 15) | (7 << 4) | (15 << 8)); break;
+    }
+#undef CSA2_VMW
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)ptr;
 }
@@ -907,6 +925,40 @@ __device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, ui
         "ds_write_b128 %0, %4 offset:%c7"
         :
         : "v"(ak), "v"(k0), "v"(k1), "v"(k2), "v"(k3), "i"(KROWB), "i"(2 * KROWB), "i"(3 * KROWB)
+        : "memory");
+}
+
+// Producer pw's four rows 4pw..4pw+3 of a tile that holds bf16 window rows
+// as copied: converted to fp16 in place (lane l: channels 8l..8l+7).  Reads
+// and writes in asm for the reason given at pc_store.
+__device__ __forceinline__ void pc_convert_rows(uint4* ktile, int pw, int lane) {
+    constexpr int D = PC_D;
+    constexpr int KROWB = (D / 8 + KROW_PAD) * 16;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t r0, r1, r2, r3;
+    const uint32_t a = lds_addr(ktile) + (uint32_t)(4 * pw * KROWB + lane * 16);
+    asm volatile(
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %4 offset:%c5\n"
+        "ds_read_b128 %2, %4 offset:%c6\n"
+        "ds_read_b128 %3, %4 offset:%c7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a), "i"(KROWB), "i"(2 * KROWB), "i"(3 * KROWB)
+        : "memory");
+    const uint4 u[4] = {make_uint4(r0.x, r0.y, r0.z, r0.w), make_uint4(r1.x, r1.y, r1.z, r1.w),
+                        make_uint4(r2.x, r2.y, r2.z, r2.w), make_uint4(r3.x, r3.y, r3.z, r3.w)};
+    uint32_t kh[4][4];
+    item_from_bf16(u, kh);
+    const u32x4_t k0{kh[0][0], kh[0][1], kh[0][2], kh[0][3]}, k1{kh[1][0], kh[1][1], kh[1][2], kh[1][3]};
+    const u32x4_t k2{kh[2][0], kh[2][1], kh[2][2], kh[2][3]}, k3{kh[3][0], kh[3][1], kh[3][2], kh[3][3]};
+    asm volatile(
+        "ds_write_b128 %0, %1\n"
+        "ds_write_b128 %0, %2 offset:%c5\n"
+        "ds_write_b128 %0, %3 offset:%c6\n"
+        "ds_write_b128 %0, %4 offset:%c7"
+        :
+        : "v"(a), "v"(k0), "v"(k1), "v"(k2), "v"(k3), "i"(KROWB), "i"(2 * KROWB), "i"(3 * KROWB)
         : "memory");
 }
 
@@ -1076,13 +1128,25 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void attn_pc_kernel(AttnParams p)
 // lands in the buffers the current row's last pair does not use.  Producer pw
 // sets up the rows of its own keys 4pw..4pw+3 of every chunk (it alone reads
 // them) and one byte per chunk of the validity bits (byte pw of kvb[c]).
+//
+// STAGED: the selected entries come from an fp16 copy of the cache by logical
+// position (p.k16, built once for a group of layers that share the cache and
+// its selections, so that neither the many query rows of a prefill chunk nor
+// the group's layers dequantise an entry again).  A producer then copies each
+// of its keys as one 1 KB row global -> LDS straight into its row of one of
+// eight tile buffers (no ring, no dequantisation), six chunks ahead of the
+// consumers and across row boundaries; a window chunk's bf16 rows are
+// converted to fp16 in place once they have landed.  The consumers are the
+// same.
+template <bool STAGED>
 __global__ __launch_bounds__(PC_NT, 1) void attn_pcr_kernel(AttnParams p, int64_t rows) {
     constexpr int D = PC_D, NW = PC_CONS;
     constexpr int NBLK = D / 32, NDT = D / 16, CPR = D / 8;
     constexpr int KPL = (MAX_CPS + 1) * 4 / 64;  // (chunk, key) pairs per producer lane
+    constexpr int NTILE = STAGED ? 8 : PC_TILES;  // tile buffers (a power of two)
     using S = Stage<D>;
-    __shared__ uint4 ktile[PC_TILES][CHUNK_KEYS * (CPR + KROW_PAD)];
-    __shared__ __attribute__((aligned(16))) uint8_t ring[PC_RING * S::SLOT];
+    __shared__ uint4 ktile[NTILE][CHUNK_KEYS * (CPR + KROW_PAD)];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[STAGED ? 16 : PC_RING * S::SLOT];
     __shared__ int64_t krow[2][MAX_CPS * CHUNK_KEYS + CHUNK_KEYS];
     __shared__ uint32_t kvb[2][MAX_CPS + 1];
 
@@ -1128,7 +1192,8 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pcr_kernel(AttnParams p, int64_
                 int zz;
                 asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
                 const int lz = lane + zz, cz = lz & 15, gz = lz >> 4;
-                attn_scores2<D, 6>(ktile[(gb + c) & 3], ktile[(gb + c + 1) & 3], cz, gz, qhi, sa, sb);
+                attn_scores2<D, 6>(ktile[(gb + c) & (NTILE - 1)], ktile[(gb + c + 1) & (NTILE - 1)], cz, gz, qhi, sa,
+                                   sb);
                 mfma_pipeline_hint<2 * NBLK, 1, 6>();
                 (void)gz;
             };
@@ -1138,7 +1203,7 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pcr_kernel(AttnParams p, int64_
                 const int lz = lane + zz, cz = lz & 15, gz = lz >> 4;
                 const uint32_t mk = bits16(kv[c]) | (bits16(kv[c + 1]) << 16);
                 const f16x8 pb = attn_weights2<NDT>(sa, sb, mk, gz, zscale, oacc, m_run, l_run);
-                attn_pv2<D>(ktile[(gb + c) & 3], ktile[(gb + c + 1) & 3], cz, gz, pb, oacc);
+                attn_pv2<D>(ktile[(gb + c) & (NTILE - 1)], ktile[(gb + c + 1) & (NTILE - 1)], cz, gz, pb, oacc);
             };
             for (int c = 0; c < npad - 2; c += 2) {
                 f32x4 sa, sb;
@@ -1174,6 +1239,118 @@ __global__ __launch_bounds__(PC_NT, 1) void attn_pcr_kernel(AttnParams p, int64_
             gb += npad;
             buf ^= 1;
             lds_barrier();
+        }
+    } else if constexpr (STAGED) {
+        // ---------------------------------------------------------- producers
+        const int pw = wv - NW;
+        constexpr int KROWB = (CPR + KROW_PAD) * 16;
+        const int64_t row0 = blockIdx.x;
+        const int64_t nloc = (rows - row0 + G - 1) / G;  // rows of this workgroup (>= 1)
+        const int64_t total = nloc * npad;               // its chunks, numbered across its rows
+        int32_t kent[KPL];
+        auto load_idx = [&](int64_t r) {
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const int t = lane + 64 * j;
+                const int kpos = (t >> 2) * CHUNK_KEYS + 4 * pw + (t & 3);
+                kent[j] = (kpos < p.K && (t >> 2) < npad) ? p.idx[r * p.K + kpos] : -1;
+            }
+        };
+        // rows of the staged copy / window ring for row r into krow[bf],
+        // validity bits into byte pw of kvb[bf]
+        auto set_rows = [&](int64_t r, int bf) {
+            const int b = (int)(r / p.Q);
+            const int qp = p.Wp ? p.q_pos[r] : -1;
+            const int wlo = max(0, qp - p.window + 1);
+            const int wrow0 = p.Wp ? wlo % p.T : 0;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const int t = lane + 64 * j;
+                const int c = t >> 2;
+                const int kpos = c * CHUNK_KEYS + 4 * pw + (t & 3);
+                int64_t rr = -1;
+                if (c >= nchunks) {
+                } else if (kpos < p.Kp) {
+                    if (kent[j] >= 0) rr = (int64_t)b * p.n_stage + kent[j];
+                } else {
+                    const int i_w = kpos - p.Kp;
+                    if (wlo + i_w <= qp)
+                        rr = (int64_t)b * p.T + (wrow0 + i_w >= p.T ? wrow0 + i_w - p.T : wrow0 + i_w);
+                }
+                const uint64_t valid = __ballot(rr >= 0);
+                if (c < npad) {
+                    krow[bf][kpos] = rr;
+                    if ((t & 3) == 0)
+                        reinterpret_cast<uint8_t*>(kvb[bf])[4 * c + pw] = (uint8_t)((valid >> (lane & 60)) & 0xFu);
+                }
+            }
+        };
+        auto sparse_chunk = [&](int c) { return c < n_sp || (c >= nchunks && p.Wp == 0); };
+        // chunks are issued in order: vis of them so far, the next being
+        // chunk is_c of this workgroup's row is_k, into tile vis % NTILE
+        int64_t vis = 0;
+        int is_k = 0, is_c = 0;
+        auto issue_next = [&]() {
+            const bool sp = sparse_chunk(is_c);
+            const int64_t* k4 = krow[is_k & 1] + is_c * CHUNK_KEYS + 4 * pw;
+            uint8_t* tb = reinterpret_cast<uint8_t*>(ktile[vis & (NTILE - 1)]) + 4 * pw * KROWB;
+            const uint8_t* base = sp ? reinterpret_cast<const uint8_t*>(p.k16) : reinterpret_cast<const uint8_t*>(p.swa);
+            int z;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+            const int lz = lane + z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // a key without a row copies row 0: finite values, weight exactly 0
+                const int64_t r = max(k4[i], (int64_t)0);
+                dma16_to_lds(base + r * (2 * D) + lz * 16, tb + i * KROWB);
+            }
+            ++vis;
+            if (++is_c == npad) {
+                is_c = 0;
+                ++is_k;
+            }
+        };
+        // issue up to chunk lim_v - 1, never past row lim_k (whose key rows
+        // are the newest set up)
+        auto issue_upto = [&](int64_t lim_v, int lim_k) {
+            while (vis < lim_v && vis < total && is_k <= lim_k) issue_next();
+        };
+        // chunk v (chunk c of its row) landed in its tile, converted if a window chunk
+        auto produce = [&](int64_t v, int c) {
+            wait_vm_at_most32(4 * (int)(vis - v - 1));
+            if (!sparse_chunk(c)) pc_convert_rows(ktile[v & (NTILE - 1)], pw, lane);
+        };
+        load_idx(row0);
+        set_rows(row0, 0);
+        if (nloc > 1) {
+            load_idx(row0 + G);
+            set_rows(row0 + G, 1);
+        }
+        if (nloc > 2) load_idx(row0 + 2 * G);
+        issue_upto(NTILE - 2, 1);
+        produce(0, 0);
+        produce(1, 1);
+        lds_barrier();
+        for (int k = 0;; ++k) {
+            // the row after next's key rows (the buffer of the row before, all
+            // of whose chunks have been issued) and the index list after that
+            if (k >= 1 && k + 1 < nloc) {
+                set_rows(row0 + (k + 1) * G, (k + 1) & 1);
+                if (k + 2 < nloc) load_idx(row0 + (k + 2) * G);
+            }
+            for (int c = 0; c < npad; c += 2) {
+                // the consumers take chunks v, v + 1; the tiles of v - 2 and
+                // v - 1 are free again
+                const int64_t v = (int64_t)k * npad + c;
+                issue_upto(v + NTILE, k + 1);
+                if (v + 2 < total) {
+                    const int cn = c + 2 < npad ? c + 2 : 0;
+                    produce(v + 2, cn);
+                    produce(v + 3, cn + 1);
+                }
+                lds_barrier();
+            }
+            if (k + 1 >= nloc) break;
         }
     } else {
         // ---------------------------------------------------------- producers
@@ -1337,6 +1514,29 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
 constexpr int MAX_SPLIT = 64;
 
 // compute units of the current device (cached per device)
+// fp16 copy of a cache's entries by logical position: one wave per entry,
+// lane l decodes channels 8l..8l+7 (four code bytes and their scale) with the
+// producers' arithmetic (bit for bit the tile they would write); an entry
+// without a page, or past the sequence's addressable capacity, is zero.
+__global__ __launch_bounds__(256) void stage_cache_kernel(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales, RowMap map,
+                                                          int64_t nrows, int64_t n_stage, uint16_t* __restrict__ k16) {
+    constexpr int D = PC_D;
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (e >= nrows) return;
+    const int b = (int)(e / n_stage);
+    const int64_t j = e - (int64_t)b * n_stage;
+    const int64_t r = j < map.capacity ? phys_row(map, b, j) : -1;
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (r >= 0) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (D / 2) + lane * 4);
+        const uint32_t sc = scales[r * (D / 16) + (lane >> 1)];
+        fp4x8_to_f16(w, e4m3_f16x2_over256(sc), o);
+    }
+    reinterpret_cast<uint4*>(k16 + e * D)[lane] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 int device_cus() {
     static int cached[64] = {};
     int dev = 0;
@@ -1377,7 +1577,8 @@ size_t attn_ws_bytes(int64_t rows, int H, int D) {
 csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                         const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,
                         const int32_t* q_pos, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
-                        void* ws, size_t ws_bytes, hipStream_t stream, const char* what) {
+                        void* ws, size_t ws_bytes, hipStream_t stream, const char* what, const uint16_t* k16,
+                        int64_t n_stage) {
     CSA2_ARG(B >= 0 && Q >= 0, "%s: B=%d Q=%d must be >= 0", what, B, Q);
     CSA2_ARG((int64_t)B * Q <= 65535, "%s: B*Q=%lld rows exceeds 65535", what, (long long)B * Q);
     CSA2_ARG(qt == CSA2_F32 || qt == CSA2_BF16, "%s: bad q dtype %d", what, (int)qt);
@@ -1451,9 +1652,17 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     if (wide && p.nsplit > 1 && !hsplit) attn_pc_kernel<true, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
     // many rows: one persistent workgroup per CU walks over them
     const int64_t ncu = device_cus();
-    const bool persist = wide && p.nsplit == 1 && rows > ncu && nchunks >= 2;
-    if (persist) attn_pcr_kernel<<<dim3((unsigned)ncu), dim3(PC_NT), 0, stream>>>(p, rows);
-    if (wide && p.nsplit == 1 && !persist) attn_pc_kernel<false, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
+    // an fp16 copy of the entries (a prefill group): the staged persistent kernel
+    const bool staged = wide && p.nsplit == 1 && nchunks >= 2 && k16 != nullptr && K > 0;
+    if (staged) {
+        p.k16 = k16;
+        p.n_stage = n_stage;
+        attn_pcr_kernel<true><<<dim3((unsigned)(rows < ncu ? rows : ncu)), dim3(PC_NT), 0, stream>>>(p, rows);
+    }
+    const bool persist = !staged && wide && p.nsplit == 1 && rows > ncu && nchunks >= 2;
+    if (persist) attn_pcr_kernel<false><<<dim3((unsigned)ncu), dim3(PC_NT), 0, stream>>>(p, rows);
+    if (wide && p.nsplit == 1 && !persist && !staged)
+        attn_pc_kernel<false, PC_CONS><<<grid, dim3(PC_NT), 0, stream>>>(p);
 #define CSA2_ATTN_NW(DD, F, NWV) \
     if (!wide && nw == NWV) attn_kernel<DD, F, NWV><<<grid, block, 0, stream>>>(p);
 #define CSA2_ATTN(DD)                                                                                   \
@@ -1490,6 +1699,34 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
 }
 
 size_t attn_workspace_bytes(int64_t rows, int H, int D) { return attn_ws_bytes(rows, H, D); }
+
+// Staging pays when a sequence's entries are selected several times per layer
+// on average (many query rows of one sequence: a prefill chunk) and the
+// persistent kernel applies (D = 512, H = 64, at least a round of rows).
+bool attn_stage_applicable(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t K) {
+    (void)B;
+    return D == PC_D && H == 16 * PC_CONS && K > 0 && Q >= 256;
+}
+
+size_t attn_stage_bytes(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t n_max, int32_t K) {
+    if (!attn_stage_applicable(B, Q, H, D, K) || n_max <= 0 || (int64_t)Q * K < 2 * (int64_t)n_max) return 0;
+    return (size_t)B * (size_t)n_max * (size_t)D * 2;
+}
+
+csa2_status attn_stage_cache(const csa2_fp4_kv* kv, int32_t B, int64_t n_stage, uint16_t* k16, hipStream_t stream) {
+    const char* what = "layer_forward (staging)";
+    CSA2_ARG(kv && kv->codes && kv->scales && k16, "%s: null cache view or staging buffer", what);
+    CSA2_REQUIRE(kv->D == PC_D, CSA2_EUNSUPPORTED, "%s: D=%d (staging supports 512)", what, kv->D);
+    CSA2_ARG(B > 0 && n_stage > 0, "%s: B=%d n=%lld", what, B, (long long)n_stage);
+    CSA2_ARG(aligned(kv->codes, 4) && aligned(k16, 16), "%s: codes must be 4-byte, the copy 16-byte aligned", what);
+    RowMap m{};
+    csa2_status st = make_rowmap(kv->page_table, kv->page_size, kv->max_pages, kv->seq_stride, 1, &m, what);
+    if (st != CSA2_OK) return st;
+    const int64_t nrows = (int64_t)B * n_stage;
+    stage_cache_kernel<<<dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, stream>>>(kv->codes, kv->scales, m, nrows,
+                                                                                   n_stage, k16);
+    return launch_status(what);
+}
 
 }  // namespace csa2
 

@@ -20,15 +20,14 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // knows whether they are still cleared even when n_max, K or P change between
 // calls.  Everything after them is scratch without initial contents.
 struct LayerWs {
-    size_t counters, scores, block_max, pool_scores, lists, attn, screen, total;
-    size_t attn_bytes, screen_bytes;
+    size_t counters, scores, block_max, pool_scores, lists, attn, screen, stage, total;
+    size_t attn_bytes, screen_bytes, stage_bytes;
 };
 
 // the two selections' counters
 inline size_t counter_region(int64_t rows) { return align256(2 * topk_counter_bytes(rows)); }
 
 LayerWs layer_ws(int32_t B, int32_t Q, int H, int D, int64_t n_max, int K, int P) {
-    (void)K;
     const int64_t rows = (int64_t)B * Q;
     LayerWs w{};
     const int64_t nblocks = (n_max + 7) / 8;
@@ -51,6 +50,11 @@ LayerWs layer_ws(int32_t B, int32_t Q, int H, int D, int64_t n_max, int K, int P
     w.screen = off;
     w.screen_bytes = screen_ws_bytes(B, Q, (int32_t)n_max);
     off = align256(off + w.screen_bytes);
+    // many query rows per sequence: the fp16 copy of the shared cache that the
+    // group's layers attend from
+    w.stage = off;
+    w.stage_bytes = attn_stage_bytes(B, Q, H, D, (int32_t)n_max, K);
+    off = align256(off + w.stage_bytes);
     w.total = off;
     return w;
 }
@@ -205,11 +209,26 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
             s = launch_status("layer_forward");
         }
     }
+    // A prefill group attends from an fp16 copy of the shared cache: its Full
+    // layer builds the copy, the Reindex and Reuse layers after it (same
+    // workspace, rows and n_max, the cache unchanged) read it again.
+    uint16_t* k16 = w.stage_bytes ? reinterpret_cast<uint16_t*>(ws + w.stage) : nullptr;
+    bool staged = false;
+    if (s == CSA2_OK && k16 && a->qt == CSA2_BF16) {
+        if (mode == CSA2_FULL) {
+            s = attn_stage_cache(a->kv, a->B, a->n_max, k16, stream);
+            staged = s == CSA2_OK;
+        } else {
+            staged = st->has_stage && st->stage_n == a->n_max && st->clean_ws == a->ws && st->clean_rows == rows32;
+        }
+    }
     if (s == CSA2_OK)
         s = attn_launch(a->q, a->qt, a->B, a->Q, a->H, a->kv->D, a->kv, st->idx, a->K, a->swa_kv, a->T, a->q_pos,
-                        a->window, a->sm_scale, 0, a->o, a->lse, aw, w.attn_bytes, stream, "layer_forward");
+                        a->window, a->sm_scale, 0, a->o, a->lse, aw, w.attn_bytes, stream, "layer_forward",
+                        staged ? k16 : nullptr, a->n_max);
     if (s != CSA2_OK) {
         st->ws_clean = 0;
+        st->has_stage = 0;
         return s;
     }
     st->ws_clean = 1;
@@ -218,6 +237,8 @@ extern "C" csa2_status csa2_layer_forward(csa2_mode mode, const csa2_layer_args*
     if (mode == CSA2_FULL) {
         st->has_idx = 1;
         if (a->build_pool) st->has_pool = 1;
+        st->has_stage = staged ? 1 : 0;
+        st->stage_n = a->n_max;
     } else if (mode == CSA2_REINDEX) {
         st->has_idx = 1;
     }

@@ -108,7 +108,14 @@ csa2_status screen_select(const uint16_t* q_idx, int32_t B, int32_t Q, int32_t H
 csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int32_t H, int32_t D,
                         const csa2_fp4_kv* kv, const int32_t* idx, int32_t K, const uint16_t* swa, int32_t T,
                         const int32_t* q_pos, int32_t window, float sm_scale, int32_t merge, float* o, float* lse,
-                        void* ws, size_t ws_bytes, hipStream_t stream, const char* what);
+                        void* ws, size_t ws_bytes, hipStream_t stream, const char* what,
+                        const uint16_t* k16 = nullptr, int64_t n_stage = 0);
 size_t attn_workspace_bytes(int64_t rows, int H, int D);
+// fp16 copy of a cache's entries by logical position, k16[b n_stage + j][D]
+// for j < n_stage (zeros where the page table maps no page); the prefill
+// attention of a group reads it instead of dequantising every selected entry
+bool attn_stage_applicable(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t K);
+size_t attn_stage_bytes(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t n_max, int32_t K);
+csa2_status attn_stage_cache(const csa2_fp4_kv* kv, int32_t B, int64_t n_stage, uint16_t* k16, hipStream_t stream);
 
 }  // namespace csa2

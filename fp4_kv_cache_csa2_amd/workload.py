@@ -155,6 +155,7 @@ class StackRunner:
         inst, w = self.inst, self.inst.w
         self.state.c.has_idx = 0
         self.state.c.has_pool = 0
+        self.state.c.has_stage = 0
         for l, mode in enumerate(w.pattern):
             L = inst.layers[l]
             api.csa2_layer_forward(mode, q=L["q"], q_idx=L["q_idx"], swa_kv=L["swa"], q_pos=inst.q_pos,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum {
     CSA2_OK = 0,
@@ -310,6 +310,18 @@ typedef struct csa2_group_state {
     int32_t ws_clean;
     int32_t clean_rows;
     const void* clean_ws;
+    /* Staged copy (maintained by csa2_layer_forward; initialise to 0): with
+     * many query rows per sequence (Q >= 256, D = 512, H = 64, bf16 queries,
+     * Q*K >= 2*n_max) a Full layer writes an fp16 copy of the FP4 entries by
+     * logical position into the workspace (B*n_max*D*2 bytes, counted by
+     * csa2_layer_workspace_size) and attends from it; later Reindex and Reuse
+     * layers of the group read the same copy while has_stage is set and the
+     * workspace, B*Q and n_max are the ones recorded.  Its values are the
+     * cache's decode, so the outputs are bit for bit those of the FP4 path.
+     * Clear has_stage, like has_idx, whenever the cache changes outside a Full
+     * layer of the group. */
+    int32_t has_stage;
+    int32_t stage_n;
 } csa2_group_state;
 
 size_t csa2_layer_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t D, int32_t n_max, int32_t K, int32_t P);

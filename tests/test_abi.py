@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa2_abi_version() == 2 == _lib.ABI_VERSION
+    assert lib.csa2_abi_version() == 3 == _lib.ABI_VERSION
     assert lib.csa2_status_string(_lib.CSA2_EMODE) == b"CSA2_EMODE"
 
 
@@ -116,7 +116,7 @@ def _layer_args(ws_bytes=1 << 40):
 
 def test_layer_mode_errors(lib):
     a, kv, kk = _layer_args()
-    st = _lib.GroupState(FAKE.value, FAKE.value, 0, 0, 0, 0, None)
+    st = _lib.GroupState(FAKE.value, FAKE.value, 0, 0, 0, 0, None, 0, 0)
     assert lib.csa2_layer_forward(_lib.CSA2_REUSE, ctypes.byref(a), ctypes.byref(st), None) == _lib.CSA2_EMODE
     assert "Reuse" in _err(lib)
     assert lib.csa2_layer_forward(_lib.CSA2_REINDEX, ctypes.byref(a), ctypes.byref(st), None) == _lib.CSA2_EMODE
