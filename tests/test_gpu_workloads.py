@@ -266,6 +266,62 @@ def test_encoder_prefill_q2k_n32k():
     check_instance(inst, range(2048), rows)
 
 
+def _fp4_path_rerun(inst, run):
+    """Every Reuse layer again with the staged copy switched off (the FP4 path:
+    each selected entry dequantised by the attention itself): outputs must be
+    bit for bit the staged ones."""
+    w = inst.w
+    staged_o = [t.clone() for t in run.o]
+    staged_l = [t.clone() for t in run.lse]
+    n = 0
+    for l, mode in enumerate(w.pattern):
+        if mode != "U":
+            continue
+        L = inst.layers[l]
+        run.state.c.has_stage = 0
+        case(f"{w.name}: layer {l} without the staged copy")
+        api.csa2_layer_forward("U", q=L["q"], q_idx=None, swa_kv=L["swa"], q_pos=inst.q_pos, window=w.window,
+                               sm_scale=inst.sm_scale, o=run.o[l], lse=run.lse[l], cache=inst.cache,
+                               kview=inst.kview, n_vis=inst.n_vis, n_max=inst.n_max, K=w.K, P=0, build_pool=False,
+                               ws=run.ws, state=run.state)
+        torch.cuda.synchronize()
+        assert torch.equal(staged_o[l].view(torch.int32), run.o[l].view(torch.int32)), f"layer {l} o"
+        assert torch.equal(staged_l[l].view(torch.int32), run.lse[l].view(torch.int32)), f"layer {l} lse"
+        n += 1
+    assert n >= 1
+
+
+@pytest.mark.parametrize("B,Q,N,K,window,paged", [
+    (2, 300, 8192, 200, 128, True),   # paged cache; 13 + 8 = 21 chunks (a padding chunk); 2 or 3 rows per workgroup
+    (1, 256, 4096, 512, 0, False),    # no window; one row per workgroup
+])
+def test_staged_prefill_attention(B, Q, N, K, window, paged):
+    """Many query rows per sequence: the Full layer stages an fp16 copy of the
+    shared cache and the group's layers attend from it.  Indices and sampled
+    attention rows against the oracle, then the Reuse layers rerun on the FP4
+    path must reproduce the staged outputs bit for bit."""
+    import dataclasses
+    w = dataclasses.replace(inputs.WORKLOADS["encoder_prefill_q2k_n32k"], name=f"staged_b{B}_q{Q}", B=B, Q=Q, N=N,
+                            K=K, window=window, pattern="FUU", ragged=paged)
+    inst = workload.make_instance(w, lengths=np.full(B, N, np.int32))
+    rows = B * Q
+    run = check_instance(inst, [0, rows // 2, rows - 1], [0, 1, 255, rows - 1])
+    assert run.state.c.has_stage == 1 and run.state.c.stage_n == N
+    _fp4_path_rerun(inst, run)
+
+
+def test_staged_prefill_bit_identical_at_full_size():
+    """The 2048-row prefill chunk (eight rows per persistent workgroup): staged
+    and FP4-path outputs of every Reuse layer bit for bit equal."""
+    inst = workload.make_instance(inputs.WORKLOADS["encoder_prefill_q2k_n32k"])
+    run = workload.StackRunner(inst)
+    case("encoder_prefill_q2k_n32k: staged step")
+    run.step()
+    torch.cuda.synchronize()
+    assert run.state.c.has_stage == 1
+    _fp4_path_rerun(inst, run)
+
+
 def test_multi_decode_b4_q4_n1m():
     # 4 causal query tokens per sequence: the scan shares K blocks among a
     # sequence's rows, the pool and Top-K histograms come from their own pass
