@@ -285,7 +285,12 @@ def _fp4_path_rerun(inst, run):
                                kview=inst.kview, n_vis=inst.n_vis, n_max=inst.n_max, K=w.K, P=0, build_pool=False,
                                ws=run.ws, state=run.state)
         torch.cuda.synchronize()
-        assert torch.equal(staged_o[l].view(torch.int32), run.o[l].view(torch.int32)), f"layer {l} o"
+        bad = staged_o[l].view(torch.int32) != run.o[l].view(torch.int32)
+        if bool(bad.any()):
+            rows_bad = bad.reshape(bad.shape[0] * bad.shape[1], -1).any(dim=1).nonzero().flatten().tolist()
+            d = (staged_o[l] - run.o[l]).abs().max().item()
+            raise AssertionError(f"layer {l} o: {int(bad.sum())} elements differ in {len(rows_bad)} rows "
+                                 f"(first {rows_bad[:12]}), max |diff| {d:.3e}")
         assert torch.equal(staged_l[l].view(torch.int32), run.lse[l].view(torch.int32)), f"layer {l} lse"
         n += 1
     assert n >= 1
