@@ -838,10 +838,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)ptr;
 }
 
-// Producer pw's copies of one chunk (kr: the chunk's 16 key rows) into a ring
-// slot laid out as in Stage: codes [16][D/2] from 0, scales in one 256-byte
-// group per producer at SCALE_OFF (key 4pw+i at +256 pw + 32 i; the group's
-// upper half takes duplicate copies), window rows [16][2D].
+// Producer pw's copies of one chunk (kr: the chunk's 16 key rows) into its own
+// quarter of a ring slot, bytes 4096 pw .. 4096 pw + 4095, whatever the kind:
+// FP4 codes of keys 4pw..4pw+3 ([4][D/2]) from its start and their scales in
+// the 256 bytes after them (key 4pw+i at +32 i; the upper half takes
+// duplicate copies), or the four window rows ([4][2D]).  The producers do not
+// wait for one another's ring reads, so no producer may copy into bytes that
+// another one reads: a slot that changes kind (FP4 entries, then window rows,
+// or back at a row's start) would otherwise have one producer's new copies
+// land on another's unread ones.
+constexpr int PC_QUARTER = 4096;
+static_assert(4 * 2 * PC_D == PC_QUARTER && 4 * (PC_D / 2) + 256 <= PC_QUARTER, "a producer's quarter holds 4 window rows or 4 FP4 rows and their scales");
 __device__ __forceinline__ void pc_issue(const AttnParams& p, bool sparse, const int64_t* kr, uint8_t* slot, int pw,
                                          int lane) {
     constexpr int D = PC_D;
@@ -854,13 +861,14 @@ __device__ __forceinline__ void pc_issue(const AttnParams& p, bool sparse, const
     if (sparse) {
         const int64_t rc = max(k4[lz >> 4], (int64_t)0);
         const int64_t rs = max(k4[(lz >> 3) & 3], (int64_t)0);
-        dma16_to_lds(p.codes + rc * (D / 2) + (lz & 15) * 16, slot + pw * 1024);
-        dma4_to_lds(p.scales + rs * (D / 16) + (lz & 7) * 4, slot + Stage<D>::SCALE_OFF + pw * 256);
+        dma16_to_lds(p.codes + rc * (D / 2) + (lz & 15) * 16, slot + pw * PC_QUARTER);
+        dma4_to_lds(p.scales + rs * (D / 16) + (lz & 7) * 4, slot + pw * PC_QUARTER + 4 * (D / 2));
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t r = max(k4[i], (int64_t)0);
-            dma16_to_lds(reinterpret_cast<const uint8_t*>(p.swa) + r * (2 * D) + lz * 16, slot + (4 * pw + i) * 1024);
+            dma16_to_lds(reinterpret_cast<const uint8_t*>(p.swa) + r * (2 * D) + lz * 16,
+                         slot + pw * PC_QUARTER + i * (2 * D));
         }
     }
 }
@@ -875,8 +883,8 @@ __device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, ui
     uint32_t kh[4][4];
     if (SPARSE) {
         uint32_t cw[4], sb[4];
-        const uint32_t ac = lds_addr(slot + 4 * pw * (D / 2) + co * 4);
-        const uint32_t as = lds_addr(slot + Stage<D>::SCALE_OFF + pw * 256 + (co >> 1));
+        const uint32_t ac = lds_addr(slot + pw * PC_QUARTER + co * 4);
+        const uint32_t as = lds_addr(slot + pw * PC_QUARTER + 4 * (D / 2) + (co >> 1));
         asm volatile(
             "ds_read_b32 %0, %8\n"
             "ds_read_b32 %1, %8 offset:256\n"
@@ -895,7 +903,7 @@ __device__ __forceinline__ void pc_store(const uint8_t* slot, int pw, int co, ui
     } else {
         typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
         u32x4_t r0, r1, r2, r3;
-        const uint32_t a = lds_addr(slot + 4 * pw * (2 * D) + co * 16);
+        const uint32_t a = lds_addr(slot + pw * PC_QUARTER + co * 16);
         asm volatile(
             "ds_read_b128 %0, %4\n"
             "ds_read_b128 %1, %4 offset:1024\n"

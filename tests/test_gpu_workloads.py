@@ -315,6 +315,26 @@ def test_staged_prefill_attention(B, Q, N, K, window, paged):
     _fp4_path_rerun(inst, run)
 
 
+def test_fp4_ring_slots_change_kind():
+    """Persistent FP4 attention whose ring slots change kind inside a row (13
+    FP4 chunks, then window chunks, so a chunk pair holds one of each) and back
+    at each row's start: every producer copies into its own quarter of a slot,
+    so none overwrites another's unread copies.  Four instances, each checked
+    bit for bit against the staged path (a shared slot layout made a row or two
+    of most instances wrong)."""
+    import dataclasses
+    w = dataclasses.replace(inputs.WORKLOADS["encoder_prefill_q2k_n32k"], name="ring_kinds", B=2, Q=300, N=8192,
+                            K=208, window=128, pattern="FUU", ragged=True)
+    for seed in range(4):
+        inst = workload.make_instance(w, seed=seed, lengths=np.full(2, 8192, np.int32))
+        run = workload.StackRunner(inst)
+        case(f"ring_kinds seed {seed}")
+        run.step()
+        torch.cuda.synchronize()
+        assert run.state.c.has_stage == 1
+        _fp4_path_rerun(inst, run)
+
+
 def test_staged_prefill_bit_identical_at_full_size():
     """The 2048-row prefill chunk (eight rows per persistent workgroup): staged
     and FP4-path outputs of every Reuse layer bit for bit equal."""
