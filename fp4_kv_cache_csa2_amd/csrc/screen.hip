@@ -9,11 +9,19 @@
 // the many-row scan far below the HBM roof.  Instead:
 //  1. approximate scores S~ = bf16(qbar) . k on the matrix cores (bf16 x bf16
 //     products are exact in fp32, accumulated in fp32), with a bound
-//     |S - S~| <= eps = 2^-8 ||qbar||_2 ||k||_2 for every entry (rounding qbar
-//     to bf16 moves it by at most 2^-9 |qbar_c| per channel; the two fp32
-//     accumulations of 128 terms add at most 2^-16 of sum |qbar_c k_c|; by
-//     Cauchy-Schwarz sum |qbar_c k_c| <= ||qbar|| ||k||; the factor keeps a
-//     margin of almost 2 over the sum of these terms);
+//     |S - S~| <= eps for every entry, S the exact score's fp32 chain.  With
+//     T = sum_c |qbar_c k_c| <= ||qbar|| ||k|| (Cauchy-Schwarz) and u = 2^-8
+//     the unit roundoff of bf16: rounding qbar to bf16 moves channel c by at
+//     most u/(1+u) |qbar_c| < (2^-8 - 2^-16 + 2^-24) |qbar_c|, so the real
+//     products move by less than (2^-8 - 2^-16 + 2^-24) T; the matrix cores'
+//     fp32 sum of 128 products adds at most 2^-16 T (two units of 2^-24 per
+//     addition, so that a truncating adder is covered), the exact chain of
+//     128 FMAs at most 2^-17 T.  eps = (2^-8 + 2^-15) ||qbar|| ||k|| covers
+//     the total, below 2^-8 + 2^-17 + 2^-24 of T, with the roundings of eps
+//     and of S~ +- eps and the norms (rounded up) inside the margin.  Subnormal operands
+//     or products, were they flushed, move a score by at most
+//     2^-122 (||qbar|| + ||k||) + 2^-118: eps carries twice that as an
+//     absolute term;
 //  2. per row, the lower bounds S~ - eps over aligned 16-entry blocks: the
 //     K-th largest block bound tau is <= the K-th largest exact score, since
 //     each of those K blocks holds an entry whose exact score is >= its bound;
@@ -36,7 +44,9 @@ constexpr int SC_KROW = SC_DI / 8 + 2;    // 16-byte chunks per staged K row (2 
 constexpr int SC_CAP = 4096;              // candidates kept per row
 constexpr int SC_WCAP = 1024;             // candidates a one-wave selection holds (16 per lane)
 constexpr int SC_MAXN = TOPK_ONEWG_N;     // longest row the screen serves (its position bitmap: 4 KB)
-constexpr float SC_EPS = 0x1p-8f;
+constexpr float SC_EPS = 0x1.02p-8f;      // relative part of the bound (times ||qbar|| ||k||): 2^-8 + 2^-15
+constexpr float SC_EABS_N = 0x1p-121f;    // absolute part: times (||qbar|| + ||k||) ...
+constexpr float SC_EABS = 0x1p-117f;      // ... plus this
 constexpr float SC_UP = 1.0f + 0x1p-20f;  // rounds a computed norm up past its fp32 rounding
 
 struct ScreenParams {
@@ -81,6 +91,18 @@ __device__ __forceinline__ float row4_max(float x) {
 // key32 back to the float it encodes (nonzero keys)
 __device__ __forceinline__ float key_float(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// the bound eps of one entry from the row's constants (qe, qa) and the
+// entry's norm: eps = qe kn + 2^-121 kn + qa, with qe = (2^-8 + 2^-15) ||qbar||
+// and qa = 2^-121 ||qbar|| + 2^-117 (both screening passes form L and U
+// through these, so that they agree bit for bit)
+__device__ __forceinline__ void row_eps(float qn, float& qe, float& qa) {
+    qe = SC_EPS * qn;
+    qa = fmaf(SC_EABS_N, qn, SC_EABS);
+}
+__device__ __forceinline__ float entry_eps(float qe, float qa, float kn) {
+    return fmaf(qe, kn, fmaf(SC_EABS_N, kn, qa));
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -181,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p, const u
     }
     // B operands and the row constants load while the visible range is agreed on
     bf16x8 qb[2][4];
-    float qe[2], taur[2];
+    float qe[2], qa[2], taur[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const uint4* qp = reinterpret_cast<const uint4*>(p.qhi + rr[rt] * SC_DI);
@@ -191,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p, const u
             if (!rok[rt]) v = make_uint4(0u, 0u, 0u, 0u);
             qb[rt][blk] = __builtin_bit_cast(bf16x8, v);
         }
-        qe[rt] = SC_EPS * p.qn[rr[rt]];
+        row_eps(p.qn[rr[rt]], qe[rt], qa[rt]);
         taur[rt] = PASS == 2 ? p.tau[rr[rt]] : 0.0f;
     }
     if (t == 0) nvmax_s = 0u;
@@ -305,12 +327,13 @@ __global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p, const u
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const bool valid = 16 * j + i < lim4[rt];
+                        const float eps = entry_eps(qe[rt], qa[rt], knv[i]);
                         if (PASS == 1) {
                             // (a NaN bound is dropped by the maximum)
-                            m = fmaxf(m, valid ? fmaf(-qe[rt], knv[i], acc[rt][i]) : -INFINITY);
+                            m = fmaxf(m, valid ? acc[rt][i] - eps : -INFINITY);
                         } else {
                             // (NaN: a candidate)
-                            const bool c = valid && !(fmaf(qe[rt], knv[i], acc[rt][i]) < taur[rt]);
+                            const bool c = valid && !(acc[rt][i] + eps < taur[rt]);
                             cm[rt][s] |= (uint32_t)c << (4 * j + i);
                         }
                     }
