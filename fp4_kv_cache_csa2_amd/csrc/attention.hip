@@ -1632,6 +1632,16 @@ csa2_status attn_launch(const void* q, csa2_dtype qt, int32_t B, int32_t Q, int3
     p.lse = lse;
     const int nchunks = (p.Kp + p.Wp) / CHUNK_KEYS;
     p.nsplit = choose_nsplit(rows, nchunks);
+    {
+        // a split decode launch of the producer/consumer kernel (D = 512,
+        // H = 64, bf16 queries) also splits the heads over four workgroups
+        // when all of them fit in one round over the CUs: with a few more
+        // rows than that allows, fewer key splits (at least two) make it fit
+        const int64_t hw = H / 16;
+        if (D == 512 && hw == 4 && qt == CSA2_BF16 && p.nsplit > 1 && rows * p.nsplit * hw > 256 &&
+            256 / (rows * hw) >= 2)
+            p.nsplit = (int)(256 / (rows * hw));
+    }
     p.cps = nchunks > 0 ? (nchunks + p.nsplit - 1) / p.nsplit : 0;
     CSA2_REQUIRE(p.cps <= MAX_CPS, CSA2_EUNSUPPORTED, "%s: %d keys per query need more than %d splits", what,
                  nchunks * CHUNK_KEYS, MAX_SPLIT);
