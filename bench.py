@@ -211,8 +211,8 @@ def bench_replay(args):
 
 
 def host_cpu():
-    """(threads to use, CPUs visible, CPU model name).  The pool is capped at the
-    16 CPUs a one-GPU machine is given, whatever the visible count."""
+    """(threads to use, CPUs visible, CPU model name).  The pool is capped at 16
+    threads (the host share of one GPU), whatever the visible count."""
     visible = len(os.sched_getaffinity(0))
     model = "unknown"
     try:
