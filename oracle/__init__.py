@@ -26,10 +26,14 @@ Functions and the passages they follow (full citations in ``csa2_oracle.c``):
                                projection itself is a reading: kv_p = bf16(h_p W^T),
                                one rounding.
 
-Parity-unpinned readings (pinned only by the workload text, never by the
-pages): the score has no ReLU / head weights / scale; the pool ranks 8-entry
-blocks by their max score; attention uses scale 1/sqrt(D), no RoPE, no sink and
-no de-duplication of tokens present in both key sets.
+Parity-unpinned readings (pinned only by the workload text or by the readings
+themselves, never by the pages): the score has no ReLU / head weights / scale;
+its fp32 evaluation order (head sum first, then one FMA chain over the channels:
+equal to the per-head sums in exact arithmetic, but its rounding decides
+near-ties of the Top-K); the pool ranks 8-entry blocks by their max score;
+attention uses scale 1/sqrt(D), no RoPE, no sink and no de-duplication of tokens
+present in both key sets; what the window projection of the replay contains
+beyond one matrix product (norms, rotary parts).
 """
 from __future__ import annotations
 

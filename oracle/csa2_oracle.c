@@ -37,6 +37,13 @@
  *
  * Everything here is fp64 unless the step itself is defined in fp32 (the
  * indexer score, whose fp32 rounding decides the integer Top-K result).
+ *
+ * Parity unpinned (fixed by these readings, not by the pages): the score's
+ * lack of ReLU, head weights or scale, and its fp32 evaluation order (equal to
+ * the per-head sums in exact arithmetic; its rounding decides near-ties); the
+ * block-max pool rule; the attention scale 1/sqrt(D) without RoPE, sink or
+ * de-duplication; the replayed window projection beyond one matrix product.
+ * The tests pin everything the mathematics and the format specifications fix.
  */
 #include <math.h>
 #include <stdint.h>
