@@ -340,7 +340,11 @@ def _attn_inputs(B, Q, H, D, n, K, T, qdtype, tag):
     # one-chunk window exercise its padding chunk), fp32 queries the
     # one-workgroup kernel
     (520, 1, 64, 512, 512, torch.bfloat16, 128), (520, 1, 64, 512, 200, torch.bfloat16, 8),
-    (300, 2, 64, 512, 200, torch.float32, 128)])
+    (300, 2, 64, 512, 200, torch.float32, 128),
+    # a few more rows than four head groups x ten key splits fit in one round
+    # over the CUs: fewer key splits keep the head split (12 rows: 5 splits of
+    # 8 chunks; 7 rows: 9 splits of 5 chunks, each padded to an even count)
+    (12, 1, 64, 512, 512, torch.bfloat16, 128), (7, 1, 64, 512, 512, torch.bfloat16, 128)])
 def test_sparse_then_swa_merge(B, Q, H, D, K, qdtype, window):
     n, T = (3000 if B < 100 else 520), 200
     cache, q, idx, swa, qpos, rc, rs = _attn_inputs(B, Q, H, D, n, K, T, qdtype, f"at{B}{H}{D}{K}")
@@ -570,6 +574,7 @@ def _all_codes_cache(n, D):
     (128, 16, torch.float32, 2), (128, 16, torch.bfloat16, 300), (256, 32, torch.bfloat16, 3),
     (256, 64, torch.float32, 400), (512, 64, torch.float32, 4),
     (512, 64, torch.bfloat16, 4),     # producer/consumer kernel, keys split over workgroups
+    (512, 64, torch.bfloat16, 12),    # the same with fewer key splits (five) so that heads split too
     (512, 64, torch.bfloat16, 300)])  # producer/consumer kernel, whole list per workgroup
 def test_attention_fp4_decode_bit_exact(D, H, qdtype, rows):
     """A query row that selects exactly one entry (window empty) has softmax
