@@ -134,6 +134,7 @@ def alg_bytes(w, n_entries_total):
 
 REPLAY = dict(name="swa_replay_b4_l20", L=20, B=4, n=128, d_model=4096, D=512, T=128, t_end=(1 << 20) - 1)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16
 
 
 def bench_replay(args):
@@ -372,16 +373,16 @@ def main():
                                       a["tok"])
             run.step()
 
-        return inst, step
+        return inst, step, run
 
-    inst, step0 = build()
+    inst, step0, run0 = build()
     stream = torch.cuda.current_stream()
     ab = alg_bytes(w, int(inst.lengths.sum()))
     # a step whose inputs would stay in the 256 MB last-level cache between
     # steps is measured over rotating copies of them (same data, other
     # addresses), so that the steps timed together touch min_footprint bytes
     n_copies = max(1, min(8, math.ceil(args.min_footprint_mib * 2**20 / ab["total"])))
-    sets = [(inst, step0)] + [build() for _ in range(n_copies - 1)]
+    sets = [(inst, step0, run0)] + [build() for _ in range(n_copies - 1)]
 
     for i in range(max(args.warmup, n_copies)):
         sets[i % n_copies][1]()
@@ -399,7 +400,7 @@ def main():
     # each copy's whole step captured once as a HIP graph, then the graphs
     # replayed in turn: the timed region
     graphs = []
-    for _, step in sets:
+    for _, step, _ in sets:
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -454,7 +455,8 @@ def main():
     achieved = ab["full"] / (scan_avg_ms * 1e-3) / 1e9  # GB/s
     out = {
         "metric": ("CSA2 decode query-tokens/s at 1M ctx; achieved HBM GB/s vs peak" if w.name == "hier_decode_b4_n1m"
-                   else f"CSA2 query-tokens/s ({w.name}); achieved HBM GB/s vs peak"),
+                   else f"CSA2 query-tokens/s ({w.name}); achieved HBM GB/s vs peak" if decode
+                   else f"CSA2 query-tokens/s ({w.name}); achieved MFMA TFLOP/s vs peak"),
         "value": round(qtok, 2),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -482,6 +484,44 @@ def main():
                      "alg_bytes_per_launch": ab["full"], "avg_launch_ms": round(scan_avg_ms, 5),
                      "launches_timed": len(scan_ms) - 1},
     }
+    if not decode:
+        # A prefill chunk's step is bound by its attention (matrix-core work over
+        # every query row), not by the scan: its roofline is one layer's
+        # attention, timed alone as the step runs it -- a Reuse layer of the
+        # group, attending from the Full layer's staged copy of the cache
+        # (outputs rewritten with the same values) -- against the dense fp16
+        # matrix-core peak.  The scan's figures stay in the line beside it.
+        run = sets[0][2]
+        sets[0][1]()  # a whole step first: selection and staged copy in place
+        torch.cuda.synchronize()
+        l_u = w.pattern.index("U")
+        Lu = inst.layers[l_u]
+
+        def attn_layer():
+            api.csa2_layer_forward("U", q=Lu["q"], q_idx=Lu["q_idx"], swa_kv=Lu["swa"], q_pos=inst.q_pos,
+                                   window=w.window, sm_scale=inst.sm_scale, o=run.o[l_u], lse=run.lse[l_u],
+                                   cache=inst.cache, kview=inst.kview, n_vis=inst.n_vis, n_max=inst.n_max, K=w.K,
+                                   P=w.P if run.has_pool else 0, build_pool=False, ws=run.ws, state=run.state)
+
+        att = []
+        for i in range(max(2, args.scan_reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            attn_layer()
+            e1.record(stream)
+            att.append((e0, e1))
+        torch.cuda.synchronize()
+        att_ms = [a.elapsed_time(b) for a, b in att]
+        att_avg_ms = sum(att_ms[1:]) / (len(att_ms) - 1)
+        # matrix-core work of one layer: S and O over every (row, head, key, channel)
+        flops = 4.0 * rows * w.H * w.D * (w.K + w.window)
+        tf = flops / (att_avg_ms * 1e-3) / 1e12
+        out["scan_roofline"] = out.pop("roofline")
+        out["roofline"] = {"bound": "mfma", "kernel": "attn_pcr_kernel<true> (one layer's attention from the staged fp16 "
+                           "copy; fp16 MFMA, fp32 accumulate)", "achieved": round(tf, 1),
+                           "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4),
+                           "traffic": None, "alg_flops_per_launch": flops, "avg_launch_ms": round(att_avg_ms, 5),
+                           "launches_timed": len(att_ms) - 1}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inst, args.cpu_seconds)
     print(json.dumps(out), flush=True)
