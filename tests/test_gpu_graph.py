@@ -12,16 +12,19 @@ from gpu_common import case, require_gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("pattern,N,P", [
-    ("FRRR", 300_000, 2048),   # the pool over 37,500 block maxima: split + finish selection
-    ("FUUU", 40_000, 0),       # 40,000 entries per row: split + finish selection of the Top-K
+@pytest.mark.parametrize("pattern,B,Q,N,P,ratio", [
+    ("FRRR", 2, 1, 300_000, 2048, 1),   # the pool over 37,500 block maxima: split + finish selection
+    ("FUUU", 2, 1, 40_000, 0, 1),       # 40,000 entries per row: split + finish selection of the Top-K
+    # a prefill chunk: screened selection of 256 rows, the group's staged fp16
+    # copy of the cache, persistent attention of the Full and Reuse layers
+    ("FUU", 1, 256, 16_384, 0, 2),
 ])
-def test_graph_replays_match_eager_step(pattern, N, P):
+def test_graph_replays_match_eager_step(pattern, B, Q, N, P, ratio):
     require_gpu()
     from fp4_kv_cache_csa2_amd import inputs, workload
 
-    w = inputs.Workload("graph_" + pattern, B=2, Q=1, N=N, D=512, H=64, H_i=8, D_i=128, pattern=pattern,
-                        P=P if P else 2048)
+    w = inputs.Workload("graph_" + pattern, B=B, Q=Q, N=N, D=512, H=64, H_i=8, D_i=128, pattern=pattern,
+                        P=P if P else 2048, ratio=ratio)
     inst = workload.make_instance(w, device="cuda:0")
     run = workload.StackRunner(inst)
     case(f"graph replay {pattern} N={N}: eager step")
