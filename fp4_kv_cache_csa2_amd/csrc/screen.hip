@@ -22,6 +22,9 @@
 //     or products, were they flushed, move a score by at most
 //     2^-122 (||qbar|| + ||k||) + 2^-118: eps carries twice that as an
 //     absolute term;
+//     Each aligned group of four entries takes the eps of the largest of its
+//     four norms (eps grows with the norm, so it bounds each of them), so that
+//     the bounds cost one operation per group of four and row, not per entry;
 //  2. per row, the lower bounds S~ - eps over aligned 16-entry blocks: the
 //     K-th largest block bound tau is <= the K-th largest exact score, since
 //     each of those K blocks holds an entry whose exact score is >= its bound;
@@ -319,25 +322,29 @@ __global__ __launch_bounds__(256, 2) void sc_gemm_kernel(ScreenParams p, const u
                     for (int rt = 0; rt < 2; ++rt)
                         acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][blk], acc[rt], 0, 0, 0);
                 }
+                // the largest norm of the lane's four entries 16 j + 4 g .. +3
                 const float4 kn4 = *reinterpret_cast<const float4*>(&kns[buf][16 * j + 4 * g]);
-                const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w};
+                const float kn4m = fmaxf(fmaxf(kn4.x, kn4.y), fmaxf(kn4.z, kn4.w));
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
-                    float m = -INFINITY;
+                    const float eps4 = entry_eps(qe[rt], qa[rt], kn4m);
+                    if (PASS == 1) {
+                        // the group's lower bound: its largest S~ less the group's eps
+                        float m = -INFINITY;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool valid = 16 * j + i < lim4[rt];
-                        const float eps = entry_eps(qe[rt], qa[rt], knv[i]);
-                        if (PASS == 1) {
-                            // (a NaN bound is dropped by the maximum)
-                            m = fmaxf(m, valid ? acc[rt][i] - eps : -INFINITY);
-                        } else {
-                            // (NaN: a candidate)
-                            const bool c = valid && !(acc[rt][i] + eps < taur[rt]);
+                        for (int i = 0; i < 4; ++i) m = fmaxf(m, 16 * j + i < lim4[rt] ? acc[rt][i] : -INFINITY);
+                        float lo = m - eps4;
+                        lo = lo == lo ? lo : -INFINITY;  // (a NaN bound bounds nothing)
+                        lbv[rt][j] = row4_max(lo);
+                    } else {
+                        // candidates: S~ >= tau - eps (NaN: a candidate)
+                        const float t4 = taur[rt] - eps4;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const bool c = 16 * j + i < lim4[rt] && !(acc[rt][i] < t4);
                             cm[rt][s] |= (uint32_t)c << (4 * j + i);
                         }
                     }
-                    if (PASS == 1) lbv[rt][j] = row4_max(m);
                 }
             }
             if (PASS == 1 && g == 0) {
