@@ -131,8 +131,10 @@ __device__ __forceinline__ float exact_score(const ScreenParams& p, int b, int64
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
     const float4* q4 = reinterpret_cast<const float4*>(qb) + z;
     float acc = 0.0f;
-    // (the row in two halves of 64 channels: half the registers in flight)
-#pragma unroll
+    // (the row in two halves of 64 channels: half the registers in flight; a
+    // rolled loop keeps the rescoring kernel within 128 registers, so that two
+    // of its workgroups share a CU)
+#pragma unroll 1
     for (int hf = 0; hf < 2; ++hf) {
         uint4 kv[SC_DI / 16];
 #pragma unroll
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(256) void sc_tau_kernel(ScreenParams p) {
 // qbar staged in LDS; one candidate per thread at a time, the next one located
 // while the current one is scored.
 constexpr int RS_NT = 512;  // threads of the rescoring workgroup
-__global__ __launch_bounds__(RS_NT, 2) void sc_rescore_kernel(ScreenParams p) {
+__global__ __launch_bounds__(RS_NT, 4) void sc_rescore_kernel(ScreenParams p) {
     // (rows padded by 4 floats: lanes reading one channel of different rows hit
     // different banks)
     __shared__ __attribute__((aligned(16))) float qs[SC_TM][SC_DI + 4];
